@@ -1,0 +1,135 @@
+"""Seeded synthetic inputs for the KDA operator.
+
+This module is shared by the tests, the benchmark and the smoke check.  It
+draws random numbers and lays them out; it holds none of the operator's
+arithmetic (no gate, no recurrence, no chunk algebra), so the CPU oracle and
+the HIP path can both be fed from it without sharing any of the method.
+
+Recipe (the shapes and distributions of the workloads on the pages: B=1,
+16 heads, head dim 128, 2K..64K and 1M tokens, plus batched decode):
+
+* every tensor is drawn from numpy ``PCG64`` seeded by
+  ``SeedSequence([seed, tensor_id, slice_id])`` with tensor ids
+  q=0, k=1, v=2, z=3, beta-logit=4, A=5, S0=6;
+* prefill tokens come in slices of ``SLICE`` = 4096 tokens (slice id =
+  token // 4096), so any slice can be regenerated on its own; decode draws
+  one slice per step (slice id = step);
+* q, k ~ N(0,1) per element, then scaled to unit L2 norm per (token, head)
+  in float32 (the caller-side normalisation the operator assumes), then
+  rounded to bfloat16 (round to nearest even) when the I/O dtype is bf16;
+* v ~ N(0,1), rounded to bf16 when the I/O dtype is bf16;
+* z ~ z_scale * N(0,1) per channel (float32);
+* beta = sigmoid(N(0,1)) per (token, head) (float32);
+* A_h ~ U(-1, 1) per head (float32);
+* S0 = 0, or s0_std * N(0,1) per element (float32).
+
+All arrays are float32 numpy arrays; bf16 tensors hold bf16-representable
+values, so widening them to float32 or float64 is exact and both sides see
+identical inputs.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+SLICE = 4096
+TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "z": 3, "beta": 4, "A": 5, "S0": 6}
+
+
+def rng(seed: int, tensor: str, slice_id: int = 0) -> np.random.Generator:
+    return np.random.Generator(
+        np.random.PCG64(np.random.SeedSequence([int(seed), TENSOR_IDS[tensor], int(slice_id)]))
+    )
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16 (ties to even); returns float32."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).reshape(x.shape)
+
+
+def _unit_rows(x: np.ndarray) -> np.ndarray:
+    n = np.sqrt(np.sum(x.astype(np.float32) ** 2, axis=-1, keepdims=True, dtype=np.float32))
+    return (x / np.maximum(n, np.float32(1e-30))).astype(np.float32)
+
+
+def _token_block(seed, tensor, t0, t1, H, D, scale=1.0):
+    """Rows [t0, t1) of a [T, H, D] standard-normal tensor built from 4096-token slices."""
+    out = np.empty((t1 - t0, H, D), dtype=np.float32)
+    s0, s1 = t0 // SLICE, (t1 - 1) // SLICE
+    for s in range(s0, s1 + 1):
+        a, b = s * SLICE, (s + 1) * SLICE
+        full = rng(seed, tensor, s).standard_normal((SLICE, H, D), dtype=np.float32)
+        lo, hi = max(a, t0), min(b, t1)
+        out[lo - t0:hi - t0] = full[lo - a:hi - a]
+    if scale != 1.0:
+        out *= np.float32(scale)
+    return out
+
+
+def prefill_tokens(seed: int, t0: int, t1: int, H: int, dtype: str = "bf16",
+                   z_scale: float = 1.0, D: int = 128) -> dict:
+    """Token rows [t0, t1) of the packed [T_total, H, D] inputs (q, k, v, z, beta)."""
+    q = _unit_rows(_token_block(seed, "q", t0, t1, H, D))
+    k = _unit_rows(_token_block(seed, "k", t0, t1, H, D))
+    v = _token_block(seed, "v", t0, t1, H, D)
+    if dtype == "bf16":
+        q, k, v = bf16_round(q), bf16_round(k), bf16_round(v)
+    elif dtype != "f32":
+        raise ValueError(dtype)
+    z = _token_block(seed, "z", t0, t1, H, D, scale=z_scale)
+    bl = _token_block(seed, "beta", t0, t1, H, 1)[..., 0]
+    beta = (1.0 / (1.0 + np.exp(-bl.astype(np.float64)))).astype(np.float32)
+    return {"q": q, "k": k, "v": v, "z": z, "beta": beta}
+
+
+def head_params(seed: int, H: int) -> np.ndarray:
+    """A_h ~ U(-1, 1)."""
+    return rng(seed, "A").uniform(-1.0, 1.0, size=H).astype(np.float32)
+
+
+def initial_state(seed: int, N: int, H: int, std: float, D: int = 128):
+    if std == 0.0:
+        return np.zeros((N, H, D, D), dtype=np.float32)
+    return (np.float32(std) * rng(seed, "S0").standard_normal((N, H, D, D), dtype=np.float32))
+
+
+def prefill_inputs(seed: int, T_total: int, H: int, dtype: str = "bf16", z_scale: float = 1.0,
+                   s0_std: float = 0.0, n_seqs: int = 1, D: int = 128) -> dict:
+    d = prefill_tokens(seed, 0, T_total, H, dtype, z_scale, D)
+    d["A"] = head_params(seed, H)
+    d["S0"] = initial_state(seed, n_seqs, H, s0_std, D)
+    return d
+
+
+def decode_tokens(seed: int, step: int, N: int, H: int, dtype: str = "bf16", D: int = 128) -> dict:
+    """Inputs of one decode step for N sequences: q, k, v, z as [N, H, D], beta as [N, H]."""
+    def draw(t, shape):
+        return rng(seed, t, step).standard_normal(shape, dtype=np.float32)
+    q = _unit_rows(draw("q", (N, H, D)))
+    k = _unit_rows(draw("k", (N, H, D)))
+    v = draw("v", (N, H, D))
+    if dtype == "bf16":
+        q, k, v = bf16_round(q), bf16_round(k), bf16_round(v)
+    z = draw("z", (N, H, D))
+    bl = draw("beta", (N, H)).astype(np.float64)
+    beta = (1.0 / (1.0 + np.exp(-bl))).astype(np.float32)
+    return {"q": q, "k": k, "v": v, "z": z, "beta": beta}
+
+
+# The five workloads (name -> recipe).  Sizes follow the pages' measurements:
+# one chunk in fp32; B=1, H=16 at 2K and 64K tokens; batched decode; a 1M-token
+# varlen pack.
+WORKLOADS = {
+    "tiny_f32": dict(kind="prefill", seed=1000, lens=[64], H=1, dtype="f32", z_scale=1.0, s0_std=0.0),
+    "prefill_2k": dict(kind="prefill", seed=1001, lens=[2048], H=16, dtype="bf16", z_scale=1.0, s0_std=0.0),
+    "prefill_64k": dict(kind="prefill", seed=1002, lens=[65536], H=16, dtype="bf16", z_scale=2.0, s0_std=0.02),
+    "decode_256x32": dict(kind="decode", seed=1003, N=256, H=32, dtype="bf16", steps=1000, s0_std=0.02),
+    "varlen_1m": dict(kind="prefill", seed=1004, lens=[1048576, 65536, 8192, 777], H=16, dtype="bf16",
+                      z_scale=1.0, s0_std=0.0),
+}
+
+
+def cu_seqlens(lens) -> np.ndarray:
+    return np.concatenate([[0], np.cumsum(np.asarray(lens, dtype=np.int64))]).astype(np.int64)
