@@ -1,0 +1,179 @@
+"""MI355X-native Kimi Delta Attention (KDA) operator.
+
+Thin ctypes binding over ``libkda.so`` (C ABI in ``include/kda.h``).  Every
+step of the operator runs in the library's HIP kernels; this module only checks
+tensor properties, allocates outputs / workspace through PyTorch and passes
+raw device pointers and the current HIP stream.  There is no CPU fallback: if
+the library is missing, every call raises.
+
+    o, S_final = kda_chunk_fwd(q, k, v, g_raw, beta, A, S0=None, cu_seqlens=None)
+    o = kda_decode_step(q, k, v, g_raw, beta, A, S)         # S updated in place
+
+Operator (pages: "Kimi Linear: An Expressive, Efficient Attention Architecture"
+summary, sections 3, 3.1 and 6.3; "Kimi K3 architecture", sequence-bottleneck
+section): per head, S_t = (I - b_t k_t k_t^T) Diag(a_t) S_{t-1} + b_t k_t v_t^T,
+o_t = S_t^T q_t, a_t = exp(-5 * Sigmoid(exp(A_h) * z_t)).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["kda_chunk_fwd", "kda_decode_step", "kda_chunk_fwd_workspace_bytes", "KDAError", "lib_path",
+           "HEAD_DIM", "status_str", "load"]
+
+HEAD_DIM = 128
+KDA_BF16, KDA_F32 = 0, 1
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libkda.so")
+_lib = None
+
+
+class KDAError(RuntimeError):
+    pass
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libkda.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise KDAError(f"{_LIB_PATH} is missing: build it with `python -m gated_delta_rule_29_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.kda_status_str.argtypes = [ctypes.c_int]
+    lib.kda_status_str.restype = ctypes.c_char_p
+    lib.kda_version.argtypes = []
+    lib.kda_version.restype = ctypes.c_int
+    lib.kda_chunk_fwd_workspace_bytes.argtypes = [i64, i32, i32]
+    lib.kda_chunk_fwd_workspace_bytes.restype = sz
+    lib.kda_chunk_fwd.argtypes = [P, P, P, ctypes.c_int, P, P, P, P, P, i32, i64, i32, i32, i32, i32, P, P, P,
+                                  sz, P]
+    lib.kda_chunk_fwd.restype = ctypes.c_int
+    lib.kda_decode_step.argtypes = [P, P, P, ctypes.c_int, P, P, P, P, i32, i32, i32, i32, P, P]
+    lib.kda_decode_step.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load().kda_status_str(int(status)).decode()
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise KDAError(f"{what}: {status_str(rc)}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, name, dtypes, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must have dtype in {dtypes}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def kda_chunk_fwd_workspace_bytes(T_total: int, n_seqs: int, H: int) -> int:
+    return int(load().kda_chunk_fwd_workspace_bytes(int(T_total), int(n_seqs), int(H)))
+
+
+def kda_chunk_fwd(q, k, v, g_raw, beta, A, S0=None, cu_seqlens=None, *, o=None, S_final=None,
+                  workspace=None, stream=None, return_final_state=True):
+    """Chunkwise KDA prefill.
+
+    q, k, v: [B, T, H, 128] (or [T, H, 128]) bf16 or fp32; g_raw: same shape fp32 (the gate's z);
+    beta: [B, T, H] fp32; A: [H] fp32; S0: [N, H, 128, 128] fp32 or None (zeros);
+    cu_seqlens: int32 device tensor [N+1] packing N sequences along T (then B must be 1).
+    Returns (o [.., H, 128] fp32, S_final [N, H, 128, 128] fp32 or None).
+    """
+    lib = load()
+    squeeze = q.dim() == 3
+    if squeeze:
+        q, k, v, g_raw, beta = (x.unsqueeze(0) for x in (q, k, v, g_raw, beta))
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, 128] or [T, H, 128]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    io = (torch.bfloat16, torch.float32)
+    _need(q, "q", io, dev)
+    _need(k, "k", (q.dtype,), dev)
+    _need(v, "v", (q.dtype,), dev)
+    _need(g_raw, "g_raw", (torch.float32,), dev)
+    _need(beta, "beta", (torch.float32,), dev)
+    _need(A, "A", (torch.float32,), dev)
+    if k.shape != q.shape or g_raw.shape != q.shape or v.shape[:3] != q.shape[:3] or beta.shape != (B, T, H):
+        raise ValueError("inconsistent shapes")
+    if A.shape != (H,):
+        raise ValueError("A must be [H]")
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", (torch.int32,), dev)
+        if B != 1:
+            raise ValueError("cu_seqlens needs B == 1")
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    if S0 is not None:
+        _need(S0, "S0", (torch.float32,), dev)
+        if S0.shape != (N, H, dk, dv):
+            raise ValueError(f"S0 must be [{N}, {H}, {dk}, {dv}]")
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    if return_final_state and S_final is None:
+        S_final = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    need = int(lib.kda_chunk_fwd_workspace_bytes(B * T, N, H))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    dtype = KDA_BF16 if q.dtype == torch.bfloat16 else KDA_F32
+    rc = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), dtype, _ptr(g_raw), _ptr(beta), _ptr(A), _ptr(S0),
+                           _ptr(cu_seqlens), B, T, H, N, dk, dv, _ptr(o), _ptr(S_final), _ptr(workspace),
+                           workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc, "kda_chunk_fwd")
+    if squeeze:
+        o = o.squeeze(0)
+    return o, S_final
+
+
+def kda_decode_step(q, k, v, g_raw, beta, A, S, *, o=None, stream=None):
+    """One recurrent step for N sequences: q, k, v, g_raw [N, H, 128]; beta [N, H]; A [H];
+    S [N, H, 128, 128] fp32 updated in place.  Returns o [N, H, 128] fp32."""
+    lib = load()
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    _need(q, "q", (torch.bfloat16, torch.float32), dev)
+    _need(k, "k", (q.dtype,), dev)
+    _need(v, "v", (q.dtype,), dev)
+    _need(g_raw, "g_raw", (torch.float32,), dev)
+    _need(beta, "beta", (torch.float32,), dev)
+    _need(A, "A", (torch.float32,), dev)
+    _need(S, "S", (torch.float32,), dev)
+    if k.shape != q.shape or g_raw.shape != q.shape or beta.shape != (N, H) or S.shape != (N, H, dk, dv):
+        raise ValueError("inconsistent shapes")
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=torch.float32, device=dev)
+    dtype = KDA_BF16 if q.dtype == torch.bfloat16 else KDA_F32
+    rc = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), dtype, _ptr(g_raw), _ptr(beta), _ptr(A), _ptr(S), N, H,
+                             dk, dv, _ptr(o), _stream(stream))
+    _check(rc, "kda_decode_step")
+    return o

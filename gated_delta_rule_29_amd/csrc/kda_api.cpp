@@ -1,0 +1,129 @@
+// kda_api.cpp -- C ABI of libkda.so (declared in include/kda.h).
+//
+// Every entry point validates its arguments on the host before touching the
+// HIP runtime, so invalid calls return a status and launch nothing.  Kernels
+// live in kda_decode.hip (recurrent step) and kda_prefill.hip (chunkwise form).
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+
+#include "kda.h"
+
+#define KDA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace kda {
+int launch_decode(const void *q, const void *k, const void *v, bool f32io, const float *z, const float *beta,
+                  const float *A, float *S, int N, int H, float *o, hipStream_t stream);
+int launch_prefill(const void *q, const void *k, const void *v, bool f32io, const float *z, const float *beta,
+                   const float *A, const float *S0, const int32_t *cu, int B, int64_t T, int H, int N,
+                   float *o, float *S_final, void *ws, hipStream_t stream);
+size_t prefill_workspace_bytes(int64_t T_total, int N, int H);
+int set_prefill_attributes();
+}  // namespace kda
+
+namespace {
+
+constexpr int kD = 128;
+
+bool misaligned(const void *p) { return p && ((uintptr_t)p & 15u) != 0; }
+
+// [a, a + na) and [b, b + nb) share a byte
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+std::once_flag g_attr_once;
+int g_attr_status = 0;
+
+}  // namespace
+
+KDA_EXPORT const char *kda_status_str(int status) {
+    switch (status) {
+        case KDA_OK: return "KDA_OK";
+        case KDA_ERR_NULL: return "KDA_ERR_NULL: a required pointer is NULL";
+        case KDA_ERR_SHAPE: return "KDA_ERR_SHAPE: dk and dv must be 128 and sizes non-negative";
+        case KDA_ERR_DTYPE: return "KDA_ERR_DTYPE: qkv_dtype must be KDA_BF16 or KDA_F32";
+        case KDA_ERR_SEQLENS: return "KDA_ERR_SEQLENS: cu_seqlens needs B == 1 and n_seqs >= 1";
+        case KDA_ERR_ALIGN: return "KDA_ERR_ALIGN: pointers must be 16-byte aligned";
+        case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing or too small";
+        case KDA_ERR_HIP: return "KDA_ERR_HIP: a HIP launch failed";
+        case KDA_ERR_ALIAS: return "KDA_ERR_ALIAS: o overlaps an input";
+        default: return "KDA_ERR_UNKNOWN";
+    }
+}
+
+KDA_EXPORT int kda_version(void) { return 100; }
+
+KDA_EXPORT size_t kda_chunk_fwd_workspace_bytes(int64_t T_total, int32_t n_seqs, int32_t H) {
+    if (T_total < 0 || n_seqs < 0 || H < 0) return 0;
+    if (T_total == 0 && n_seqs == 0) return 0;
+    return kda::prefill_workspace_bytes(T_total, n_seqs, H);
+}
+
+KDA_EXPORT int kda_chunk_fwd(const void *q, const void *k, const void *v, kda_dtype qkv_dtype,
+                             const float *g_raw, const float *beta, const float *A, const float *S0,
+                             const int32_t *cu_seqlens, int32_t B, int64_t T, int32_t H, int32_t n_seqs,
+                             int32_t dk, int32_t dv, float *o, float *S_final, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+    if (dk != kD || dv != kD) return KDA_ERR_SHAPE;
+    if (B < 0 || T < 0 || H < 0 || n_seqs < 0) return KDA_ERR_SHAPE;
+    if (qkv_dtype != KDA_BF16 && qkv_dtype != KDA_F32) return KDA_ERR_DTYPE;
+    if (cu_seqlens) {
+        if (B != 1 || n_seqs < 1) return KDA_ERR_SEQLENS;
+    } else if (n_seqs != B) {
+        return KDA_ERR_SEQLENS;
+    }
+    const int64_t T_total = (int64_t)B * T;
+    if (T_total > INT32_MAX - 64 || (int64_t)n_seqs * H > INT32_MAX / 64) return KDA_ERR_SHAPE;
+    if (n_seqs == 0 || H == 0) return KDA_OK;  // nothing to compute
+    if (!A) return KDA_ERR_NULL;
+    if (T_total > 0 && (!q || !k || !v || !g_raw || !beta || !o)) return KDA_ERR_NULL;
+    const void *ptrs[] = {q, k, v, g_raw, beta, A, S0, o, S_final, workspace};
+    for (const void *p : ptrs)
+        if (misaligned(p)) return KDA_ERR_ALIGN;
+    const size_t need = kda_chunk_fwd_workspace_bytes(T_total, n_seqs, H);
+    if (!workspace || workspace_bytes < need) return KDA_ERR_WORKSPACE;
+    const size_t esz = qkv_dtype == KDA_F32 ? 4 : 2;
+    const size_t tok = (size_t)T_total * H;
+    const size_t o_bytes = tok * kD * 4;
+    const size_t st_bytes = (size_t)n_seqs * H * kD * kD * 4;
+    if (overlap(o, o_bytes, q, tok * kD * esz) || overlap(o, o_bytes, k, tok * kD * esz) ||
+        overlap(o, o_bytes, v, tok * kD * esz) || overlap(o, o_bytes, g_raw, tok * kD * 4) ||
+        overlap(o, o_bytes, beta, tok * 4) || overlap(o, o_bytes, A, (size_t)H * 4) ||
+        overlap(o, o_bytes, S0, st_bytes) || overlap(o, o_bytes, S_final, st_bytes) ||
+        overlap(o, o_bytes, workspace, need))
+        return KDA_ERR_ALIAS;
+
+    std::call_once(g_attr_once, [] { g_attr_status = kda::set_prefill_attributes(); });
+    if (g_attr_status != 0) return KDA_ERR_HIP;
+    const int rc = kda::launch_prefill(q, k, v, qkv_dtype == KDA_F32, g_raw, beta, A, S0, cu_seqlens, B, T, H,
+                                       n_seqs, o, S_final, workspace, (hipStream_t)stream);
+    return rc == 0 ? KDA_OK : KDA_ERR_HIP;
+}
+
+KDA_EXPORT int kda_decode_step(const void *q, const void *k, const void *v, kda_dtype qkv_dtype,
+                               const float *g_raw, const float *beta, const float *A, float *S, int32_t N,
+                               int32_t H, int32_t dk, int32_t dv, float *o, void *stream) {
+    if (dk != kD || dv != kD) return KDA_ERR_SHAPE;
+    if (N < 0 || H < 0) return KDA_ERR_SHAPE;
+    if (qkv_dtype != KDA_BF16 && qkv_dtype != KDA_F32) return KDA_ERR_DTYPE;
+    if ((int64_t)N * H > INT32_MAX) return KDA_ERR_SHAPE;
+    if (N == 0 || H == 0) return KDA_OK;
+    if (!q || !k || !v || !g_raw || !beta || !A || !S || !o) return KDA_ERR_NULL;
+    const void *ptrs[] = {q, k, v, g_raw, beta, A, S, o};
+    for (const void *p : ptrs)
+        if (misaligned(p)) return KDA_ERR_ALIGN;
+    const size_t esz = qkv_dtype == KDA_F32 ? 4 : 2;
+    const size_t nh = (size_t)N * H;
+    const size_t o_bytes = nh * kD * 4;
+    if (overlap(o, o_bytes, S, nh * kD * kD * 4) || overlap(o, o_bytes, q, nh * kD * esz) ||
+        overlap(o, o_bytes, k, nh * kD * esz) || overlap(o, o_bytes, v, nh * kD * esz) ||
+        overlap(o, o_bytes, g_raw, nh * kD * 4) || overlap(o, o_bytes, beta, nh * 4) ||
+        overlap(o, o_bytes, A, (size_t)H * 4))
+        return KDA_ERR_ALIAS;
+    const int rc = kda::launch_decode(q, k, v, qkv_dtype == KDA_F32, g_raw, beta, A, S, N, H, o,
+                                      (hipStream_t)stream);
+    return rc == 0 ? KDA_OK : KDA_ERR_HIP;
+}

@@ -1,0 +1,118 @@
+// kda_common.hpp -- shared device helpers for the gfx950 KDA kernels.
+//
+// MFMA fragment conventions (v_mfma_f32_16x16x32_bf16, wave64):
+//   A operand (16 x 32): lane l holds row (l & 15) and the 8 consecutive k
+//                        indices 8 * (l >> 4) + e, e = 0..7;
+//   B operand (32 x 16): lane l holds column (l & 15), same 8 k indices;
+//   C / D     (16 x 16): lane l holds column (l & 15), rows 4 * (l >> 4) + i.
+// Because the k index is summed, any permutation of k is allowed as long as
+// the A and B fragments use the same one.  The fp32 path feeds the same
+// 8-element fragments to eight v_mfma_f32_16x16x4_f32 (one per element e),
+// which again pairs equal k on both sides.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+constexpr int D = 128;      // d_k = d_v (Kimi Linear summary, sections 4 and 6.3)
+constexpr int CH = 64;      // chunk length (section 6.3, appendix C)
+constexpr int SUB = 16;     // sub-chunk length (Kimi K3: 16-token tiles)
+constexpr float GMIN = -5.f;  // Kimi K3 lower bound of the log-decay
+
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Eight fp32 values of one lane's 32-deep k slice.
+struct F8 {
+    float v[8];
+};
+// The same values as an unevaluated sum hi + lo of two bf16 vectors.
+struct S8 {
+    bf16x8 hi, lo;
+};
+
+__device__ __forceinline__ S8 split8(const F8 &x) {
+    S8 s;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        __bf16 h = (__bf16)x.v[e];
+        s.hi[e] = h;
+        s.lo[e] = (__bf16)(x.v[e] - (float)h);
+    }
+    return s;
+}
+__device__ __forceinline__ bf16x8 round8(const F8 &x) {
+    bf16x8 h;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[e] = (__bf16)x.v[e];
+    return h;
+}
+
+// Products of fragments.  "s" = split (hi + lo), "1" = single bf16.
+// hi*lo and lo*hi are kept, lo*lo is dropped (below fp32 rounding of the sum).
+__device__ __forceinline__ f32x4 mma_ss(f32x4 c, const S8 &a, const S8 &b) {
+    c = mfma_bf16(a.lo, b.hi, c);
+    c = mfma_bf16(a.hi, b.lo, c);
+    return mfma_bf16(a.hi, b.hi, c);
+}
+__device__ __forceinline__ f32x4 mma_s1(f32x4 c, const S8 &a, bf16x8 b) {
+    c = mfma_bf16(a.lo, b, c);
+    return mfma_bf16(a.hi, b, c);
+}
+__device__ __forceinline__ f32x4 mma_1s(f32x4 c, bf16x8 a, const S8 &b) {
+    c = mfma_bf16(a, b.lo, c);
+    return mfma_bf16(a, b.hi, c);
+}
+__device__ __forceinline__ f32x4 mma_11(f32x4 c, bf16x8 a, bf16x8 b) { return mfma_bf16(a, b, c); }
+// exact fp32 products (fp32 I/O build)
+__device__ __forceinline__ f32x4 mma_ff(f32x4 c, const F8 &a, const F8 &b) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) c = mfma_f32(a.v[e], b.v[e], c);
+    return c;
+}
+
+__device__ __forceinline__ F8 ld_f8(const float *p) {  // 32-byte aligned
+    F8 r;
+    const float4 a = *(const float4 *)p, b = *(const float4 *)(p + 4);
+    r.v[0] = a.x; r.v[1] = a.y; r.v[2] = a.z; r.v[3] = a.w;
+    r.v[4] = b.x; r.v[5] = b.y; r.v[6] = b.z; r.v[7] = b.w;
+    return r;
+}
+__device__ __forceinline__ bf16x8 ld_b8(const __bf16 *p) { return *(const bf16x8 *)p; }
+
+// load 8 consecutive inputs of type IO as fp32
+__device__ __forceinline__ F8 ld_io8(const float *p) { return ld_f8(p); }
+__device__ __forceinline__ F8 ld_io8(const __bf16 *p) {
+    bf16x8 b = ld_b8(p);
+    F8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r.v[e] = (float)b[e];
+    return r;
+}
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float to_f(__bf16 x) { return (float)x; }
+
+// Kimi K3 gate: g = g_min * Sigmoid(e^A z), written so that z = +-inf gives
+// exactly g_min / 0 and NaN propagates.
+__device__ __forceinline__ float kda_gate(float expA, float z) {
+    float x = expA * z;
+    float s;
+    if (x >= 0.f) {
+        s = 1.f / (1.f + __expf(-x));
+    } else {
+        float e = __expf(x);
+        s = e / (1.f + e);
+    }
+    return GMIN * s;
+}
+
+}  // namespace kda

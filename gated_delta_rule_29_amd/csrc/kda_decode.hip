@@ -1,0 +1,112 @@
+// kda_decode.hip -- single-token recurrent KDA update (Kimi Linear summary,
+// section 6.3: generation uses the recurrent update; each head keeps a fixed
+// 128 x 128 state), with the Kimi K3 lower-bounded gate.
+//
+// One workgroup of 256 threads per (sequence, head).  The 64 KiB fp32 state is
+// streamed from HBM once and written back once:
+//   wave w owns key rows [32w, 32w+32); lane l owns columns 4*(l&31)..+3 of the
+//   rows 32w + 2m + (l>>5), m = 0..15 (16 float4 per lane, held in registers).
+// Per head: alpha = exp(g(z)); S' = Diag(alpha) S; p = S'^T k and r = S'^T q
+// (partial sums per lane, reduced across the two row parities by a lane swap
+// and across the four waves through LDS); delta = beta (v - p);
+// o = r + (k.q) delta (= S_new^T q); S_new = S' + k delta^T.
+#include "kda_common.hpp"
+
+namespace kda {
+
+template <typename IO>
+__global__ __launch_bounds__(256) void decode_kernel(const IO *__restrict__ q, const IO *__restrict__ k,
+                                                     const IO *__restrict__ v, const float *__restrict__ z,
+                                                     const float *__restrict__ beta,
+                                                     const float *__restrict__ A, float *__restrict__ S,
+                                                     int H, float *__restrict__ o) {
+    const int nh = blockIdx.x;  // n * H + h
+    const int h = nh % H;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const int cg = l & 31, rp = l >> 5;
+
+    __shared__ float s_alpha[D], s_k[D], s_q[D], s_v[D];
+    __shared__ float s_p[4][D], s_r[4][D];
+    __shared__ float s_delta[D];
+    __shared__ float s_kq[2];
+
+    float *Sh = S + (size_t)nh * D * D;
+    float4 st[16];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+        const int i = 32 * w + 2 * m + rp;
+        st[m] = *(const float4 *)(Sh + (size_t)i * D + 4 * cg);
+    }
+
+    const size_t vec = (size_t)nh * D;
+    if (tid < D) {
+        const float eA = __expf(A[h]);
+        s_alpha[tid] = __expf(kda_gate(eA, z[vec + tid]));
+        s_k[tid] = to_f(k[vec + tid]);
+        s_q[tid] = to_f(q[vec + tid]);
+        s_v[tid] = to_f(v[vec + tid]);
+    }
+    __syncthreads();
+    if (w == 0) {  // k . q over the 128 channels
+        float kq = s_k[l] * s_q[l] + s_k[l + 64] * s_q[l + 64];
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) kq += __shfl_xor(kq, off);
+        if (l == 0) s_kq[0] = kq;
+    }
+
+    float p[4] = {0.f, 0.f, 0.f, 0.f}, r[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+        const int i = 32 * w + 2 * m + rp;
+        const float a = s_alpha[i], ki = s_k[i], qi = s_q[i];
+        st[m].x *= a; st[m].y *= a; st[m].z *= a; st[m].w *= a;
+        p[0] += ki * st[m].x; p[1] += ki * st[m].y; p[2] += ki * st[m].z; p[3] += ki * st[m].w;
+        r[0] += qi * st[m].x; r[1] += qi * st[m].y; r[2] += qi * st[m].z; r[3] += qi * st[m].w;
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        p[c] += __shfl_xor(p[c], 32);
+        r[c] += __shfl_xor(r[c], 32);
+    }
+    if (rp == 0) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            s_p[w][4 * cg + c] = p[c];
+            s_r[w][4 * cg + c] = r[c];
+        }
+    }
+    __syncthreads();
+    if (tid < D) {
+        const float pj = s_p[0][tid] + s_p[1][tid] + s_p[2][tid] + s_p[3][tid];
+        const float rj = s_r[0][tid] + s_r[1][tid] + s_r[2][tid] + s_r[3][tid];
+        const float dj = beta[nh] * (s_v[tid] - pj);
+        s_delta[tid] = dj;
+        o[vec + tid] = rj + s_kq[0] * dj;
+    }
+    __syncthreads();
+    const float4 dl = *(const float4 *)(s_delta + 4 * cg);
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+        const int i = 32 * w + 2 * m + rp;
+        const float ki = s_k[i];
+        float4 x = st[m];
+        x.x += ki * dl.x; x.y += ki * dl.y; x.z += ki * dl.z; x.w += ki * dl.w;
+        *(float4 *)(Sh + (size_t)i * D + 4 * cg) = x;
+    }
+}
+
+int launch_decode(const void *q, const void *k, const void *v, bool f32io, const float *z,
+                  const float *beta, const float *A, float *S, int N, int H, float *o,
+                  hipStream_t stream) {
+    const unsigned blocks = (unsigned)N * (unsigned)H;
+    if (blocks == 0) return 0;
+    if (f32io)
+        hipLaunchKernelGGL(decode_kernel<float>, dim3(blocks), dim3(256), 0, stream, (const float *)q,
+                           (const float *)k, (const float *)v, z, beta, A, S, H, o);
+    else
+        hipLaunchKernelGGL(decode_kernel<__bf16>, dim3(blocks), dim3(256), 0, stream, (const __bf16 *)q,
+                           (const __bf16 *)k, (const __bf16 *)v, z, beta, A, S, H, o);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace kda

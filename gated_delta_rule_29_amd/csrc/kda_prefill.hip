@@ -1,0 +1,656 @@
+// kda_prefill.hip -- chunkwise KDA prefill on gfx950.
+//
+// Pages: "Kimi Linear: An Expressive, Efficient Attention Architecture" summary
+// (sections 2.1, 3.1, 3.2, 6.3, appendix B/C) and "Kimi K3 architecture"
+// (sequence-bottleneck section: g = -5 Sigmoid(e^A z), 16-token tiles that keep
+// the cumulative log-decay inside (-80, 0)).
+//
+// Within a chunk of n <= 64 tokens with incoming state S (rows = key channel):
+//   G_t      inclusive cumulative log-decay per key channel, Gam_t = e^{G_t}
+//   Akk[r,c] = beta_r sum_j k_rj k_cj e^{G_rj - G_cj}   (c < r)
+//   Aqk[r,c] = sum_j q_rj k_cj e^{G_rj - G_cj}          (c <= r)
+//   T        = (I + Akk)^{-1}            (forward substitution)
+//   W = T diag(beta) (K * Gam),  U = T diag(beta) V      (WY / UT vectors)
+//   Delta = U - W S,  O = (Q * Gam) S + Aqk Delta,
+//   S' = Diag(Gam_n) S + (K * e^{G_n - G})^T Delta.
+// Every e^{G_r - G_c} is evaluated through the 16-token sub-chunk of r with
+// reference R_i (G just before the sub-chunk): a row factor e^{G_r - R_i} in
+// [e^-80, 1] and a column factor e^{R_i - G_c} in [0, e^80], both inside the
+// fp32 / bf16 range, so the diagonal tiles are dense MFMA products too.
+//
+// Kernels (one launch each, in stream order):
+//   prep_kernel   sequence boundaries (clamped, non-decreasing) and the first
+//                 chunk index of every sequence;
+//   intra_kernel  one workgroup per (chunk, head), all chunks in parallel:
+//                 gate + sub-chunk cumsums, the two Gram tiles on MFMA, the
+//                 blocked forward substitution, W and U on MFMA; writes the
+//                 per-chunk operands of the chain to the workspace;
+//   chain_kernel  one workgroup per (sequence, head, 16 value columns): keeps
+//                 its 128 x 16 fp32 state slice in registers across the
+//                 sequence's chunks and forms Delta, the output and the next
+//                 state with MFMA.
+//
+// Precision: q, k, v arrive in bf16 (exact MFMA operands).  Intermediates that
+// carry fp32 information enter bf16 MFMAs as an unevaluated hi + lo pair
+// (hi*hi + hi*lo + lo*hi), except W in W S, which tolerates a single bf16
+// rounding.  The fp32 I/O build uses fp32 MFMA for every product.
+#include "kda_common.hpp"
+
+namespace kda {
+
+// ----------------------------------------------------------------- layout --
+
+// Per (chunk, head) block of chain operands in the workspace (bytes).  "Split"
+// arrays hold the bf16 hi part followed by the bf16 lo part in the bf16 build
+// and plain fp32 in the fp32 build; both use 4 bytes per element.
+constexpr size_t OFF_W = 0;            // W      [64][128]  bf16 (fp32 build: fp32)
+constexpr size_t OFF_U = 32768;        // U      [64][128]  fp32
+constexpr size_t OFF_KT = 65536;       // K~^T   [128][64]  split, K~ = K * e^{G_n - G}
+constexpr size_t OFF_QT = 98304;       // Q~     [64][128]  split, Q~ = Q * Gam
+constexpr size_t OFF_AQ = 131072;      // Aqk    [64][64]   split, zero above the diagonal
+constexpr size_t OFF_GM = 147456;      // gamma  [128]      fp32, e^{G_n}
+constexpr size_t BLK_BYTES = 147968;   // multiple of 256
+
+__host__ __device__ constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Table {  // workspace header
+    int32_t *chunk_off;  // [N+1] first chunk of each sequence; chunk_off[N] = total
+    int64_t *seq_start;  // [N]
+    int64_t *seq_end;    // [N]
+    char *blocks;        // chain operands, block (c, h) at (c * H + h) * BLK_BYTES
+};
+
+__host__ __device__ inline size_t table_bytes(int N) {
+    return align256(4 * (size_t)(N + 1)) + 2 * align256(8 * (size_t)N);
+}
+__host__ __device__ inline Table carve(void *ws, int N) {
+    char *p = (char *)ws;
+    Table t;
+    t.chunk_off = (int32_t *)p;
+    p += align256(4 * (size_t)(N + 1));
+    t.seq_start = (int64_t *)p;
+    p += align256(8 * (size_t)N);
+    t.seq_end = (int64_t *)p;
+    p += align256(8 * (size_t)N);
+    t.blocks = p;
+    return t;
+}
+__host__ inline int64_t max_chunks(int64_t T_total, int N) { return (T_total + CH - 1) / CH + N; }
+
+// ------------------------------------------------------------------- prep --
+
+// Sequence n spans [s_n, s_{n+1}) with s_m = max_{m' <= m} clamp(cu[m'], 0, T),
+// so sequences never overlap and the chunk count is at most ceil(T/64) + N.
+// cu == nullptr means B equal sequences of Tper tokens.  One workgroup walks
+// the N + 1 offsets in tiles of 256 with a running max and a running sum.
+__global__ __launch_bounds__(256) void prep_kernel(const int32_t *__restrict__ cu, int N, int64_t T_total,
+                                                   int64_t Tper, Table tab) {
+    __shared__ int64_t s_scan[256];
+    __shared__ int64_t s_prev_max, s_prev_sum;
+    const int tid = threadIdx.x;
+    if (tid == 0) {
+        s_prev_max = 0;
+        s_prev_sum = 0;
+    }
+    __syncthreads();
+    for (int base = 0; base <= N; base += 256) {
+        const int m = base + tid;
+        int64_t c = 0;
+        if (m <= N) {
+            c = cu ? (int64_t)cu[m] : (int64_t)m * Tper;
+            c = c < 0 ? 0 : (c > T_total ? T_total : c);
+        }
+        // running max over the tile (Hillis-Steele), then fold in the previous tiles
+        s_scan[tid] = c;
+        __syncthreads();
+        for (int off = 1; off < 256; off <<= 1) {
+            const int64_t x = tid >= off ? s_scan[tid - off] : 0;
+            __syncthreads();
+            if (x > s_scan[tid]) s_scan[tid] = x;
+            __syncthreads();
+        }
+        const int64_t pm = s_prev_max;
+        const int64_t sm = s_scan[tid] > pm ? s_scan[tid] : pm;            // s_m
+        const int64_t sp = tid > 0 ? (s_scan[tid - 1] > pm ? s_scan[tid - 1] : pm) : pm;  // s_{m-1}
+        if (m < N) tab.seq_start[m] = sm;
+        if (m >= 1 && m <= N) tab.seq_end[m - 1] = sm;
+        // chunks of sequence m - 1, inclusive running sum = chunk_off[m]
+        const int64_t cnt = (m >= 1 && m <= N) ? (sm - sp + CH - 1) / CH : 0;
+        __syncthreads();
+        s_scan[tid] = cnt;
+        __syncthreads();
+        for (int off = 1; off < 256; off <<= 1) {
+            const int64_t x = tid >= off ? s_scan[tid - off] : 0;
+            __syncthreads();
+            s_scan[tid] += x;
+            __syncthreads();
+        }
+        const int64_t incl = s_scan[tid] + s_prev_sum;
+        if (m <= N) tab.chunk_off[m] = (int32_t)incl;
+        __syncthreads();
+        if (tid == 255) {
+            s_prev_max = sm;
+            s_prev_sum = incl;
+        }
+        __syncthreads();
+    }
+}
+
+// locate chunk c: sequence n with chunk_off[n] <= c < chunk_off[n+1]
+__device__ inline int find_seq(const int32_t *chunk_off, int N, int c) {
+    int lo = 0, hi = N - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (chunk_off[mid] <= c)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
+// ----------------------------------------------------------------- intra --
+
+constexpr int PG = 132;  // LDS pitch (floats) of [64][128] token-major arrays
+constexpr int PT = 68;   // LDS pitch (floats) of [*][64] arrays
+
+template <typename IO>
+struct IntraSmem {
+    float E1[CH * PG];     // e^{G_t - R_{s(t)}}: row factor, in [e^-80, 1]
+    float KG[D * PT];      // (K * Gam)^T  [channel][token]
+    float Vt[D * PT];      // V^T          [channel][token]
+    float Akk[CH * PT];    // Akk, then T = (I + Akk)^{-1} in place
+    float R[5 * D];        // R_s: cumulative log-decay before sub-chunk s (R_4 = G_n)
+    float PF[6 * D];       // e^{R_i - R_j} for the six sub-chunk pairs j < i
+    float beta[CH];
+};
+
+__device__ __forceinline__ int pair_index(int i, int j) { return i * (i - 1) / 2 + j; }  // j < i
+
+// store a split (hi | lo) or fp32 value quad at element offset e of an array of
+// n_elems elements starting at base
+template <bool F32>
+__device__ __forceinline__ void st_split4(char *base, size_t n_elems, size_t e, float a, float b, float c,
+                                          float d) {
+    if constexpr (F32) {
+        *(float4 *)((float *)base + e) = make_float4(a, b, c, d);
+    } else {
+        bf16x4 h, l;
+        h[0] = (__bf16)a; h[1] = (__bf16)b; h[2] = (__bf16)c; h[3] = (__bf16)d;
+        l[0] = (__bf16)(a - (float)h[0]); l[1] = (__bf16)(b - (float)h[1]);
+        l[2] = (__bf16)(c - (float)h[2]); l[3] = (__bf16)(d - (float)h[3]);
+        *(bf16x4 *)((__bf16 *)base + e) = h;
+        *(bf16x4 *)((__bf16 *)base + n_elems + e) = l;
+    }
+}
+template <bool F32>
+__device__ __forceinline__ void st_split1(char *base, size_t n_elems, size_t e, float a) {
+    if constexpr (F32) {
+        ((float *)base)[e] = a;
+    } else {
+        __bf16 h = (__bf16)a;
+        ((__bf16 *)base)[e] = h;
+        ((__bf16 *)base)[n_elems + e] = (__bf16)(a - (float)h);
+    }
+}
+
+template <typename IO>
+__global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, const IO *__restrict__ k,
+                                                    const IO *__restrict__ v, const float *__restrict__ z,
+                                                    const float *__restrict__ beta,
+                                                    const float *__restrict__ A, int N, int H, Table tab) {
+    constexpr bool F32 = sizeof(IO) == 4;
+    extern __shared__ __align__(16) char smem_raw[];
+    IntraSmem<IO> &sm = *reinterpret_cast<IntraSmem<IO> *>(smem_raw);
+
+    const int c = blockIdx.x, h = blockIdx.y;
+    const int total = tab.chunk_off[N];
+    if (c >= total) return;
+    const int n = find_seq(tab.chunk_off, N, c);
+    const int64_t t0 = tab.seq_start[n] + (int64_t)(c - tab.chunk_off[n]) * CH;
+    const int len = (int)min((int64_t)CH, tab.seq_end[n] - t0);
+    char *blk = tab.blocks + ((size_t)c * H + h) * BLK_BYTES;
+
+    const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63, g = l >> 4, lr = l & 15;
+    const size_t HD = (size_t)H * D;
+    auto tok = [&](int t) -> size_t { return (size_t)(t0 + t) * HD + (size_t)h * D; };
+
+    // ---- phase 1: gate, sub-chunk cumulative sums, elementwise operands ----
+    const int ch = tid & (D - 1), half = tid >> 7;
+    const float eA = __expf(A[h]);
+    float Gl[2][SUB];
+#pragma unroll
+    for (int si = 0; si < 2; ++si) {
+        const int s = half + 2 * si;
+        float acc = 0.f;
+#pragma unroll
+        for (int u = 0; u < SUB; ++u) {
+            const int t = s * SUB + u;
+            const float gt = t < len ? kda_gate(eA, z[tok(t) + ch]) : 0.f;
+            acc += gt;
+            Gl[si][u] = acc;
+            sm.E1[t * PG + ch] = __expf(acc);
+        }
+        sm.R[(s + 1) * D + ch] = acc;  // sub-chunk total, turned into R below
+    }
+    if (tid < CH) sm.beta[tid] = tid < len ? beta[(size_t)(t0 + tid) * H + h] : 0.f;
+    __syncthreads();
+    if (tid < D) {
+        float r = 0.f;
+        sm.R[tid] = 0.f;
+#pragma unroll
+        for (int s = 1; s <= 4; ++s) {
+            r += sm.R[s * D + tid];
+            sm.R[s * D + tid] = r;
+        }
+    }
+    __syncthreads();
+    if (tid < D) {
+#pragma unroll
+        for (int i = 1; i < 4; ++i)
+            for (int j = 0; j < i; ++j)
+                sm.PF[pair_index(i, j) * D + tid] = __expf(sm.R[i * D + tid] - sm.R[j * D + tid]);
+    }
+    {
+        const float Gn = sm.R[4 * D + ch];
+        char *qt = blk + OFF_QT, *kt = blk + OFF_KT;
+#pragma unroll
+        for (int si = 0; si < 2; ++si) {
+            const int s = half + 2 * si;
+            const float Rs = sm.R[s * D + ch];
+            float kt_vals[SUB];
+#pragma unroll
+            for (int u = 0; u < SUB; ++u) {
+                const int t = s * SUB + u;
+                const float Gt = Rs + Gl[si][u];
+                const float gam = __expf(Gt);
+                const bool ok = t < len;
+                const float kv = ok ? to_f(k[tok(t) + ch]) : 0.f;
+                const float qv = ok ? to_f(q[tok(t) + ch]) : 0.f;
+                const float vv = ok ? to_f(v[tok(t) + ch]) : 0.f;
+                sm.KG[ch * PT + t] = kv * gam;
+                sm.Vt[ch * PT + t] = vv;
+                st_split1<F32>(qt, CH * D, (size_t)t * D + ch, qv * gam);
+                kt_vals[u] = kv * __expf(Gn - Gt);
+            }
+#pragma unroll
+            for (int u = 0; u < SUB; u += 4)
+                st_split4<F32>(kt, D * CH, (size_t)ch * CH + s * SUB + u, kt_vals[u], kt_vals[u + 1],
+                               kt_vals[u + 2], kt_vals[u + 3]);
+        }
+        if (half == 0) ((float *)(blk + OFF_GM))[ch] = __expf(Gn);
+    }
+    // the six tiles of Aqk above the diagonal are zero
+    for (int e = tid; e < 6 * 64; e += 256) {
+        const int tile = e >> 6, quad = e & 63;
+        const int ti = tile < 3 ? 0 : (tile < 5 ? 1 : 2);
+        const int tj = tile < 3 ? tile + 1 : (tile < 5 ? tile - 1 : 3);
+        const int r = 16 * ti + (quad >> 2), c0 = 16 * tj + 4 * (quad & 3);
+        st_split4<F32>(blk + OFF_AQ, CH * CH, (size_t)r * CH + c0, 0.f, 0.f, 0.f, 0.f);
+    }
+    __syncthreads();
+
+    // ---- phase 2: the two decay-scaled Gram matrices on MFMA ----
+    // tile list: for mat in {kk, qk}, i in 0..3, j in 0..i (20 tiles), wave wv
+    // takes tiles wv, wv+4, ..  The product is formed transposed (column side as
+    // the A operand) so that each lane ends up with 4 consecutive columns of a row.
+    for (int tix = wv; tix < 20; tix += 4) {
+        const int mat = tix / 10, rem = tix % 10;
+        int i = 0;
+        while ((i + 1) * (i + 2) / 2 <= rem) ++i;
+        const int j = rem - i * (i + 1) / 2;
+        const IO *X = mat == 0 ? k : q;
+        const int cr = 16 * j + lr;  // column-side token (A operand row)
+        const int rr = 16 * i + lr;  // row-side token (B operand column)
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int c0 = 32 * ks + 8 * g;
+            F8 a, b;
+            const F8 kc = cr < len ? ld_io8(k + tok(cr) + c0) : F8{};
+            const F8 xr = rr < len ? ld_io8(X + tok(rr) + c0) : F8{};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float inv = __frcp_rn(sm.E1[cr * PG + c0 + e]);  // e^{R_j - G_c}
+                if (j < i) inv *= sm.PF[pair_index(i, j) * D + c0 + e];
+                a.v[e] = kc.v[e] * inv;
+                b.v[e] = xr.v[e] * sm.E1[rr * PG + c0 + e];
+            }
+            if constexpr (F32)
+                acc = mma_ff(acc, a, b);
+            else
+                acc = mma_ss(acc, split8(a), split8(b));
+        }
+        // acc[m] = M[r = rr][c = 16 j + 4 g + m]
+        const int cb = 16 * j + 4 * g;
+        float val[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int cc = cb + m;
+            if (mat == 0)
+                val[m] = cc < rr ? sm.beta[rr] * acc[m] : 0.f;
+            else
+                val[m] = cc <= rr ? acc[m] : 0.f;
+        }
+        if (mat == 0)
+            *(float4 *)&sm.Akk[rr * PT + cb] = make_float4(val[0], val[1], val[2], val[3]);
+        else
+            st_split4<F32>(blk + OFF_AQ, CH * CH, (size_t)rr * CH + cb, val[0], val[1], val[2], val[3]);
+    }
+    __syncthreads();
+
+    // ---- phase 3: T = (I + Akk)^{-1}, blocked forward substitution (in place) ----
+    // diagonal 16 x 16 blocks: lane m < 16 of wave b solves column m of block b
+    if (l < 16) {
+        const int b = wv, m = l;
+        float tcol[SUB];
+#pragma unroll
+        for (int r = 0; r < SUB; ++r) {
+            float acc = r == m ? 1.f : 0.f;
+#pragma unroll
+            for (int cc = 0; cc < r; ++cc) acc -= sm.Akk[(16 * b + r) * PT + 16 * b + cc] * tcol[cc];
+            tcol[r] = acc;
+        }
+#pragma unroll
+        for (int r = 0; r < SUB; ++r) sm.Akk[(16 * b + r) * PT + 16 * b + m] = tcol[r];
+    }
+    __syncthreads();
+    // off-diagonal blocks: T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj (fp32 MFMA, exact products)
+    for (int i = 1; i < 4; ++i) {
+        f32x4 X = {0.f, 0.f, 0.f, 0.f};
+        const int j = wv;
+        if (j < i) {
+            for (int kb = j; kb < i; ++kb) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const float a = sm.Akk[(16 * i + lr) * PT + 16 * kb + 4 * s + g];
+                    const float b = sm.Akk[(16 * kb + 4 * s + g) * PT + 16 * j + lr];
+                    X = mfma_f32(a, b, X);
+                }
+            }
+        }
+        __syncthreads();
+        if (j < i) {
+            // X is in C layout (lane holds rows 4g+m of column lr); pair k = 4g + s
+            f32x4 Y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const float a = sm.Akk[(16 * i + lr) * PT + 16 * i + 4 * g + s];
+                Y = mfma_f32(a, X[s], Y);
+            }
+#pragma unroll
+            for (int m = 0; m < 4; ++m) sm.Akk[(16 * i + 4 * g + m) * PT + 16 * j + lr] = -Y[m];
+        }
+        __syncthreads();
+    }
+
+    // ---- phase 4: W = T diag(beta) (K*Gam), U = T diag(beta) V, formed transposed ----
+    // wave wv: row tile rt = wv for W and 3 - wv for U; 8 column tiles each
+    for (int pass = 0; pass < 2; ++pass) {
+        const int rt = pass == 0 ? wv : 3 - wv;
+        const float *src = pass == 0 ? sm.KG : sm.Vt;
+        const int nks = rt < 2 ? 1 : 2;
+        const int r = 16 * rt + lr;
+        F8 tb[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int cc = 32 * ks + 8 * g + e;
+                tb[ks].v[e] = (ks < nks && cc <= r) ? sm.Akk[r * PT + cc] * sm.beta[cc] : 0.f;
+            }
+        }
+        S8 tbs[2];
+        if constexpr (!F32) {
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) tbs[ks] = split8(tb[ks]);
+        }
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                if (ks >= nks) break;
+                const F8 xa = ld_f8(&src[(16 * ct + lr) * PT + 32 * ks + 8 * g]);
+                if constexpr (F32)
+                    acc = mma_ff(acc, xa, tb[ks]);
+                else
+                    acc = mma_1s(acc, round8(xa), tbs[ks]);
+            }
+            // acc[m] = out[row r][col 16 ct + 4 g + m]
+            const size_t e0 = (size_t)r * D + 16 * ct + 4 * g;
+            if (pass == 0) {
+                if constexpr (F32) {
+                    *(float4 *)((float *)(blk + OFF_W) + e0) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+                } else {
+                    bf16x4 hv;
+                    hv[0] = (__bf16)acc[0]; hv[1] = (__bf16)acc[1];
+                    hv[2] = (__bf16)acc[2]; hv[3] = (__bf16)acc[3];
+                    *(bf16x4 *)((__bf16 *)(blk + OFF_W) + e0) = hv;
+                }
+            } else {
+                *(float4 *)((float *)(blk + OFF_U) + e0) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            }
+        }
+    }
+}
+
+// ----------------------------------------------------------------- chain --
+
+constexpr int NB = 16;  // value columns per workgroup
+
+template <bool F32>
+struct ChainSmem;
+template <>
+struct ChainSmem<false> {          // bf16 hi / lo, transposed [column][k]
+    __bf16 Sh[NB * 136], Sl[NB * 136];
+    __bf16 Dh[NB * 72], Dl[NB * 72];
+};
+template <>
+struct ChainSmem<true> {
+    float S[NB * 132];
+    float Dl[NB * 68];
+};
+
+template <typename IO>
+__global__ __launch_bounds__(256) void chain_kernel(const float *__restrict__ S0, int N, int H, Table tab,
+                                                    float *__restrict__ o, float *__restrict__ S_final) {
+    constexpr bool F32 = sizeof(IO) == 4;
+    __shared__ ChainSmem<F32> sm;
+    // XCD-aware mapping: workgroups L with equal L % 8 share an XCD (and its L2);
+    // the 8 column blocks of one (sequence, head) get equal L % 8.
+    const int L = blockIdx.x;
+    const int p = (L & 7) + 8 * (L >> 6), cb = (L >> 3) & 7;
+    if (p >= N * H) return;
+    const int n = p / H, h = p % H;
+    const int col0 = NB * cb;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, lr = l & 15;
+
+    // state slice: wave w owns key rows [32w, 32w+32) as two 16-row tiles (C layout)
+    f32x4 Sr[2];
+    const size_t sbase = ((size_t)n * H + h) * D * D;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            Sr[u][m] = S0 ? S0[sbase + (size_t)(32 * w + 16 * u + 4 * g + m) * D + col0 + lr] : 0.f;
+
+    const int cbeg = tab.chunk_off[n], cend = tab.chunk_off[n + 1];
+    const int64_t sstart = tab.seq_start[n], send = tab.seq_end[n];
+    const int nks_aq = w < 2 ? 1 : 2;  // 32-token k-steps of Aqk row tile w
+
+    for (int c = cbeg; c < cend; ++c) {
+        const char *blk = tab.blocks + ((size_t)c * H + h) * BLK_BYTES;
+        const int64_t t0 = sstart + (int64_t)(c - cbeg) * CH;
+        const int len = (int)min((int64_t)CH, send - t0);
+
+        // (1) publish the state slice as the B operand of W S and Q~ S
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int r0 = 32 * w + 16 * u + 4 * g;
+            if constexpr (F32) {
+                *(float4 *)&sm.S[lr * 132 + r0] = make_float4(Sr[u][0], Sr[u][1], Sr[u][2], Sr[u][3]);
+            } else {
+                bf16x4 hv, lv;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    hv[m] = (__bf16)Sr[u][m];
+                    lv[m] = (__bf16)(Sr[u][m] - (float)hv[m]);
+                }
+                *(bf16x4 *)&sm.Sh[lr * 136 + r0] = hv;
+                *(bf16x4 *)&sm.Sl[lr * 136 + r0] = lv;
+            }
+        }
+        __syncthreads();
+
+        // (2) Delta rows [16w, 16w+16) = U - W S ;  O = Q~ S
+        f32x4 ws = {0.f, 0.f, 0.f, 0.f}, oacc = {0.f, 0.f, 0.f, 0.f};
+        const int row = 16 * w + lr;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int k0 = 32 * ks + 8 * g;
+            if constexpr (F32) {
+                const F8 sb = ld_f8(&sm.S[lr * 132 + k0]);
+                ws = mma_ff(ws, ld_f8((const float *)(blk + OFF_W) + row * D + k0), sb);
+                oacc = mma_ff(oacc, ld_f8((const float *)(blk + OFF_QT) + row * D + k0), sb);
+            } else {
+                S8 sb;
+                sb.hi = ld_b8(&sm.Sh[lr * 136 + k0]);
+                sb.lo = ld_b8(&sm.Sl[lr * 136 + k0]);
+                ws = mma_11(ws, ld_b8((const __bf16 *)(blk + OFF_W) + row * D + k0), sb.hi);
+                S8 qa;
+                qa.hi = ld_b8((const __bf16 *)(blk + OFF_QT) + row * D + k0);
+                qa.lo = ld_b8((const __bf16 *)(blk + OFF_QT) + CH * D + row * D + k0);
+                oacc = mma_ss(oacc, qa, sb);
+            }
+        }
+        f32x4 dl;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            dl[m] = ((const float *)(blk + OFF_U))[(16 * w + 4 * g + m) * D + col0 + lr] - ws[m];
+
+        // (3) publish Delta as the B operand of Aqk Delta and K~^T Delta
+        {
+            const int r0 = 16 * w + 4 * g;
+            if constexpr (F32) {
+                *(float4 *)&sm.Dl[lr * 68 + r0] = make_float4(dl[0], dl[1], dl[2], dl[3]);
+            } else {
+                bf16x4 hv, lv;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    hv[m] = (__bf16)dl[m];
+                    lv[m] = (__bf16)(dl[m] - (float)hv[m]);
+                }
+                *(bf16x4 *)&sm.Dh[lr * 72 + r0] = hv;
+                *(bf16x4 *)&sm.Dl[lr * 72 + r0] = lv;
+            }
+        }
+        __syncthreads();
+
+        // Delta fragments for the two 32-token k-steps
+        F8 dF[2];
+        S8 dS[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int k0 = 32 * ks + 8 * g;
+            if constexpr (F32) {
+                dF[ks] = ld_f8(&sm.Dl[lr * 68 + k0]);
+            } else {
+                dS[ks].hi = ld_b8(&sm.Dh[lr * 72 + k0]);
+                dS[ks].lo = ld_b8(&sm.Dl[lr * 72 + k0]);
+            }
+        }
+        // (4) O += Aqk Delta  (row tile w; Aqk is zero above the diagonal)
+        for (int ks = 0; ks < nks_aq; ++ks) {
+            const int k0 = 32 * ks + 8 * g;
+            if constexpr (F32) {
+                oacc = mma_ff(oacc, ld_f8((const float *)(blk + OFF_AQ) + row * CH + k0), dF[ks]);
+            } else {
+                S8 aa;
+                aa.hi = ld_b8((const __bf16 *)(blk + OFF_AQ) + row * CH + k0);
+                aa.lo = ld_b8((const __bf16 *)(blk + OFF_AQ) + CH * CH + row * CH + k0);
+                oacc = mma_ss(oacc, aa, dS[ks]);
+            }
+        }
+        // (5) S <- Diag(gamma) S + K~^T Delta  (key rows [32w, 32w+32))
+        const float *gam = (const float *)(blk + OFF_GM);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int kr = 32 * w + 16 * u;
+            f32x4 acc;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) acc[m] = gam[kr + 4 * g + m] * Sr[u][m];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const int k0 = 32 * ks + 8 * g;
+                if constexpr (F32) {
+                    acc = mma_ff(acc, ld_f8((const float *)(blk + OFF_KT) + (kr + lr) * CH + k0), dF[ks]);
+                } else {
+                    S8 ka;
+                    ka.hi = ld_b8((const __bf16 *)(blk + OFF_KT) + (kr + lr) * CH + k0);
+                    ka.lo = ld_b8((const __bf16 *)(blk + OFF_KT) + D * CH + (kr + lr) * CH + k0);
+                    acc = mma_ss(acc, ka, dS[ks]);
+                }
+            }
+            Sr[u] = acc;
+        }
+        // (6) output rows of this chunk
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int t = 16 * w + 4 * g + m;
+            if (t < len) o[((size_t)(t0 + t) * H + h) * D + col0 + lr] = oacc[m];
+        }
+    }
+    if (S_final) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                S_final[sbase + (size_t)(32 * w + 16 * u + 4 * g + m) * D + col0 + lr] = Sr[u][m];
+    }
+}
+
+// ------------------------------------------------------------------ host --
+
+size_t prefill_workspace_bytes(int64_t T_total, int N, int H) {
+    return table_bytes(N) + (size_t)max_chunks(T_total, N) * (size_t)H * BLK_BYTES;
+}
+
+int launch_prefill(const void *q, const void *k, const void *v, bool f32io, const float *z, const float *beta,
+                   const float *A, const float *S0, const int32_t *cu, int B, int64_t T, int H, int N,
+                   float *o, float *S_final, void *ws, hipStream_t stream) {
+    const int64_t T_total = (int64_t)B * T;
+    Table tab = carve(ws, N);
+    hipLaunchKernelGGL(prep_kernel, dim3(1), dim3(256), 0, stream, cu, N, T_total, cu ? (int64_t)0 : T, tab);
+    const int64_t nc = max_chunks(T_total, N);
+    if (T_total > 0) {
+        const size_t smem = sizeof(IntraSmem<float>);
+        if (f32io) {
+            hipLaunchKernelGGL(intra_kernel<float>, dim3((unsigned)nc, (unsigned)H), dim3(256), smem, stream,
+                               (const float *)q, (const float *)k, (const float *)v, z, beta, A, N, H, tab);
+        } else {
+            hipLaunchKernelGGL(intra_kernel<__bf16>, dim3((unsigned)nc, (unsigned)H), dim3(256), smem, stream,
+                               (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, z, beta, A, N, H, tab);
+        }
+    }
+    const int64_t pairs = (int64_t)N * H;
+    const unsigned nwg = (unsigned)(64 * ((pairs + 7) / 8));
+    if (f32io)
+        hipLaunchKernelGGL(chain_kernel<float>, dim3(nwg), dim3(256), 0, stream, S0, N, H, tab, o, S_final);
+    else
+        hipLaunchKernelGGL(chain_kernel<__bf16>, dim3(nwg), dim3(256), 0, stream, S0, N, H, tab, o, S_final);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int set_prefill_attributes() {
+    const int smem = (int)sizeof(IntraSmem<float>);
+    if (hipFuncSetAttribute((const void *)intra_kernel<float>, hipFuncAttributeMaxDynamicSharedMemorySize, smem) !=
+        hipSuccess)
+        return -1;
+    if (hipFuncSetAttribute((const void *)intra_kernel<__bf16>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            smem) != hipSuccess)
+        return -1;
+    return 0;
+}
+
+}  // namespace kda

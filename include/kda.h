@@ -1,0 +1,140 @@
+/*
+ * kda.h -- C ABI of libkda.so, the MI355X (gfx950) Kimi Delta Attention operator.
+ *
+ * The operator (pages: "Kimi Linear: An Expressive, Efficient Attention
+ * Architecture" summary, section 3; "Kimi K3 architecture", sequence-bottleneck
+ * section) updates, per head, a d_k x d_v state
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,
+ *     o_t = S_t^T q_t,
+ *     alpha_t = exp(g_t),  g_t = -5 * Sigmoid(exp(A_h) * z_t)   (per key channel),
+ *
+ * decaying first and then applying the delta-rule correction.  Prefill uses the
+ * chunkwise form (Kimi Linear summary, sections 3.1 and 6.3, appendix C:
+ * chunk size 64, WY / UT transform with a forward-substitution inverse, 16-token
+ * sub-chunks, inter-chunk state recurrence); generation uses the recurrent
+ * single-token update (section 6.3).
+ *
+ * Conventions shared by every entry point
+ *   - Head dims are fixed: d_k = d_v = 128 (Kimi Linear summary, sections 4 and
+ *     6.3).  Any other value returns KDA_ERR_SHAPE.
+ *   - Every tensor pointer is a device pointer owned by the caller; the library
+ *     allocates no device memory and keeps no mutable global state.
+ *   - Layouts are dense, row-major, innermost dimension last:
+ *       q, k, z : [tokens, H, 128]   v, o : [tokens, H, 128]
+ *       beta    : [tokens, H]        A    : [H]
+ *       states  : [N, H, 128, 128] with rows = key channel, columns = value channel.
+ *   - q, k and v are bf16 (KDA_BF16) or fp32 (KDA_F32); z, beta, A, the states
+ *     and o are always fp32.
+ *   - q and k are expected to be L2-normalised by the caller (the KDA layer
+ *     normalises them before the operator); the operator does not normalise and
+ *     applies no query scale.
+ *   - beta is the final delta strength (already squashed into (0, 1)).
+ *   - z = -inf gives alpha = 1 exactly and z = +inf gives alpha = e^-5; both are
+ *     valid.  NaN inputs propagate to the outputs.
+ *   - Pointers must be 16-byte aligned (KDA_ERR_ALIGN otherwise).
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream).  Arguments are validated on the host before any launch; a
+ *     launch failure returns KDA_ERR_HIP; faults during execution surface at the
+ *     caller's next synchronisation.  Nothing is thrown across the ABI.
+ *   - Calls on different streams are independent as long as they use distinct
+ *     outputs and distinct workspaces.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
+
+enum {
+    KDA_OK = 0,
+    KDA_ERR_NULL = -1,      /* a required pointer is NULL                          */
+    KDA_ERR_SHAPE = -2,     /* dk or dv != 128, or a negative / inconsistent size  */
+    KDA_ERR_DTYPE = -3,     /* qkv_dtype is not a kda_dtype                        */
+    KDA_ERR_SEQLENS = -4,   /* cu_seqlens given with B != 1, or n_seqs < 1         */
+    KDA_ERR_ALIGN = -5,     /* a pointer is not 16-byte aligned                    */
+    KDA_ERR_WORKSPACE = -6, /* workspace NULL or smaller than required             */
+    KDA_ERR_HIP = -7,       /* a HIP launch failed                                 */
+    KDA_ERR_ALIAS = -8      /* o overlaps an input                                 */
+};
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *kda_status_str(int status);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int kda_version(void);
+
+/*
+ * Bytes of device workspace kda_chunk_fwd needs for T_total packed tokens in
+ * n_seqs sequences and H heads (0 for an empty problem).  The workspace holds
+ * the per-chunk intermediates of the chunkwise form (WY vectors, decay-scaled
+ * keys and queries, the intra-chunk query-key matrix, the chunk decay) and a
+ * small sequence / chunk table.  Its contents are scratch between calls.
+ * Returns 0 and writes nothing when the sizes are invalid.
+ */
+size_t kda_chunk_fwd_workspace_bytes(int64_t T_total, int32_t n_seqs, int32_t H);
+
+/*
+ * Chunkwise KDA prefill (Kimi Linear summary, sections 3.1 and 6.3; appendix C
+ * chunk_kda(q, k, v, g, beta, initial_state, chunk_size=64), here with the
+ * Kimi K3 gate fused: the operator takes z and A instead of g).
+ *
+ * Sequences:
+ *   cu_seqlens == NULL: B sequences of T tokens each; tensors are [B, T, H, 128]
+ *                       and n_seqs must equal B.
+ *   cu_seqlens != NULL: B must be 1; the token axis packs n_seqs sequences;
+ *                       cu_seqlens is a DEVICE int32 array of n_seqs + 1
+ *                       offsets, cu_seqlens[0] = 0, non-decreasing,
+ *                       cu_seqlens[n_seqs] = T.  Its contents are not read on
+ *                       the host: offsets outside [0, T] are clamped and a
+ *                       decreasing entry gives an empty sequence, so malformed
+ *                       offsets give wrong results but never out-of-bounds
+ *                       accesses.
+ *   Each sequence starts from its own initial state and its chunk grid starts
+ *   at its first token; its last chunk may be partial.  Zero-length sequences
+ *   are allowed (S_final = S0).
+ *
+ * Arguments:
+ *   q, k, v     [B*T, H, 128] of qkv_dtype          (input)
+ *   g_raw       [B*T, H, 128] fp32, z of the gate    (input)
+ *   beta        [B*T, H] fp32                        (input)
+ *   A           [H] fp32, the gate uses exp(A[h])    (input)
+ *   S0          [n_seqs, H, 128, 128] fp32 or NULL (= zeros)            (input)
+ *   o           [B*T, H, 128] fp32; must not overlap any input         (output)
+ *   S_final     [n_seqs, H, 128, 128] fp32 or NULL; may alias S0       (output)
+ *   workspace   device scratch of workspace_bytes >=
+ *               kda_chunk_fwd_workspace_bytes(B*T, n_seqs, H)
+ *   stream      hipStream_t
+ */
+int kda_chunk_fwd(const void *q, const void *k, const void *v, kda_dtype qkv_dtype,
+                  const float *g_raw, const float *beta, const float *A, const float *S0,
+                  const int32_t *cu_seqlens, int32_t B, int64_t T, int32_t H, int32_t n_seqs,
+                  int32_t dk, int32_t dv, float *o, float *S_final, void *workspace,
+                  size_t workspace_bytes, void *stream);
+
+/*
+ * One recurrent decode step for N independent sequences (Kimi Linear summary,
+ * section 6.3: generation uses the recurrent update; each head keeps a fixed
+ * 128 x 128 state).  For every (n, h): alpha from z, S' = Diag(alpha) S,
+ * delta = beta (v - S'^T k), S <- S' + k delta^T, o = S^T q.  S is read and
+ * written once, in place.
+ *
+ *   q, k, v  [N, H, 128] of qkv_dtype; g_raw [N, H, 128] fp32; beta [N, H] fp32;
+ *   A [H] fp32; S [N, H, 128, 128] fp32 (in/out); o [N, H, 128] fp32 (output,
+ *   must not overlap S or an input).
+ */
+int kda_decode_step(const void *q, const void *k, const void *v, kda_dtype qkv_dtype,
+                    const float *g_raw, const float *beta, const float *A, float *S, int32_t N,
+                    int32_t H, int32_t dk, int32_t dv, float *o, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

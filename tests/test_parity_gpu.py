@@ -1,0 +1,185 @@
+"""GPU parity of the HIP path against the CPU oracle (fp64 token recurrence).
+
+Bars (stated for the operator): max|o - o_ref| / RMS(o_ref) <= 1e-2 and the same
+for S_final with bf16 q/k/v; <= 1e-4 with fp32 q/k/v.  Inputs come from the
+seeded generator in synth/, identical bits on both sides.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_helpers import DEV, err, run_prefill, say, to_dev
+
+import gated_delta_rule_29_amd as kda
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 1e-2, "f32": 1e-4}
+
+
+def check(d, o, Sf, cu=None, io="bf16", label=""):
+    o_ref, S_ref = oracle.recurrent(d["q"], d["k"], d["v"], d["z"], d["beta"], d["A"], d.get("S0"), cu)
+    eo, es = err(o, o_ref), err(Sf, S_ref)
+    say(f"  {label} err_o={eo:.3e} err_S={es:.3e}")
+    assert eo <= TOL[io] and es <= TOL[io], (eo, es)
+    return eo, es
+
+
+def test_tiny_one_chunk_fp32():
+    """B=1, H=1, T=64 (one chunk = four sub-chunks), fp32 I/O, S0 = 0."""
+    w = synth.WORKLOADS["tiny_f32"]
+    d = synth.prefill_inputs(w["seed"], 64, 1, dtype="f32")
+    say("case tiny_f32 T=64 H=1")
+    o, Sf = run_prefill(d, S0=d["S0"], io="f32")
+    check(d, o, Sf, io="f32", label="tiny_f32")
+
+
+def test_prefill_2k_bf16():
+    """B=1, H=16, T=2048 (32 chunks), bf16 q/k/v, S0 = 0."""
+    w = synth.WORKLOADS["prefill_2k"]
+    d = synth.prefill_inputs(w["seed"], 2048, 16, dtype="bf16")
+    say("case prefill_2k T=2048 H=16")
+    o, Sf = run_prefill(d, S0=None)
+    check(d, o, Sf, label="prefill_2k")
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("T", [1, 9, 15, 16, 17, 63, 64, 65, 777])
+def test_ragged_lengths(T, io):
+    d = synth.prefill_inputs(2000 + T, T, 2, dtype=io, z_scale=1.5, s0_std=0.02)
+    say(f"case ragged T={T} io={io}")
+    o, Sf = run_prefill(d, S0=d["S0"], io=io)
+    check(d, o, Sf, io=io, label=f"T={T}")
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_varlen_pack(io):
+    lens = [100, 37, 64, 1, 0, 200, 129]
+    cu = synth.cu_seqlens(lens)
+    d = synth.prefill_inputs(3000, int(cu[-1]), 3, dtype=io, s0_std=0.02, n_seqs=len(lens))
+    say(f"case varlen {lens} io={io}")
+    o, Sf = run_prefill(d, cu=cu, S0=d["S0"], io=io)
+    check(d, o, Sf, cu=cu, io=io, label="varlen")
+    assert np.array_equal(Sf[4], d["S0"][4])  # the empty sequence keeps its state exactly
+
+
+def test_batched_without_cu_seqlens():
+    B, T, H = 3, 70, 2
+    d = synth.prefill_inputs(3100, B * T, H, s0_std=0.02, n_seqs=B)
+    say("case batched B=3 T=70")
+    dt = torch.bfloat16
+    shp = (B, T, H, 128)
+    q, k, v = (to_dev(d[n].reshape(shp), dt) for n in ("q", "k", "v"))
+    z = to_dev(d["z"].reshape(shp), torch.float32)
+    beta = to_dev(d["beta"].reshape(B, T, H), torch.float32)
+    o, Sf = kda.kda_chunk_fwd(q, k, v, z, beta, to_dev(d["A"], torch.float32), to_dev(d["S0"], torch.float32))
+    torch.cuda.synchronize()
+    check(d, o.cpu().numpy().reshape(B * T, H, 128), Sf.cpu().numpy(), cu=synth.cu_seqlens([T] * B),
+          label="batched")
+
+
+def test_state_aliasing_and_split_resume():
+    """S_final may alias S0; a call resumed from a previous S_final continues the sequence
+    (chunk-aligned and unaligned splits)."""
+    T = 300
+    d = synth.prefill_inputs(3200, T, 2, s0_std=0.02)
+    o_ref, S_ref = oracle.recurrent(d["q"], d["k"], d["v"], d["z"], d["beta"], d["A"], d["S0"])
+    for split in (128, 100):
+        say(f"case split-resume split={split}")
+        p1 = {n: d[n][:split] for n in ("q", "k", "v", "z", "beta")}
+        p2 = {n: d[n][split:] for n in ("q", "k", "v", "z", "beta")}
+        p1["A"] = p2["A"] = d["A"]
+        S = to_dev(d["S0"], torch.float32)
+        outs = []
+        for part in (p1, p2):
+            dt = torch.bfloat16
+            q, k, v = (to_dev(part[n], dt) for n in ("q", "k", "v"))
+            o, _ = kda.kda_chunk_fwd(q, k, v, to_dev(part["z"], torch.float32), to_dev(part["beta"], torch.float32),
+                                     to_dev(part["A"], torch.float32), S, None, S_final=S)
+            outs.append(o)
+        torch.cuda.synchronize()
+        o = torch.cat(outs).cpu().numpy()
+        assert err(o, o_ref) <= 1e-2 and err(S.cpu().numpy(), S_ref) <= 1e-2
+
+
+@pytest.mark.parametrize("mode", ["minus_inf", "plus_inf", "mixed"])
+def test_gate_infinities(mode):
+    """z = -inf gives alpha = 1, z = +inf gives alpha = e^-5; both are valid inputs."""
+    d = synth.prefill_inputs(3300, 150, 2, s0_std=0.02)
+    if mode == "minus_inf":
+        d["z"][:] = -np.inf
+    elif mode == "plus_inf":
+        d["z"][:] = np.inf
+    else:
+        d["z"][::3] = np.inf
+        d["z"][1::3] = -np.inf
+    say(f"case gate {mode}")
+    o, Sf = run_prefill(d, S0=d["S0"])
+    assert np.isfinite(o).all() and np.isfinite(Sf).all()
+    check(d, o, Sf, label=mode)
+
+
+def test_frozen_state():
+    """beta = 0 and z = -inf: the state is unchanged and o_t = S0^T q_t."""
+    d = synth.prefill_inputs(3400, 130, 2, s0_std=0.02)
+    d["z"][:] = -np.inf
+    d["beta"][:] = 0.0
+    say("case frozen state")
+    o, Sf = run_prefill(d, S0=d["S0"])
+    assert np.array_equal(Sf, d["S0"])
+    ref = np.einsum("thi,hij->thj", d["q"].astype(np.float64), d["S0"][0].astype(np.float64))
+    assert err(o, ref) < 1e-4
+
+
+def test_deterministic():
+    d = synth.prefill_inputs(3500, 500, 4, s0_std=0.02)
+    say("case determinism")
+    o1, S1 = run_prefill(d, S0=d["S0"])
+    o2, S2 = run_prefill(d, S0=d["S0"])
+    assert np.array_equal(o1, o2) and np.array_equal(S1, S2)
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_decode_matches_oracle(io):
+    N, H, steps = 16, 4, 6
+    S0 = synth.initial_state(3600, N, H, 0.02)
+    A = synth.head_params(3600, H)
+    S_ref = S0.astype(np.float64)
+    dt = torch.bfloat16 if io == "bf16" else torch.float32
+    S = to_dev(S0, torch.float32)
+    Ad = to_dev(A, torch.float32)
+    say(f"case decode N={N} H={H} io={io}")
+    for step in range(steps):
+        x = synth.decode_tokens(3600, step, N, H, dtype=io)
+        o = kda.kda_decode_step(to_dev(x["q"], dt), to_dev(x["k"], dt), to_dev(x["v"], dt),
+                                to_dev(x["z"], torch.float32), to_dev(x["beta"], torch.float32), Ad, S)
+        o_ref, S_ref = oracle.decode_step(x["q"], x["k"], x["v"], x["z"], x["beta"], A, S_ref)
+        torch.cuda.synchronize()
+        assert err(o.cpu().numpy(), o_ref) <= TOL[io]
+    assert err(S.cpu().numpy(), S_ref) <= TOL[io]
+
+
+def test_decode_steps_continue_prefill():
+    """Prefill the first tokens, then decode the rest one by one from its final state."""
+    T, Tp, H = 90, 70, 2
+    d = synth.prefill_inputs(3700, T, H, s0_std=0.02)
+    o_ref, S_ref = oracle.recurrent(d["q"], d["k"], d["v"], d["z"], d["beta"], d["A"], d["S0"])
+    say("case prefill + decode")
+    dt = torch.bfloat16
+    part = {n: d[n][:Tp] for n in ("q", "k", "v", "z", "beta")}
+    S = to_dev(d["S0"], torch.float32)
+    Ad = to_dev(d["A"], torch.float32)
+    o_p, _ = kda.kda_chunk_fwd(to_dev(part["q"], dt), to_dev(part["k"], dt), to_dev(part["v"], dt),
+                               to_dev(part["z"], torch.float32), to_dev(part["beta"], torch.float32), Ad, S, None,
+                               S_final=S)
+    outs = [o_p]
+    for t in range(Tp, T):
+        sl = slice(t, t + 1)
+        outs.append(kda.kda_decode_step(to_dev(d["q"][sl], dt), to_dev(d["k"][sl], dt), to_dev(d["v"][sl], dt),
+                                        to_dev(d["z"][sl], torch.float32), to_dev(d["beta"][sl], torch.float32),
+                                        Ad, S))
+    torch.cuda.synchronize()
+    o = torch.cat(outs).cpu().numpy()
+    assert err(o, o_ref) <= 1e-2 and err(S.cpu().numpy(), S_ref) <= 1e-2
