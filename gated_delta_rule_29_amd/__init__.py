@@ -57,6 +57,8 @@ def load():
     lib.kda_chunk_fwd.argtypes = [P, P, P, ctypes.c_int, P, P, P, P, P, i32, i64, i32, i32, i32, i32, P, P, P,
                                   sz, P]
     lib.kda_chunk_fwd.restype = ctypes.c_int
+    lib.kda_chunk_fwd_timed.argtypes = lib.kda_chunk_fwd.argtypes + [P]
+    lib.kda_chunk_fwd_timed.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [P, P, P, ctypes.c_int, P, P, P, P, i32, i32, i32, i32, P, P]
     lib.kda_decode_step.restype = ctypes.c_int
     _lib = lib
@@ -98,13 +100,14 @@ def kda_chunk_fwd_workspace_bytes(T_total: int, n_seqs: int, H: int) -> int:
 
 
 def kda_chunk_fwd(q, k, v, g_raw, beta, A, S0=None, cu_seqlens=None, *, o=None, S_final=None,
-                  workspace=None, stream=None, return_final_state=True):
+                  workspace=None, stream=None, return_final_state=True, stage_events=None):
     """Chunkwise KDA prefill.
 
     q, k, v: [B, T, H, 128] (or [T, H, 128]) bf16 or fp32; g_raw: same shape fp32 (the gate's z);
     beta: [B, T, H] fp32; A: [H] fp32; S0: [N, H, 128, 128] fp32 or None (zeros);
     cu_seqlens: int32 device tensor [N+1] packing N sequences along T (then B must be 1).
     Returns (o [.., H, 128] fp32, S_final [N, H, 128, 128] fp32 or None).
+    stage_events: optional ctypes array of four hipEvent_t recorded around the library's stages.
     """
     lib = load()
     squeeze = q.dim() == 3
@@ -145,9 +148,13 @@ def kda_chunk_fwd(q, k, v, g_raw, beta, A, S0=None, cu_seqlens=None, *, o=None, 
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     dtype = KDA_BF16 if q.dtype == torch.bfloat16 else KDA_F32
-    rc = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), dtype, _ptr(g_raw), _ptr(beta), _ptr(A), _ptr(S0),
-                           _ptr(cu_seqlens), B, T, H, N, dk, dv, _ptr(o), _ptr(S_final), _ptr(workspace),
-                           workspace.numel() * workspace.element_size(), _stream(stream))
+    args = (_ptr(q), _ptr(k), _ptr(v), dtype, _ptr(g_raw), _ptr(beta), _ptr(A), _ptr(S0),
+            _ptr(cu_seqlens), B, T, H, N, dk, dv, _ptr(o), _ptr(S_final), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(stream))
+    if stage_events is None:
+        rc = lib.kda_chunk_fwd(*args)
+    else:
+        rc = lib.kda_chunk_fwd_timed(*args, ctypes.cast(stage_events, ctypes.c_void_p))
     _check(rc, "kda_chunk_fwd")
     if squeeze:
         o = o.squeeze(0)

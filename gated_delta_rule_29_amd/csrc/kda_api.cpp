@@ -16,7 +16,7 @@ int launch_decode(const void *q, const void *k, const void *v, bool f32io, const
                   const float *A, float *S, int N, int H, float *o, hipStream_t stream);
 int launch_prefill(const void *q, const void *k, const void *v, bool f32io, const float *z, const float *beta,
                    const float *A, const float *S0, const int32_t *cu, int B, int64_t T, int H, int N,
-                   float *o, float *S_final, void *ws, hipStream_t stream);
+                   float *o, float *S_final, void *ws, hipStream_t stream, hipEvent_t *ev);
 size_t prefill_workspace_bytes(int64_t T_total, int N, int H);
 int set_prefill_attributes();
 }  // namespace kda
@@ -62,11 +62,11 @@ KDA_EXPORT size_t kda_chunk_fwd_workspace_bytes(int64_t T_total, int32_t n_seqs,
     return kda::prefill_workspace_bytes(T_total, n_seqs, H);
 }
 
-KDA_EXPORT int kda_chunk_fwd(const void *q, const void *k, const void *v, kda_dtype qkv_dtype,
-                             const float *g_raw, const float *beta, const float *A, const float *S0,
-                             const int32_t *cu_seqlens, int32_t B, int64_t T, int32_t H, int32_t n_seqs,
-                             int32_t dk, int32_t dv, float *o, float *S_final, void *workspace,
-                             size_t workspace_bytes, void *stream) {
+KDA_EXPORT int kda_chunk_fwd_timed(const void *q, const void *k, const void *v, kda_dtype qkv_dtype,
+                                   const float *g_raw, const float *beta, const float *A, const float *S0,
+                                   const int32_t *cu_seqlens, int32_t B, int64_t T, int32_t H, int32_t n_seqs,
+                                   int32_t dk, int32_t dv, float *o, float *S_final, void *workspace,
+                                   size_t workspace_bytes, void *stream, void *const *stage_events) {
     if (dk != kD || dv != kD) return KDA_ERR_SHAPE;
     if (B < 0 || T < 0 || H < 0 || n_seqs < 0) return KDA_ERR_SHAPE;
     if (qkv_dtype != KDA_BF16 && qkv_dtype != KDA_F32) return KDA_ERR_DTYPE;
@@ -99,8 +99,18 @@ KDA_EXPORT int kda_chunk_fwd(const void *q, const void *k, const void *v, kda_dt
     std::call_once(g_attr_once, [] { g_attr_status = kda::set_prefill_attributes(); });
     if (g_attr_status != 0) return KDA_ERR_HIP;
     const int rc = kda::launch_prefill(q, k, v, qkv_dtype == KDA_F32, g_raw, beta, A, S0, cu_seqlens, B, T, H,
-                                       n_seqs, o, S_final, workspace, (hipStream_t)stream);
+                                       n_seqs, o, S_final, workspace, (hipStream_t)stream,
+                                       (hipEvent_t *)stage_events);
     return rc == 0 ? KDA_OK : KDA_ERR_HIP;
+}
+
+KDA_EXPORT int kda_chunk_fwd(const void *q, const void *k, const void *v, kda_dtype qkv_dtype,
+                             const float *g_raw, const float *beta, const float *A, const float *S0,
+                             const int32_t *cu_seqlens, int32_t B, int64_t T, int32_t H, int32_t n_seqs,
+                             int32_t dk, int32_t dv, float *o, float *S_final, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+    return kda_chunk_fwd_timed(q, k, v, qkv_dtype, g_raw, beta, A, S0, cu_seqlens, B, T, H, n_seqs, dk, dv, o,
+                               S_final, workspace, workspace_bytes, stream, nullptr);
 }
 
 KDA_EXPORT int kda_decode_step(const void *q, const void *k, const void *v, kda_dtype qkv_dtype,

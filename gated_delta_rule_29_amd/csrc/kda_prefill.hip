@@ -618,11 +618,13 @@ size_t prefill_workspace_bytes(int64_t T_total, int N, int H) {
 
 int launch_prefill(const void *q, const void *k, const void *v, bool f32io, const float *z, const float *beta,
                    const float *A, const float *S0, const int32_t *cu, int B, int64_t T, int H, int N,
-                   float *o, float *S_final, void *ws, hipStream_t stream) {
+                   float *o, float *S_final, void *ws, hipStream_t stream, hipEvent_t *ev) {
     const int64_t T_total = (int64_t)B * T;
     Table tab = carve(ws, N);
+    if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return -1;
     hipLaunchKernelGGL(prep_kernel, dim3(1), dim3(256), 0, stream, cu, N, T_total, cu ? (int64_t)0 : T, tab);
     const int64_t nc = max_chunks(T_total, N);
+    if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return -1;
     if (T_total > 0) {
         const size_t smem = sizeof(IntraSmem<float>);
         if (f32io) {
@@ -633,13 +635,16 @@ int launch_prefill(const void *q, const void *k, const void *v, bool f32io, cons
                                (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, z, beta, A, N, H, tab);
         }
     }
+    if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return -1;
     const int64_t pairs = (int64_t)N * H;
     const unsigned nwg = (unsigned)(64 * ((pairs + 7) / 8));
     if (f32io)
         hipLaunchKernelGGL(chain_kernel<float>, dim3(nwg), dim3(256), 0, stream, S0, N, H, tab, o, S_final);
     else
         hipLaunchKernelGGL(chain_kernel<__bf16>, dim3(nwg), dim3(256), 0, stream, S0, N, H, tab, o, S_final);
-    return hipGetLastError() == hipSuccess ? 0 : -1;
+    if (hipGetLastError() != hipSuccess) return -1;
+    if (ev && hipEventRecord(ev[3], stream) != hipSuccess) return -1;
+    return 0;
 }
 
 int set_prefill_attributes() {

@@ -119,6 +119,20 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, kda_dtype qkv_dty
                   size_t workspace_bytes, void *stream);
 
 /*
+ * kda_chunk_fwd with stage timing: when stage_events is not NULL it points to
+ * four hipEvent_t created by the caller; they are recorded on `stream` before
+ * the sequence-table kernel, before the intra-chunk kernel, before the
+ * inter-chunk (chain) kernel and after it, so the caller can read each stage's
+ * duration with hipEventElapsedTime.  Everything else is as kda_chunk_fwd.
+ * A failing hipEventRecord returns KDA_ERR_HIP.
+ */
+int kda_chunk_fwd_timed(const void *q, const void *k, const void *v, kda_dtype qkv_dtype,
+                        const float *g_raw, const float *beta, const float *A, const float *S0,
+                        const int32_t *cu_seqlens, int32_t B, int64_t T, int32_t H, int32_t n_seqs,
+                        int32_t dk, int32_t dv, float *o, float *S_final, void *workspace,
+                        size_t workspace_bytes, void *stream, void *const *stage_events);
+
+/*
  * One recurrent decode step for N independent sequences (Kimi Linear summary,
  * section 6.3: generation uses the recurrent update; each head keeps a fixed
  * 128 x 128 state).  For every (n, h): alpha from z, S' = Diag(alpha) S,

@@ -44,9 +44,10 @@ def rng(seed: int, tensor: str, slice_id: int = 0) -> np.random.Generator:
 def bf16_round(x: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bfloat16 (ties to even); returns float32."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32).reshape(x.shape)
+    u = x.view(np.uint32)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) & np.uint32(0xFFFF0000)
+    r = np.where(np.isnan(x), u, r)  # keep NaN payloads; finite values never wrap
+    return r.view(np.float32).reshape(x.shape)
 
 
 def _unit_rows(x: np.ndarray) -> np.ndarray:
