@@ -52,7 +52,7 @@ def load():
     lib.kda_status_str.restype = ctypes.c_char_p
     lib.kda_version.argtypes = []
     lib.kda_version.restype = ctypes.c_int
-    lib.kda_chunk_fwd_workspace_bytes.argtypes = [i64, i32, i32]
+    lib.kda_chunk_fwd_workspace_bytes.argtypes = [i64, i32, i32, ctypes.c_int]
     lib.kda_chunk_fwd_workspace_bytes.restype = sz
     lib.kda_chunk_fwd.argtypes = [P, P, P, ctypes.c_int, P, P, P, P, P, i32, i64, i32, i32, i32, i32, P, P, P,
                                   sz, P]
@@ -95,8 +95,9 @@ def _need(t, name, dtypes, device):
         raise ValueError(f"{name} must be contiguous")
 
 
-def kda_chunk_fwd_workspace_bytes(T_total: int, n_seqs: int, H: int) -> int:
-    return int(load().kda_chunk_fwd_workspace_bytes(int(T_total), int(n_seqs), int(H)))
+def kda_chunk_fwd_workspace_bytes(T_total: int, n_seqs: int, H: int, dtype=torch.bfloat16) -> int:
+    code = KDA_BF16 if dtype == torch.bfloat16 else KDA_F32
+    return int(load().kda_chunk_fwd_workspace_bytes(int(T_total), int(n_seqs), int(H), code))
 
 
 def kda_chunk_fwd(q, k, v, g_raw, beta, A, S0=None, cu_seqlens=None, *, o=None, S_final=None,
@@ -107,7 +108,7 @@ def kda_chunk_fwd(q, k, v, g_raw, beta, A, S0=None, cu_seqlens=None, *, o=None, 
     beta: [B, T, H] fp32; A: [H] fp32; S0: [N, H, 128, 128] fp32 or None (zeros);
     cu_seqlens: int32 device tensor [N+1] packing N sequences along T (then B must be 1).
     Returns (o [.., H, 128] fp32, S_final [N, H, 128, 128] fp32 or None).
-    stage_events: optional ctypes array of four hipEvent_t recorded around the library's stages.
+    stage_events: optional ctypes array of five hipEvent_t recorded at the library's stage boundaries.
     """
     lib = load()
     squeeze = q.dim() == 3
@@ -144,10 +145,10 @@ def kda_chunk_fwd(q, k, v, g_raw, beta, A, S0=None, cu_seqlens=None, *, o=None, 
         o = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
     if return_final_state and S_final is None:
         S_final = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
-    need = int(lib.kda_chunk_fwd_workspace_bytes(B * T, N, H))
+    dtype = KDA_BF16 if q.dtype == torch.bfloat16 else KDA_F32
+    need = int(lib.kda_chunk_fwd_workspace_bytes(B * T, N, H, dtype))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    dtype = KDA_BF16 if q.dtype == torch.bfloat16 else KDA_F32
     args = (_ptr(q), _ptr(k), _ptr(v), dtype, _ptr(g_raw), _ptr(beta), _ptr(A), _ptr(S0),
             _ptr(cu_seqlens), B, T, H, N, dk, dv, _ptr(o), _ptr(S_final), _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream(stream))

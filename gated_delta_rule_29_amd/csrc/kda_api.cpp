@@ -17,7 +17,7 @@ int launch_decode(const void *q, const void *k, const void *v, bool f32io, const
 int launch_prefill(const void *q, const void *k, const void *v, bool f32io, const float *z, const float *beta,
                    const float *A, const float *S0, const int32_t *cu, int B, int64_t T, int H, int N,
                    float *o, float *S_final, void *ws, hipStream_t stream, hipEvent_t *ev);
-size_t prefill_workspace_bytes(int64_t T_total, int N, int H);
+size_t prefill_workspace_bytes(int64_t T_total, int N, int H, bool f32io);
 int set_prefill_attributes();
 }  // namespace kda
 
@@ -56,10 +56,11 @@ KDA_EXPORT const char *kda_status_str(int status) {
 
 KDA_EXPORT int kda_version(void) { return 100; }
 
-KDA_EXPORT size_t kda_chunk_fwd_workspace_bytes(int64_t T_total, int32_t n_seqs, int32_t H) {
+KDA_EXPORT size_t kda_chunk_fwd_workspace_bytes(int64_t T_total, int32_t n_seqs, int32_t H, kda_dtype qkv_dtype) {
     if (T_total < 0 || n_seqs < 0 || H < 0) return 0;
+    if (qkv_dtype != KDA_BF16 && qkv_dtype != KDA_F32) return 0;
     if (T_total == 0 && n_seqs == 0) return 0;
-    return kda::prefill_workspace_bytes(T_total, n_seqs, H);
+    return kda::prefill_workspace_bytes(T_total, n_seqs, H, qkv_dtype == KDA_F32);
 }
 
 KDA_EXPORT int kda_chunk_fwd_timed(const void *q, const void *k, const void *v, kda_dtype qkv_dtype,
@@ -83,7 +84,7 @@ KDA_EXPORT int kda_chunk_fwd_timed(const void *q, const void *k, const void *v, 
     const void *ptrs[] = {q, k, v, g_raw, beta, A, S0, o, S_final, workspace};
     for (const void *p : ptrs)
         if (misaligned(p)) return KDA_ERR_ALIGN;
-    const size_t need = kda_chunk_fwd_workspace_bytes(T_total, n_seqs, H);
+    const size_t need = kda_chunk_fwd_workspace_bytes(T_total, n_seqs, H, qkv_dtype);
     if (!workspace || workspace_bytes < need) return KDA_ERR_WORKSPACE;
     const size_t esz = qkv_dtype == KDA_F32 ? 4 : 2;
     const size_t tok = (size_t)T_total * H;

@@ -24,6 +24,8 @@ constexpr int CH = 64;      // chunk length (section 6.3, appendix C)
 constexpr int SUB = 16;     // sub-chunk length (Kimi K3: 16-token tiles)
 constexpr float GMIN = -5.f;  // Kimi K3 lower bound of the log-decay
 
+__host__ __device__ constexpr size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
 __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -101,18 +103,12 @@ __device__ __forceinline__ F8 ld_io8(const __bf16 *p) {
 __device__ __forceinline__ float to_f(float x) { return x; }
 __device__ __forceinline__ float to_f(__bf16 x) { return (float)x; }
 
-// Kimi K3 gate: g = g_min * Sigmoid(e^A z), written so that z = +-inf gives
-// exactly g_min / 0 and NaN propagates.
+// Kimi K3 gate: g = g_min * Sigmoid(e^A z) with Sigmoid(x) = 1 / (1 + e^-x)
+// evaluated as v_rcp(1 + v_exp): x = +inf gives exactly g_min, x = -inf gives
+// e^-x = inf and exactly 0, NaN propagates.  v_rcp_f32 is accurate to 1 ulp.
 __device__ __forceinline__ float kda_gate(float expA, float z) {
-    float x = expA * z;
-    float s;
-    if (x >= 0.f) {
-        s = 1.f / (1.f + __expf(-x));
-    } else {
-        float e = __expf(x);
-        s = e / (1.f + e);
-    }
-    return GMIN * s;
+    const float x = expA * z;
+    return GMIN * __builtin_amdgcn_rcpf(1.f + __expf(-x));
 }
 
 }  // namespace kda

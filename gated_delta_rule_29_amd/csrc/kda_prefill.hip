@@ -612,13 +612,25 @@ __global__ __launch_bounds__(256) void chain_kernel(const float *__restrict__ S0
 
 // ------------------------------------------------------------------ host --
 
-size_t prefill_workspace_bytes(int64_t T_total, int N, int H) {
+size_t seg_workspace_bytes(int64_t T_total, int N, int H);
+int launch_segment_prefill(const __bf16 *q, const __bf16 *k, const __bf16 *v, const float *z, const float *beta,
+                           const float *A, const float *S0, const int32_t *cu, int B, int64_t T, int H, int N,
+                           float *o, float *S_final, void *ws, hipStream_t stream, hipEvent_t *ev);
+int set_segment_attributes();
+
+// bf16 q/k/v run the segment-parallel fused path (kda_segment.hip); fp32 q/k/v
+// run the three-kernel path below with exact fp32 MFMA products.
+size_t prefill_workspace_bytes(int64_t T_total, int N, int H, bool f32io) {
+    if (!f32io) return seg_workspace_bytes(T_total, N, H);
     return table_bytes(N) + (size_t)max_chunks(T_total, N) * (size_t)H * BLK_BYTES;
 }
 
 int launch_prefill(const void *q, const void *k, const void *v, bool f32io, const float *z, const float *beta,
                    const float *A, const float *S0, const int32_t *cu, int B, int64_t T, int H, int N,
                    float *o, float *S_final, void *ws, hipStream_t stream, hipEvent_t *ev) {
+    if (!f32io)
+        return launch_segment_prefill((const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, z, beta, A, S0, cu, B,
+                                      T, H, N, o, S_final, ws, stream, ev);
     const int64_t T_total = (int64_t)B * T;
     Table tab = carve(ws, N);
     if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return -1;
@@ -644,10 +656,12 @@ int launch_prefill(const void *q, const void *k, const void *v, bool f32io, cons
         hipLaunchKernelGGL(chain_kernel<__bf16>, dim3(nwg), dim3(256), 0, stream, S0, N, H, tab, o, S_final);
     if (hipGetLastError() != hipSuccess) return -1;
     if (ev && hipEventRecord(ev[3], stream) != hipSuccess) return -1;
+    if (ev && hipEventRecord(ev[4], stream) != hipSuccess) return -1;
     return 0;
 }
 
 int set_prefill_attributes() {
+    if (set_segment_attributes() != 0) return -1;
     const int smem = (int)sizeof(IntraSmem<float>);
     if (hipFuncSetAttribute((const void *)intra_kernel<float>, hipFuncAttributeMaxDynamicSharedMemorySize, smem) !=
         hipSuccess)

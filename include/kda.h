@@ -72,13 +72,14 @@ int kda_version(void);
 
 /*
  * Bytes of device workspace kda_chunk_fwd needs for T_total packed tokens in
- * n_seqs sequences and H heads (0 for an empty problem).  The workspace holds
- * the per-chunk intermediates of the chunkwise form (WY vectors, decay-scaled
- * keys and queries, the intra-chunk query-key matrix, the chunk decay) and a
- * small sequence / chunk table.  Its contents are scratch between calls.
- * Returns 0 and writes nothing when the sizes are invalid.
+ * n_seqs sequences, H heads and the given q/k/v dtype (0 for an empty problem
+ * or invalid sizes).  With bf16 q/k/v the workspace holds a sequence /
+ * segment table and, per (segment, head), the segment's state transition, its
+ * state offset and its incoming state (3 x 64 KiB); about 55 MB for 64K tokens
+ * x 16 heads.  With fp32 q/k/v it holds the per-chunk operands of the chain
+ * (145 KiB per chunk and head).  Contents are scratch between calls.
  */
-size_t kda_chunk_fwd_workspace_bytes(int64_t T_total, int32_t n_seqs, int32_t H);
+size_t kda_chunk_fwd_workspace_bytes(int64_t T_total, int32_t n_seqs, int32_t H, kda_dtype qkv_dtype);
 
 /*
  * Chunkwise KDA prefill (Kimi Linear summary, sections 3.1 and 6.3; appendix C
@@ -109,7 +110,7 @@ size_t kda_chunk_fwd_workspace_bytes(int64_t T_total, int32_t n_seqs, int32_t H)
  *   o           [B*T, H, 128] fp32; must not overlap any input         (output)
  *   S_final     [n_seqs, H, 128, 128] fp32 or NULL; may alias S0       (output)
  *   workspace   device scratch of workspace_bytes >=
- *               kda_chunk_fwd_workspace_bytes(B*T, n_seqs, H)
+ *               kda_chunk_fwd_workspace_bytes(B*T, n_seqs, H, qkv_dtype)
  *   stream      hipStream_t
  */
 int kda_chunk_fwd(const void *q, const void *k, const void *v, kda_dtype qkv_dtype,
@@ -120,11 +121,13 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, kda_dtype qkv_dty
 
 /*
  * kda_chunk_fwd with stage timing: when stage_events is not NULL it points to
- * four hipEvent_t created by the caller; they are recorded on `stream` before
- * the sequence-table kernel, before the intra-chunk kernel, before the
- * inter-chunk (chain) kernel and after it, so the caller can read each stage's
- * duration with hipEventElapsedTime.  Everything else is as kda_chunk_fwd.
- * A failing hipEventRecord returns KDA_ERR_HIP.
+ * five hipEvent_t created by the caller; they are recorded on `stream` at the
+ * boundaries of the library's four stages, so the caller can read each
+ * stage's duration with hipEventElapsedTime.  bf16 q/k/v: [sequence table,
+ * segment transitions (pass A), segment scan, segment outputs (pass B)];
+ * fp32 q/k/v: [chunk table, intra-chunk kernel, chain kernel, (empty)].
+ * Everything else is as kda_chunk_fwd.  A failing hipEventRecord returns
+ * KDA_ERR_HIP.
  */
 int kda_chunk_fwd_timed(const void *q, const void *k, const void *v, kda_dtype qkv_dtype,
                         const float *g_raw, const float *beta, const float *A, const float *S0,

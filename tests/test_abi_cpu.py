@@ -45,14 +45,17 @@ def test_status_strings():
 
 def test_workspace_size():
     lib = kda.load()
-    assert lib.kda_chunk_fwd_workspace_bytes(0, 0, 16) == 0
-    assert lib.kda_chunk_fwd_workspace_bytes(-1, 1, 16) == 0
-    a = lib.kda_chunk_fwd_workspace_bytes(65536, 1, 16)
-    b = lib.kda_chunk_fwd_workspace_bytes(2 * 65536, 1, 16)
-    assert a > 0 and b > a
-    # grows with the chunk count ceil(T/64) + N and with H
-    assert lib.kda_chunk_fwd_workspace_bytes(64, 1, 2) > lib.kda_chunk_fwd_workspace_bytes(64, 1, 1)
-    assert lib.kda_chunk_fwd_workspace_bytes(65, 1, 1) > lib.kda_chunk_fwd_workspace_bytes(64, 1, 1)
+    for dt in (0, 1):
+        assert lib.kda_chunk_fwd_workspace_bytes(0, 0, 16, dt) == 0
+        assert lib.kda_chunk_fwd_workspace_bytes(-1, 1, 16, dt) == 0
+        a = lib.kda_chunk_fwd_workspace_bytes(65536, 1, 16, dt)
+        b = lib.kda_chunk_fwd_workspace_bytes(4 * 65536, 1, 16, dt)
+        assert a > 0 and b >= a
+        assert lib.kda_chunk_fwd_workspace_bytes(64, 1, 2, dt) > lib.kda_chunk_fwd_workspace_bytes(64, 1, 1, dt)
+    assert lib.kda_chunk_fwd_workspace_bytes(64, 1, 1, 9) == 0
+    # fp32 I/O keeps per-chunk operands (grows with ceil(T/64) + N); bf16 keeps per-segment states
+    assert lib.kda_chunk_fwd_workspace_bytes(65, 1, 1, 1) > lib.kda_chunk_fwd_workspace_bytes(64, 1, 1, 1)
+    assert lib.kda_chunk_fwd_workspace_bytes(65536, 1, 16, 0) < 100 * 2**20
 
 
 # Fake, 256-aligned, non-overlapping "device" addresses: validation must fail

@@ -128,9 +128,9 @@ def test_frozen_state():
     d["beta"][:] = 0.0
     say("case frozen state")
     o, Sf = run_prefill(d, S0=d["S0"])
-    assert np.array_equal(Sf, d["S0"])
+    assert np.array_equal(Sf, d["S0"])  # identity transitions reproduce the state bit for bit
     ref = np.einsum("thi,hij->thj", d["q"].astype(np.float64), d["S0"][0].astype(np.float64))
-    assert err(o, ref) < 1e-4
+    assert err(o, ref) <= TOL["bf16"]
 
 
 def test_deterministic():
