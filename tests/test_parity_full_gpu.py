@@ -1,0 +1,121 @@
+"""GPU parity at the full workload sizes, in the launch configuration the benchmark times.
+
+* prefill B=1, H=16, T=65,536 (z x2, S0 ~ N(0, 0.02^2)): every output and the final state
+  against the fp64 oracle recurrence;
+* batched decode, 256 sequences x 32 heads, 1,000 in-place steps: step 1 on all 8,192 heads;
+  after step 1,000 the outputs and states of a seeded set of 8 sequences x 32 heads, the oracle
+  having run all 1,000 steps for them;
+* 1M-token varlen pack (lengths 1,048,576 / 65,536 / 8,192 / 777, H=16, S0 = 0): the last 4,096
+  tokens of the long sequence from the state the GPU reaches before them (a second call over the
+  first 1,044,480 tokens), plus the other three sequences in full.
+
+Bar: max|d| / RMS(ref) <= 1e-2 for o and S_final (bf16 q/k/v).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_helpers import DEV, err, host_pool_size, say, to_dev, upload_prefill_streamed
+
+import gated_delta_rule_29_amd as kda
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-2
+
+
+@pytest.mark.timeout(300)
+def test_prefill_64k_full():
+    w = synth.WORKLOADS["prefill_64k"]
+    T, H = w["lens"][0], w["H"]
+    say(f"case prefill_64k T={T} H={H}: generating")
+    d = synth.prefill_inputs(w["seed"], T, H, dtype="bf16", z_scale=w["z_scale"], s0_std=w["s0_std"])
+    q, k, v = (to_dev(d[n], torch.bfloat16) for n in ("q", "k", "v"))
+    say("case prefill_64k: GPU call")
+    o, Sf = kda.kda_chunk_fwd(q, k, v, to_dev(d["z"], torch.float32), to_dev(d["beta"], torch.float32),
+                              to_dev(d["A"], torch.float32), to_dev(d["S0"], torch.float32))
+    torch.cuda.synchronize()
+    o, Sf = o.cpu().numpy(), Sf.cpu().numpy()
+    say("case prefill_64k: oracle")
+    o_ref, S_ref = oracle.recurrent(d["q"], d["k"], d["v"], d["z"], d["beta"], d["A"], d["S0"],
+                                    threads=host_pool_size())
+    eo, es = err(o, o_ref), err(Sf, S_ref)
+    # per-head errors: no head may drift, not only the worst element overall
+    eh = max(err(o[:, h], o_ref[:, h]) for h in range(H))
+    say(f"  prefill_64k err_o={eo:.3e} err_S={es:.3e} worst-head err_o={eh:.3e}")
+    assert eo <= TOL and es <= TOL and eh <= TOL
+
+
+@pytest.mark.timeout(600)
+def test_decode_256x32_1000_steps():
+    w = synth.WORKLOADS["decode_256x32"]
+    N, H, steps, seed = w["N"], w["H"], w["steps"], w["seed"]
+    S0 = synth.initial_state(seed, N, H, w["s0_std"])
+    A = synth.head_params(seed, H)
+    sel = np.sort(np.random.Generator(np.random.PCG64(seed + 77)).choice(N, 8, replace=False))
+    S = to_dev(S0, torch.float32)
+    Ad = to_dev(A, torch.float32)
+    S_sub = S0[sel].astype(np.float64)
+    bf = torch.bfloat16
+    from concurrent.futures import ThreadPoolExecutor
+
+    n = host_pool_size()
+    say(f"case decode N={N} H={H} steps={steps} checked sequences {sel.tolist()}")
+    with ThreadPoolExecutor(n) as ex:
+        for b in range(0, steps, 2 * n):
+            for step, x in ex.map(lambda s: (s, synth.decode_tokens(seed, s, N, H)),
+                                  range(b, min(steps, b + 2 * n))):
+                o = kda.kda_decode_step(to_dev(x["q"], bf), to_dev(x["k"], bf), to_dev(x["v"], bf),
+                                        to_dev(x["z"], torch.float32), to_dev(x["beta"], torch.float32), Ad, S)
+                if step == 0:  # step 1: every head
+                    torch.cuda.synchronize()
+                    o_ref, S_ref = oracle.decode_step(x["q"], x["k"], x["v"], x["z"], x["beta"], A, S0,
+                                                      threads=n)
+                    e1, e2 = err(o.cpu().numpy(), o_ref), err(S.cpu().numpy(), S_ref)
+                    say(f"  step 1 (all {N * H} heads): err_o={e1:.3e} err_S={e2:.3e}")
+                    assert e1 <= TOL and e2 <= TOL
+                    del S_ref
+                o_sub, S_sub = oracle.decode_step(x["q"][sel], x["k"][sel], x["v"][sel], x["z"][sel],
+                                                  x["beta"][sel], A, S_sub, threads=n)
+    torch.cuda.synchronize()
+    eo = err(o.cpu().numpy()[sel], o_sub)
+    es = err(S.cpu().numpy()[sel], S_sub)
+    say(f"  step {steps} ({len(sel)} sequences x {H} heads): err_o={eo:.3e} err_S={es:.3e}")
+    assert eo <= TOL and es <= TOL
+
+
+@pytest.mark.timeout(600)
+def test_varlen_1m():
+    w = synth.WORKLOADS["varlen_1m"]
+    lens, H, seed = w["lens"], w["H"], w["seed"]
+    cu = synth.cu_seqlens(lens)
+    T = int(cu[-1])
+    say(f"case varlen_1m lens={lens} H={H}: generating {T} tokens")
+    q, k, v, z, beta = upload_prefill_streamed(seed, T, H, w["z_scale"])
+    A = synth.head_params(seed, H)
+    Ad = to_dev(A, torch.float32)
+    cu_t = to_dev(np.asarray(cu, np.int32), torch.int32)
+    say("case varlen_1m: full call")
+    o, Sf = kda.kda_chunk_fwd(q, k, v, z, beta, Ad, None, cu_t)
+    # the state just before the last 4,096 tokens of sequence 0, from a second call
+    t_mid = lens[0] - 4096
+    say(f"case varlen_1m: second call over the first {t_mid} tokens")
+    _, S_mid = kda.kda_chunk_fwd(q[:t_mid], k[:t_mid], v[:t_mid], z[:t_mid], beta[:t_mid], Ad, None)
+    torch.cuda.synchronize()
+    Sf = Sf.cpu().numpy()
+    S_mid = S_mid.cpu().numpy()
+    n = host_pool_size()
+
+    def check(t0, t1, S_start, S_end, label):
+        d = synth.prefill_tokens(seed, t0, t1, H, "bf16", w["z_scale"])
+        o_ref, S_ref = oracle.recurrent(d["q"], d["k"], d["v"], d["z"], d["beta"], A, S_start, threads=n)
+        eo = err(o[t0:t1].cpu().numpy(), o_ref)
+        es = err(S_end, S_ref[0])
+        say(f"  {label} tokens [{t0}, {t1}): err_o={eo:.3e} err_S={es:.3e}")
+        assert eo <= TOL and es <= TOL
+
+    check(t_mid, lens[0], S_mid, Sf[0], "seq 0 tail")
+    for i in (1, 2, 3):
+        check(int(cu[i]), int(cu[i + 1]), None, Sf[i], f"seq {i}")
