@@ -108,7 +108,7 @@ def kda_chunk_fwd(q, k, v, g_raw, beta, A, S0=None, cu_seqlens=None, *, o=None, 
     beta: [B, T, H] fp32; A: [H] fp32; S0: [N, H, 128, 128] fp32 or None (zeros);
     cu_seqlens: int32 device tensor [N+1] packing N sequences along T (then B must be 1).
     Returns (o [.., H, 128] fp32, S_final [N, H, 128, 128] fp32 or None).
-    stage_events: optional ctypes array of five hipEvent_t recorded at the library's stage boundaries.
+    stage_events: optional ctypes array of six hipEvent_t recorded at the library's stage boundaries.
     """
     lib = load()
     squeeze = q.dim() == 3

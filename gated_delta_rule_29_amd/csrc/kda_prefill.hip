@@ -655,8 +655,8 @@ int launch_prefill(const void *q, const void *k, const void *v, bool f32io, cons
     else
         hipLaunchKernelGGL(chain_kernel<__bf16>, dim3(nwg), dim3(256), 0, stream, S0, N, H, tab, o, S_final);
     if (hipGetLastError() != hipSuccess) return -1;
-    if (ev && hipEventRecord(ev[3], stream) != hipSuccess) return -1;
-    if (ev && hipEventRecord(ev[4], stream) != hipSuccess) return -1;
+    for (int e = 3; e < 6; ++e)
+        if (ev && hipEventRecord(ev[e], stream) != hipSuccess) return -1;
     return 0;
 }
 

@@ -121,13 +121,13 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, kda_dtype qkv_dty
 
 /*
  * kda_chunk_fwd with stage timing: when stage_events is not NULL it points to
- * five hipEvent_t created by the caller; they are recorded on `stream` at the
- * boundaries of the library's four stages, so the caller can read each
+ * six hipEvent_t created by the caller; they are recorded on `stream` at the
+ * boundaries of the library's five stages, so the caller can read each
  * stage's duration with hipEventElapsedTime.  bf16 q/k/v: [sequence table,
- * segment transitions (pass A), segment scan, segment outputs (pass B)];
- * fp32 q/k/v: [chunk table, intra-chunk kernel, chain kernel, (empty)].
- * Everything else is as kda_chunk_fwd.  A failing hipEventRecord returns
- * KDA_ERR_HIP.
+ * intra-chunk WY / UT operands, segment transitions (pass A), segment scan,
+ * segment outputs (pass B)]; fp32 q/k/v: [chunk table, intra-chunk kernel,
+ * chain kernel, (empty), (empty)].  Everything else is as kda_chunk_fwd.
+ * A failing hipEventRecord returns KDA_ERR_HIP.
  */
 int kda_chunk_fwd_timed(const void *q, const void *k, const void *v, kda_dtype qkv_dtype,
                         const float *g_raw, const float *beta, const float *A, const float *S0,

@@ -53,9 +53,11 @@ def test_workspace_size():
         assert a > 0 and b >= a
         assert lib.kda_chunk_fwd_workspace_bytes(64, 1, 2, dt) > lib.kda_chunk_fwd_workspace_bytes(64, 1, 1, dt)
     assert lib.kda_chunk_fwd_workspace_bytes(64, 1, 1, 9) == 0
-    # fp32 I/O keeps per-chunk operands (grows with ceil(T/64) + N); bf16 keeps per-segment states
-    assert lib.kda_chunk_fwd_workspace_bytes(65, 1, 1, 1) > lib.kda_chunk_fwd_workspace_bytes(64, 1, 1, 1)
-    assert lib.kda_chunk_fwd_workspace_bytes(65536, 1, 16, 0) < 100 * 2**20
+    # both paths keep one block of chain operands per (chunk, head): the size grows with ceil(T/64) + N
+    for dt in (0, 1):
+        assert lib.kda_chunk_fwd_workspace_bytes(65, 1, 1, dt) > lib.kda_chunk_fwd_workspace_bytes(64, 1, 1, dt)
+        per_chunk_head = lib.kda_chunk_fwd_workspace_bytes(64 * 4096, 1, 16, dt) / (4097 * 16)
+        assert 64 * 1024 < per_chunk_head < 192 * 1024
 
 
 # Fake, 256-aligned, non-overlapping "device" addresses: validation must fail
