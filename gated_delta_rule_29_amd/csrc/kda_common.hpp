@@ -42,13 +42,23 @@ struct S8 {
     bf16x8 hi, lo;
 };
 
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+// hi = RNE bf16 of each value; lo = RNE bf16 of the remainder.  Pairs are
+// rounded with one packed conversion and widened back with shifts/masks.
 __device__ __forceinline__ S8 split8(const F8 &x) {
     S8 s;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        __bf16 h = (__bf16)x.v[e];
-        s.hi[e] = h;
-        s.lo[e] = (__bf16)(x.v[e] - (float)h);
+    for (int p = 0; p < 4; ++p) {
+        const float a = x.v[2 * p], b = x.v[2 * p + 1];
+        const bf16x2 hp = {(__bf16)a, (__bf16)b};
+        uint32_t u = __builtin_bit_cast(uint32_t, hp);
+        asm("" : "+v"(u));  // keep the packed pair: widen it instead of converting a again
+        const float fa = __builtin_bit_cast(float, u << 16), fb = __builtin_bit_cast(float, u & 0xffff0000u);
+        const bf16x2 lp = {(__bf16)(a - fa), (__bf16)(b - fb)};
+        s.hi[2 * p] = hp[0];
+        s.hi[2 * p + 1] = hp[1];
+        s.lo[2 * p] = lp[0];
+        s.lo[2 * p + 1] = lp[1];
     }
     return s;
 }

@@ -167,10 +167,11 @@ __device__ inline int seg_find(const int32_t *off, int N, int x) {
 
 struct WySmem {
     union {
-        float E1[CH * PE];  // e^{G_t - R_s(t)} [token][channel] (phases 1-2)
+        float E1[CH * PE];  // e^{G_t - R_s}, s = sub-chunk of t [token][channel] (phases 1-2)
         float T[CH * PTT];  // Akk, then T = (I + Akk)^{-1} (phases 2-4)
     } a;
-    float PF[6 * D];        // e^{R_i - R_j} for j < i, row i(i-1)/2 + j
+    float CB[CH * PE];      // k_t e^{R_{s+1} - G_t}, in [e^-80, 1] |k_t|  [token][channel] (phases 1-2)
+    float F[10 * D];        // e^{R_i - R_{j+1}} for j <= i, row i(i+1)/2 + j
     float eR[4 * D];        // e^{R_s}
     float beta[CH];
 };
@@ -185,7 +186,10 @@ struct WySmem {
 // of the W and U products.  The 16-token cumulative sums run in-lane over m
 // and across the lanes g = 0..3 by shuffles.  E1 is passed through LDS to the
 // Gram phase, which works on token rows (wave i = sub-chunk i).
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void wy_kernel(
+#ifndef WY_WPE
+#define WY_WPE 2
+#endif
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WY_WPE))) void wy_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     const float *__restrict__ z, const float *__restrict__ beta, const float *__restrict__ A, int N, int H,
     SegTable tab) {
@@ -195,7 +199,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void w
     const int n = seg_find(tab.chunk_off, N, c);
     const int64_t t0 = tab.seq_start[n] + (int64_t)(c - tab.chunk_off[n]) * CH;
     const int len = (int)min((int64_t)CH, tab.seq_end[n] - t0);
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, lr = l & 15;
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, g = l >> 4, lr = l & 15;
     const size_t HD = (size_t)H * D;
     const size_t base = (size_t)t0 * HD + (size_t)h * D;  // element (t, ch) at base + t * HD + ch
     char *blk = tab.blocks + ((size_t)c * H + h) * BLK;
@@ -255,8 +259,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void w
         Rs[c2][0] = 0.f;
 #pragma unroll
         for (int s = 0; s < 4; ++s) Rs[c2][s + 1] = Rs[c2][s] + st[s];
+        float eN[4];  // e^{G_n - R_{s+1}}
 #pragma unroll
-        for (int s = 0; s < 4; ++s) eRs[c2][s] = __expf(Rs[c2][s]);
+        for (int s = 0; s < 4; ++s) {
+            eRs[c2][s] = __expf(Rs[c2][s]);
+            eN[s] = __expf(Rs[c2][4] - Rs[c2][s + 1]);
+        }
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             f16x8 kt;
@@ -266,9 +274,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void w
                 const int t = 32 * ks + 16 * (e >> 2) + 4 * g + (e & 3);
                 const float cs = gv[ks][e];
                 const float e1 = __expf(cs);
-                sm.a.E1[t * PE + ch] = e1;
                 const float kf = (float)kb[ks][e];
-                kt[e] = (_Float16)(kf * __expf(Rs[c2][4] - Rs[c2][s] - cs));
+                const float cb = kf * __expf(st[s] - cs);  // k e^{R_{s+1} - G_t}
+                sm.a.E1[t * PE + ch] = e1;
+                sm.CB[t * PE + ch] = cb;
+                kt[e] = (_Float16)(cb * eN[s]);             // k e^{G_n - G_t}
                 kga[c2][ks][e] = (__bf16)(kf * (eRs[c2][s] * e1));
             }
             *(f16x8 *)(blk + BO_KT + frag((2 * w + c2) * 2 + ks, l)) = kt;
@@ -281,19 +291,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void w
 #pragma unroll
             for (int s = 0; s < 4; ++s) sm.eR[s * D + ch] = eRs[c2][s];
 #pragma unroll
-            for (int i = 1; i < 4; ++i)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int jj = 0; jj < i; ++jj)
-                    sm.PF[(i * (i - 1) / 2 + jj) * D + ch] = __expf(Rs[c2][i] - Rs[c2][jj]);
+                for (int jj = 0; jj <= i; ++jj)
+                    sm.F[(i * (i + 1) / 2 + jj) * D + ch] = __expf(Rs[c2][i] - Rs[c2][jj + 1]);
             ((float *)(blk + BO_GM))[ch] = __expf(Rs[c2][4]);
         }
     }
     __syncthreads();
 
     // ---- phase 2: Gram tiles of sub-chunk i = w against sub-chunks j <= i, and Q~.
-    // Row operands x_r e^{G_r - R_i} (x = k, q) are formed once; the column
-    // operand k_c e^{R_i - G_c} = k_c / E1_c, times e^{R_{j+1} - R_j} e^{R_i - R_{j+1}}
-    // for j < i (each factor in range; the first keeps the product >= e^-80).
+    // Row operands x_r e^{G_r - R_i} (x = k, q) are formed once per 32-channel
+    // block; the column operand k_c e^{R_i - G_c} is CB_c e^{R_i - R_{j+1}}: CB
+    // lies in [e^-80, 1] |k|, the factor is <= 1 for j < i (an underflow drops
+    // only terms below e^-87) and in [1, e^80] for j = i.
     // The channel order inside each 32-block is perm32, shared by both operands
     // and by Q~.  Tiles come out transposed: lane (lr, g) holds row r = 16i + lr
     // against columns 16j + 4g + m.
@@ -332,33 +343,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void w
             for (int j = 0; j < 4; ++j) {
                 if (j > i) break;
                 const int cc = 16 * j + lr;
-                const uint32_t co = (uint32_t)min(cc, len - 1) * ph + 2u * c0;
-                bf16x4 c0v = *(const bf16x4 *)(kc + co), c1v = *(const bf16x4 *)(kc + co + 32);
-                if (cc >= len) c0v = c1v = z4;
-                const f32x4 fa0 = *(const f32x4 *)&sm.a.E1[cc * PE + c0], fb0 = *(const f32x4 *)&sm.a.E1[cc * PE + c0 + 16];
+                // k_c e^{R_i - G_c} = CB_c e^{R_i - R_{j+1}} (rows past the end hold k = 0)
+                const float *cb = &sm.CB[cc * PE + c0];
+                const float *fij = &sm.F[(i * (i + 1) / 2 + j) * D + c0];
+                const f32x4 ca = *(const f32x4 *)cb, cbv = *(const f32x4 *)(cb + 16);
+                const f32x4 fa = *(const f32x4 *)fij, fb = *(const f32x4 *)(fij + 16);
                 F8 xc;
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    xc.v[m] = (float)c0v[m] * __builtin_amdgcn_rcpf(fa0[m]);
-                    xc.v[4 + m] = (float)c1v[m] * __builtin_amdgcn_rcpf(fb0[m]);
-                }
-                if (j < i) {
-                    const float *f1 = &sm.PF[((j + 1) * j / 2 + j) * D];  // e^{R_{j+1} - R_j}
-                    const f32x4 fa = *(const f32x4 *)&f1[c0], fb = *(const f32x4 *)&f1[c0 + 16];
-#pragma unroll
-                    for (int m = 0; m < 4; ++m) {
-                        xc.v[m] *= fa[m];
-                        xc.v[4 + m] *= fb[m];
-                    }
-                    if (j + 1 < i) {
-                        const float *f2 = &sm.PF[(i * (i - 1) / 2 + j + 1) * D];  // e^{R_i - R_{j+1}}
-                        const f32x4 ga = *(const f32x4 *)&f2[c0], gb = *(const f32x4 *)&f2[c0 + 16];
-#pragma unroll
-                        for (int m = 0; m < 4; ++m) {
-                            xc.v[m] *= ga[m];
-                            xc.v[4 + m] *= gb[m];
-                        }
-                    }
+                    xc.v[m] = ca[m] * fa[m];
+                    xc.v[4 + m] = cbv[m] * fb[m];
                 }
                 const S8 cs = split8(xc);
                 a1[j] = mma_ss(a1[j], cs, rk);
