@@ -71,6 +71,14 @@ constexpr size_t BLK = 94720;  // multiple of 256
 __device__ __forceinline__ int aq_tile(int rt, int s) { return rt < 2 ? rt : 2 * rt - 2 + s; }
 __device__ __forceinline__ int frag(int tile, int lane) { return (tile * 64 + lane) * 16; }
 
+// Buffer resource word 3 for raw (untyped) buffer access on gfx9-family chips:
+// 32-bit data format, so accesses past num_records read 0 and drop writes.
+constexpr int BUF_RSRC3 = 0x00020000;
+__device__ __forceinline__ bf16x4 ld_bf16x4(__amdgpu_buffer_rsrc_t r, int off) {
+    typedef __attribute__((ext_vector_type(2))) int i32x2;
+    return __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+
 constexpr int PE = 132;   // pitch (floats) of E1 [64][128]
 constexpr int PTT = 72;   // pitch (floats) of T [64][64]
 
@@ -207,11 +215,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WY_WPE))) v
     if (w == 0) sm.beta[l] = l < len ? beta[(size_t)(t0 + l) * H + h] : 0.f;
 
     // ---- phase 1: gate, cumulative sums, E1 (to LDS), K~^T (to the block), (K * Gam)^T and V.
-    // Loads use 32-bit byte offsets from the chunk's row-0 pointers; rows past
-    // the end read the last row (always in bounds) and are dropped.
-    const char *zc = (const char *)(z + base), *kc = (const char *)(k + base), *vc = (const char *)(v + base);
-    const char *qc = (const char *)(q + base);
+    // Buffer loads: the resource of each input covers this chunk's rows of the
+    // tensor (num_records = len rows), so a row past the end reads as 0 and the
+    // row part of every offset is a scalar.
     const uint32_t pz = (uint32_t)(HD * 4), ph = (uint32_t)(HD * 2);  // row pitches in bytes
+    const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc((void *)(z + base), 0, len * pz, BUF_RSRC3);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)(k + base), 0, len * ph, BUF_RSRC3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)(v + base), 0, len * ph, BUF_RSRC3);
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void *)(q + base), 0, len * ph, BUF_RSRC3);
     bf16x8 kga[2][2], vb[2][2];
     float Rs[2][5], eRs[2][4];
 #pragma unroll
@@ -224,15 +235,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WY_WPE))) v
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int t = 32 * ks + 16 * (e >> 2) + 4 * g + (e & 3);
-                const uint32_t tr = (uint32_t)min(t, len - 1);
-                const bool ok = t < len;
-                const float zv = *(const float *)(zc + tr * pz + 4u * ch);
-                const __bf16 kv = *(const __bf16 *)(kc + tr * ph + 2u * ch);
-                const __bf16 vv = *(const __bf16 *)(vc + tr * ph + 2u * ch);
+                const int tl = 4 * g + (e & 3), tu = 32 * ks + 16 * (e >> 2);  // row = tu (scalar) + tl
+                const bool ok = tu + tl < len;
+                const float zv = __builtin_bit_cast(
+                    float, __builtin_amdgcn_raw_buffer_load_b32(rz, tl * pz + 4 * ch, tu * pz, 0));
+                const uint16_t kv = __builtin_amdgcn_raw_buffer_load_b16(rk, tl * ph + 2 * ch, tu * ph, 0);
+                const uint16_t vv = __builtin_amdgcn_raw_buffer_load_b16(rv, tl * ph + 2 * ch, tu * ph, 0);
                 gv[ks][e] = kda_gate(eA, ok ? zv : -__builtin_inff());  // z = -inf gives g = 0
-                kb[ks][e] = ok ? kv : (__bf16)0.f;
-                vb[c2][ks][e] = ok ? vv : (__bf16)0.f;
+                kb[ks][e] = __builtin_bit_cast(__bf16, kv);
+                vb[c2][ks][e] = __builtin_bit_cast(__bf16, vv);
             }
         float st[4];
 #pragma unroll
@@ -311,8 +322,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WY_WPE))) v
     f32x4 akk[4];
     {
         const int i = w, r = 16 * i + lr;
-        const bool rok = r < len;
-        const bf16x4 z4 = {(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
         f32x4 a1[4], a2[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) a1[j] = a2[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -320,10 +329,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WY_WPE))) v
         for (int ks = 0; ks < 4; ++ks) {
             __builtin_amdgcn_sched_barrier(0);  // one 32-channel block at a time
             const int c0 = 32 * ks + 4 * g;
-            const uint32_t ro = (uint32_t)min(r, len - 1) * ph + 2u * c0;
-            bf16x4 k0 = *(const bf16x4 *)(kc + ro), k1 = *(const bf16x4 *)(kc + ro + 32);
-            bf16x4 q0 = *(const bf16x4 *)(qc + ro), q1 = *(const bf16x4 *)(qc + ro + 32);
-            if (!rok) k0 = k1 = q0 = q1 = z4;
+            const int ro = r * ph + 2 * c0;  // rows past the end read as 0
+            const bf16x4 k0 = ld_bf16x4(rk, ro), k1 = ld_bf16x4(rk, ro + 32);
+            const bf16x4 q0 = ld_bf16x4(rq, ro), q1 = ld_bf16x4(rq, ro + 32);
             const f32x4 ea = *(const f32x4 *)&sm.a.E1[r * PE + c0], eb = *(const f32x4 *)&sm.a.E1[r * PE + c0 + 16];
             const f32x4 pa = *(const f32x4 *)&sm.eR[i * D + c0], pb = *(const f32x4 *)&sm.eR[i * D + c0 + 16];
             F8 xk, xq;
@@ -501,54 +509,31 @@ struct ChainLds {
     static constexpr int AQ = 49152;                 // pass B only
     static constexpr int GM = PASS_A ? 32768 : 61440;
     static constexpr int BYTES = GM + 512;
-    static constexpr int PIECES = BYTES / 16;        // 16 B pieces copied per chunk
 };
 
 constexpr int CH_NW = 8;  // waves per chain workgroup
 constexpr int CH_NT = 64 * CH_NW;
 
-template <bool PASS_A>
-struct ChainPf {
-    static constexpr int PPT = (ChainLds<PASS_A>::PIECES + CH_NT - 1) / CH_NT;
-    static constexpr int NCT = PASS_A ? 2 : 1;
-    u32x4 pc[PPT];
-    f32x4 u[4][NCT];
-};
+typedef __attribute__((address_space(3))) void lds_void;
 
-// source offset in the block of LDS-image byte x
+// Copy one chunk's LDS image straight from its block into LDS
+// (global_load_lds_dwordx4: lane l of a wave lands at dst + 16 l, so each
+// instruction moves 1 KB).  Completion is awaited with vmcnt by the caller.
 template <bool PASS_A>
-__device__ __forceinline__ int chain_src(int x) {
+__device__ __forceinline__ void chain_dma(const char *__restrict__ blk, char *lds, int wv, int l) {
     using Lo = ChainLds<PASS_A>;
-    if (x >= Lo::GM) return BO_GM + (x - Lo::GM);
-    if (PASS_A && x >= Lo::KT) return BO_KT + (x - Lo::KT);
-    return x;  // pass B: W | Q~ | K~^T | Aqk is the block's first 61440 bytes
-}
-
-template <bool PASS_A>
-__device__ __forceinline__ ChainPf<PASS_A> chain_load(const char *__restrict__ blk, int tid, int l, bool has_u,
-                                                      int utile) {
-    using P = ChainPf<PASS_A>;
-    P p;
+    constexpr int NKB = Lo::GM / 1024;
 #pragma unroll
-    for (int i = 0; i < P::PPT; ++i) {
-        const int x = 16 * (tid + CH_NT * i);
-        p.pc[i] = x < ChainLds<PASS_A>::BYTES ? *(const u32x4 *)(blk + chain_src<PASS_A>(x)) : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < (NKB + CH_NW - 1) / CH_NW; ++i) {
+        const int kb = wv + CH_NW * i;
+        if (kb < NKB) {
+            const int x = 1024 * kb;
+            const int src = (PASS_A && x >= Lo::KT) ? BO_KT + (x - Lo::KT) : x;
+            __builtin_amdgcn_global_load_lds((const void *)(blk + src + 16 * l), (lds_void *)(lds + x), 16, 0, 0);
+        }
     }
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-        for (int ct = 0; ct < P::NCT; ++ct)
-            p.u[rt][ct] = has_u ? *(const f32x4 *)(blk + BO_U + frag(8 * rt + utile + ct, l)) : f32x4{0.f, 0.f, 0.f, 0.f};
-    return p;
-}
-
-template <bool PASS_A>
-__device__ __forceinline__ void chain_stage(char *lds, const ChainPf<PASS_A> &p, int tid) {
-#pragma unroll
-    for (int i = 0; i < ChainPf<PASS_A>::PPT; ++i) {
-        const int x = 16 * (tid + CH_NT * i);
-        if (x < ChainLds<PASS_A>::BYTES) *(u32x4 *)(lds + x) = p.pc[i];
-    }
+    if (wv == NKB % CH_NW && l < 32)  // gamma: 512 B
+        __builtin_amdgcn_global_load_lds((const void *)(blk + BO_GM + 16 * l), (lds_void *)(lds + Lo::GM), 16, 0, 0);
 }
 
 // One workgroup (8 waves) per (segment, head).  Pass A: wave w owns columns
@@ -557,9 +542,12 @@ __device__ __forceinline__ void chain_stage(char *lds, const ChainPf<PASS_A> &p,
 template <bool PASS_A>
 __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void seg_chain_kernel(
     int N, int H, SegTable tab, float *__restrict__ o, float *__restrict__ S_final) {
-    extern __shared__ __align__(16) char smem_raw[];
     using Lo = ChainLds<PASS_A>;
-    constexpr int NCT = ChainPf<PASS_A>::NCT;
+    // Two distinct arrays (not one array indexed by parity): a read of one
+    // then provably does not alias a copy in flight into the other.
+    __shared__ __align__(16) char buf0[Lo::BYTES];
+    __shared__ __align__(16) char buf1[Lo::BYTES];
+    constexpr int NCT = PASS_A ? 2 : 1;
 
     const int x = blockIdx.x, h = blockIdx.y;
     const int nseg = tab.seg_off[N];
@@ -574,7 +562,8 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     const size_t bstride = (size_t)H * BLK;
     const char *blk0 = tab.blocks + ((size_t)tab.chunk_off[n] * H + h) * BLK;
 
-    const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63, g = l >> 4, lr = l & 15;
+    const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, g = l >> 4,
+              lr = l & 15;
     const size_t HD = (size_t)H * D;
     const size_t sblk = ((size_t)x * H + h) * D * D;
     const int colw = 16 * NCT * wv;  // pass A: columns 0..127 are M, 128..255 are B
@@ -595,104 +584,141 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
                     X[rt][ct][m] = tab.Sin[sblk + (size_t)r * D + col];
             }
 
-    ChainPf<PASS_A> pf;
+    auto load_u = [&](int chunk, f32x4 (&u)[4][NCT]) {
+        const char *blk = blk0 + chunk * bstride;
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+                u[rt][ct] = has_u ? *(const f32x4 *)(blk + BO_U + frag(8 * rt + utile + ct, l)) : f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+    // Output rows of chunk n leave at the start of chain step n + 1 and drain
+    // during that whole step.
+    auto store_o = [&](const f32x4 (&O)[4], int64_t t0, int len) {
+        float *orow = o + ((size_t)t0 * HD + (size_t)h * D + colw + lr);
+        if (len == CH) {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) orow[(size_t)(16 * rt + 4 * g + m) * HD] = O[rt][m];
+        } else {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int t = 16 * rt + 4 * g + m;
+                    if (t < len) orow[(size_t)t * HD] = O[rt][m];
+                }
+        }
+    };
+
+    f32x4 un[4][NCT];  // U of the next chunk, in flight
+    f32x4 O[4];
+    int64_t t0_prev = 0;
+    int len_prev = 0;
     if (cbeg < cend) {
-        pf = chain_load<PASS_A>(blk0 + cbeg * bstride, tid, l, has_u, utile);
-        chain_stage<PASS_A>(smem_raw, pf, tid);
+        chain_dma<PASS_A>(blk0 + cbeg * bstride, buf0, wv, l);
+        load_u(cbeg, un);
     }
-    for (int chunk = cbeg; chunk < cend; ++chunk) {
-        const char *lb = smem_raw + ((chunk - cbeg) & 1) * Lo::BYTES;
+
+    // One chain step on the image in `cur`, prefetching the next chunk into `nxt`.
+    auto step = [&](int chunk, const char *cur, char *nxt) __attribute__((always_inline)) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's copies and U have landed
+        __syncthreads();                                   // every wave's have; `nxt` is free
         f32x4 Dl[4][NCT];  // Delta starts as U (C layout, rows = tokens)
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) Dl[rt][ct] = pf.u[rt][ct];
-        __syncthreads();  // this chunk's LDS image is complete; the other buffer is free
-        if (chunk + 1 < cend) pf = chain_load<PASS_A>(blk0 + (chunk + 1) * bstride, tid, l, has_u, utile);
+            for (int ct = 0; ct < NCT; ++ct) Dl[rt][ct] = un[rt][ct];
+        if constexpr (!PASS_A)
+            if (chunk > cbeg) store_o(O, t0_prev, len_prev);
+        if (chunk + 1 < cend) {
+            chain_dma<PASS_A>(blk0 + (chunk + 1) * bstride, nxt, wv, l);
+            load_u(chunk + 1, un);
+        }
 
         const int64_t t0 = s0 + (int64_t)chunk * CH;
         const int len = (int)min((int64_t)CH, s1 - t0);
-        const float *gam = (const float *)(lb + Lo::GM);
+        const float *gam = (const float *)(cur + Lo::GM);
+        // The state as B operand: k-step s pairs the C tiles 2s and 2s+1.
+        f16x8 sf[NCT][4];
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            __builtin_amdgcn_sched_barrier(0);  // one column tile at a time
-            f16x8 sf[4];  // state as B operand: k-step s pairs C tiles 2s, 2s+1
+        for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
             for (int s = 0; s < 4; ++s)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) sf[s][e] = (_Float16)X[2 * s + (e >> 2)][ct][e & 3];
-            f32x4 O[4];
+                for (int e = 0; e < 8; ++e) sf[ct][s][e] = (_Float16)X[2 * s + (e >> 2)][ct][e & 3];
+        // Delta = U - W S and O = Q~ S: k-step outermost, so the accumulators of
+        // a step are independent and each A tile is read once.
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) O[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
-                __builtin_amdgcn_sched_barrier(0);  // bound the fragments kept in flight
-                O[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                const f16x8 wf = *(const f16x8 *)(cur + Lo::W + frag(4 * rt + s, l));
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const f16x8 wf = *(const f16x8 *)(lb + Lo::W + frag(4 * rt + s, l));
-                    Dl[rt][ct] = mfma_f16(wf, sf[s], Dl[rt][ct]);
-                    if constexpr (!PASS_A) {
-                        const f16x8 qf = *(const f16x8 *)(lb + Lo::QT + frag(4 * rt + s, l));
-                        O[rt] = mfma_f16(qf, sf[s], O[rt]);
-                    }
+                for (int ct = 0; ct < NCT; ++ct) Dl[rt][ct] = mfma_f16(wf, sf[ct][s], Dl[rt][ct]);
+                if constexpr (!PASS_A) {
+                    const f16x8 qf = *(const f16x8 *)(cur + Lo::QT + frag(4 * rt + s, l));
+                    O[rt] = mfma_f16(qf, sf[0][s], O[rt]);
                 }
             }
-            f16x8 dh[2], dlo[2];  // Delta as B operand (tokens), fp16 hi + lo
+        f16x8 dh[NCT][2], dlo[NCT][2];  // Delta as B operand (tokens), fp16 hi + lo
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
             for (int s = 0; s < 2; ++s)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float d = Dl[2 * s + (e >> 2)][ct][e & 3];
                     const _Float16 hh = (_Float16)d;
-                    dh[s][e] = hh;
-                    dlo[s][e] = (_Float16)(d - (float)hh);
+                    dh[ct][s][e] = hh;
+                    dlo[ct][s][e] = (_Float16)(d - (float)hh);
                 }
-            if constexpr (!PASS_A) {
-                const int col = colw + 16 * ct + lr;
-                float *orow = o + ((size_t)t0 * HD + (size_t)h * D + col);
+        if constexpr (!PASS_A) {  // O += (Aqk * Tril) Delta
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt) {
-                    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                    for (int s = 0; s < 2; ++s) {
-                        if (s > (rt >> 1)) break;
-                        const char *aq = lb + Lo::AQ + aq_tile(rt, s) * 2048;
-                        const f16x8 ah = *(const f16x8 *)(aq + l * 16);
-                        const f16x8 al = *(const f16x8 *)(aq + 1024 + l * 16);
-                        O[rt] = mfma_f16(al, dh[s], O[rt]);
-                        O[rt] = mfma_f16(ah, dlo[s], O[rt]);
-                        O[rt] = mfma_f16(ah, dh[s], O[rt]);
-                    }
-                    if (len == CH) {
-#pragma unroll
-                        for (int m = 0; m < 4; ++m) orow[(size_t)(16 * rt + 4 * g + m) * HD] = O[rt][m];
-                    } else {
-#pragma unroll
-                        for (int m = 0; m < 4; ++m) {
-                            const int t = 16 * rt + 4 * g + m;
-                            if (t < len) orow[(size_t)t * HD] = O[rt][m];
-                        }
-                    }
+                    if (s > (rt >> 1)) continue;
+                    const char *aq = cur + Lo::AQ + aq_tile(rt, s) * 2048;
+                    const f16x8 ah = *(const f16x8 *)(aq + l * 16);
+                    const f16x8 al = *(const f16x8 *)(aq + 1024 + l * 16);
+                    O[rt] = mfma_f16(al, dh[0][s], O[rt]);
+                    O[rt] = mfma_f16(ah, dlo[0][s], O[rt]);
+                    O[rt] = mfma_f16(ah, dh[0][s], O[rt]);
                 }
-            }
-            // S <- Diag(gamma) S + K~^T Delta
+            t0_prev = t0;
+            len_prev = len;
+        }
+        // S <- Diag(gamma) S + K~^T Delta, eight independent accumulators per k-step
+#pragma unroll
+        for (int rt = 0; rt < 8; ++rt) {
+            const f32x4 gm = *(const f32x4 *)&gam[16 * rt + 4 * g];
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) X[rt][ct][m] *= gm[m];
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
 #pragma unroll
             for (int rt = 0; rt < 8; ++rt) {
-                __builtin_amdgcn_sched_barrier(0);
-                const f32x4 gm = *(const f32x4 *)&gam[16 * rt + 4 * g];
-                f32x4 acc;
+                const f16x8 kf = *(const f16x8 *)(cur + Lo::KT + frag(2 * rt + s, l));
 #pragma unroll
-                for (int m = 0; m < 4; ++m) acc[m] = gm[m] * X[rt][ct][m];
-#pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    const f16x8 kf = *(const f16x8 *)(lb + Lo::KT + frag(2 * rt + s, l));
-                    acc = mfma_f16(kf, dlo[s], acc);
-                    acc = mfma_f16(kf, dh[s], acc);
+                for (int ct = 0; ct < NCT; ++ct) {
+                    X[rt][ct] = mfma_f16(kf, dlo[ct][s], X[rt][ct]);
+                    X[rt][ct] = mfma_f16(kf, dh[ct][s], X[rt][ct]);
                 }
-                X[rt][ct] = acc;
             }
-        }
-        if (chunk + 1 < cend) chain_stage<PASS_A>(smem_raw + ((chunk + 1 - cbeg) & 1) * Lo::BYTES, pf, tid);
+    };
+    for (int chunk = cbeg; chunk < cend; chunk += 2) {
+        step(chunk, buf0, buf1);
+        if (chunk + 1 < cend) step(chunk + 1, buf1, buf0);
     }
+    if constexpr (!PASS_A)
+        if (cbeg < cend) store_o(O, t0_prev, len_prev);
 
     // ---- segment end
     if constexpr (PASS_A) {
@@ -830,26 +856,18 @@ int launch_segment_prefill(const __bf16 *q, const __bf16 *k, const __bf16 *v, co
         hipLaunchKernelGGL(wy_kernel, dim3((unsigned)(ncm * H)), dim3(256), 0, stream, q, k, v, z, beta, A, N, H,
                            tab);
     if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return -1;
-    hipLaunchKernelGGL(seg_chain_kernel<true>, dim3((unsigned)nsm, (unsigned)H), dim3(CH_NT),
-                       2 * ChainLds<true>::BYTES, stream, N, H, tab, o, S_final);
+    hipLaunchKernelGGL(seg_chain_kernel<true>, dim3((unsigned)nsm, (unsigned)H), dim3(CH_NT), 0, stream, N, H, tab,
+                       o, S_final);
     if (ev && hipEventRecord(ev[3], stream) != hipSuccess) return -1;
     hipLaunchKernelGGL(seg_scan_kernel, dim3((unsigned)(N * H), 8), dim3(256), 0, stream, S0, N, H, tab, S_final);
     if (ev && hipEventRecord(ev[4], stream) != hipSuccess) return -1;
-    hipLaunchKernelGGL(seg_chain_kernel<false>, dim3((unsigned)nsm, (unsigned)H), dim3(CH_NT),
-                       2 * ChainLds<false>::BYTES, stream, N, H, tab, o, S_final);
+    hipLaunchKernelGGL(seg_chain_kernel<false>, dim3((unsigned)nsm, (unsigned)H), dim3(CH_NT), 0, stream, N, H, tab,
+                       o, S_final);
     if (hipGetLastError() != hipSuccess) return -1;
     if (ev && hipEventRecord(ev[5], stream) != hipSuccess) return -1;
     return 0;
 }
 
-int set_segment_attributes() {
-    if (hipFuncSetAttribute((const void *)seg_chain_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            2 * ChainLds<true>::BYTES) != hipSuccess)
-        return -1;
-    if (hipFuncSetAttribute((const void *)seg_chain_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            2 * ChainLds<false>::BYTES) != hipSuccess)
-        return -1;
-    return 0;
-}
+int set_segment_attributes() { return 0; }  // every kernel here uses static LDS only
 
 }  // namespace kda
