@@ -79,8 +79,14 @@ __device__ __forceinline__ bf16x4 ld_bf16x4(__amdgpu_buffer_rsrc_t r, int off) {
     return __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }
 
-constexpr int PE = 132;   // pitch (floats) of E1 [64][128]
-constexpr int PTT = 72;   // pitch (floats) of T [64][64]
+#ifndef WY_PE
+#define WY_PE 136
+#endif
+#ifndef WY_PTT
+#define WY_PTT 68
+#endif
+constexpr int PE = WY_PE;   // pitch (floats) of E1 [64][128]
+constexpr int PTT = WY_PTT;  // pitch (floats) of T [64][64]
 
 struct SegTable {
     int32_t *seg_off;    // [N+1] first segment of each sequence
