@@ -79,14 +79,7 @@ __device__ __forceinline__ bf16x4 ld_bf16x4(__amdgpu_buffer_rsrc_t r, int off) {
     return __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }
 
-#ifndef WY_PE
-#define WY_PE 136
-#endif
-#ifndef WY_PTT
-#define WY_PTT 68
-#endif
-constexpr int PE = WY_PE;   // pitch (floats) of E1 [64][128]
-constexpr int PTT = WY_PTT;  // pitch (floats) of T [64][64]
+constexpr int PTT = 68;  // pitch (floats) of T [64][64]
 
 struct SegTable {
     int32_t *seg_off;    // [N+1] first segment of each sequence
@@ -179,16 +172,19 @@ __device__ inline int seg_find(const int32_t *off, int N, int x) {
 
 // -------------------------------------------------------------- WY / UT --
 
+constexpr int PEH = 68;  // pitch (floats) of the half-width arrays [64 tokens][64 channels]
+
 struct WySmem {
     union {
-        float E1[CH * PE];  // e^{G_t - R_s}, s = sub-chunk of t [token][channel] (phases 1-2)
-        float T[CH * PTT];  // Akk, then T = (I + Akk)^{-1} (phases 2-4)
+        float E1[CH * PEH];  // e^{G_t - R_s}, s = sub-chunk of t, one 64-channel half (phases 1-2)
+        float T[CH * PTT];   // Akk, then T = (I + Akk)^{-1} (phases 2-4)
     } a;
-    float CB[CH * PE];      // k_t e^{R_{s+1} - G_t}, in [e^-80, 1] |k_t|  [token][channel] (phases 1-2)
-    float F[10 * D];        // e^{R_i - R_{j+1}} for j <= i, row i(i+1)/2 + j
-    float eR[4 * D];        // e^{R_s}
+    float CB[CH * PEH];      // k_t e^{R_{s+1} - G_t}, in [e^-80, 1] |k_t|, same half (phases 1-2)
+    float F[10 * D];         // e^{R_i - R_{j+1}} for j <= i, row i(i+1)/2 + j
+    float eR[4 * D];         // e^{R_s}
     float beta[CH];
 };
+static_assert(PTT <= PEH, "T lives in the E1 region");
 
 // One workgroup (4 waves) per (chunk, head); blockIdx.x = chunk * H + head.
 //
@@ -201,7 +197,7 @@ struct WySmem {
 // and across the lanes g = 0..3 by shuffles.  E1 is passed through LDS to the
 // Gram phase, which works on token rows (wave i = sub-chunk i).
 #ifndef WY_WPE
-#define WY_WPE 2
+#define WY_WPE 3
 #endif
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WY_WPE))) void wy_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
@@ -220,159 +216,164 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WY_WPE))) v
     const float eA = __expf(A[h]);
     if (w == 0) sm.beta[l] = l < len ? beta[(size_t)(t0 + l) * H + h] : 0.f;
 
-    // ---- phase 1: gate, cumulative sums, E1 (to LDS), K~^T (to the block), (K * Gam)^T and V.
-    // Buffer loads: the resource of each input covers this chunk's rows of the
-    // tensor (num_records = len rows), so a row past the end reads as 0 and the
-    // row part of every offset is a scalar.
+    // Phases 1 and 2 run twice, once per 64-channel half hf, so E1 and CB only
+    // ever hold half the channels (that keeps three workgroups on a CU).
+    //
+    // ---- phase 1: gate, cumulative sums, E1 and CB (to LDS), K~^T (to the
+    // block), (K * Gam)^T (kept as an MFMA operand).  Wave w takes key
+    // channels 64 hf + 16 w + lr.  Buffer loads: the resource of each input
+    // covers this chunk's rows, so a row past the end reads as 0 and the row
+    // part of every offset is a scalar.
     const uint32_t pz = (uint32_t)(HD * 4), ph = (uint32_t)(HD * 2);  // row pitches in bytes
     const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc((void *)(z + base), 0, len * pz, BUF_RSRC3);
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)(k + base), 0, len * ph, BUF_RSRC3);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)(v + base), 0, len * ph, BUF_RSRC3);
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void *)(q + base), 0, len * ph, BUF_RSRC3);
-    bf16x8 kga[2][2], vb[2][2];
-    float Rs[2][5], eRs[2][4];
+    bf16x8 kga[2][2];  // [hf][ks]: channel tile 4 hf + w
+    // Gram accumulators of sub-chunk i = w against sub-chunks j <= i; tiles come
+    // out transposed: lane (lr, g) holds row r = 16i + lr against columns
+    // 16j + 4g + m.
+    f32x4 a1[4], a2[4];
 #pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2) {
-        __builtin_amdgcn_sched_barrier(0);  // one channel at a time
-        const int ch = 32 * w + 16 * c2 + lr;
-        float gv[2][8];
-        bf16x8 kb[2];
+    for (int j = 0; j < 4; ++j) a1[j] = a2[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+    for (int hf = 0; hf < 2; ++hf) {
+        if (hf) __syncthreads();  // the Gram half before is done with E1 and CB
+        __builtin_amdgcn_sched_barrier(0);
+        const int ch = 64 * hf + 16 * w + lr, chl = 16 * w + lr;
+        float Rs[5], eRs[4];
+        {
+            float gv[2][8];
+            bf16x8 kb[2];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int tl = 4 * g + (e & 3), tu = 32 * ks + 16 * (e >> 2);  // row = tu (scalar) + tl
-                const bool ok = tu + tl < len;
-                const float zv = __builtin_bit_cast(
-                    float, __builtin_amdgcn_raw_buffer_load_b32(rz, tl * pz + 4 * ch, tu * pz, 0));
-                const uint16_t kv = __builtin_amdgcn_raw_buffer_load_b16(rk, tl * ph + 2 * ch, tu * ph, 0);
-                const uint16_t vv = __builtin_amdgcn_raw_buffer_load_b16(rv, tl * ph + 2 * ch, tu * ph, 0);
-                gv[ks][e] = kda_gate(eA, ok ? zv : -__builtin_inff());  // z = -inf gives g = 0
-                kb[ks][e] = __builtin_bit_cast(__bf16, kv);
-                vb[c2][ks][e] = __builtin_bit_cast(__bf16, vv);
-            }
-        float st[4];
+            for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                float a = 0.f;
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    a += gv[ks][4 * hh + m];
-                    gv[ks][4 * hh + m] = a;
+                for (int e = 0; e < 8; ++e) {
+                    const int tl = 4 * g + (e & 3), tu = 32 * ks + 16 * (e >> 2);  // row = tu (scalar) + tl
+                    const bool ok = tu + tl < len;
+                    const float zv = __builtin_bit_cast(
+                        float, __builtin_amdgcn_raw_buffer_load_b32(rz, tl * pz + 4 * ch, tu * pz, 0));
+                    const uint16_t kv = __builtin_amdgcn_raw_buffer_load_b16(rk, tl * ph + 2 * ch, tu * ph, 0);
+                    gv[ks][e] = kda_gate(eA, ok ? zv : -__builtin_inff());  // z = -inf gives g = 0
+                    kb[ks][e] = __builtin_bit_cast(__bf16, kv);
                 }
-                // inclusive sum over the lanes g' <= g holding the same channel
-                float x = a;
-                float y = __shfl_up(x, 16);
-                if (g >= 1) x += y;
-                y = __shfl_up(x, 32);
-                if (g >= 2) x += y;
-                const float ex = x - a;
+            float st[4];
 #pragma unroll
-                for (int m = 0; m < 4; ++m) gv[ks][4 * hh + m] += ex;  // G_t - R_s
-                st[2 * ks + hh] = __shfl(x, 48 + lr);                   // sub-chunk total
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    float a = 0.f;
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        a += gv[ks][4 * hh + m];
+                        gv[ks][4 * hh + m] = a;
+                    }
+                    // inclusive sum over the lanes g' <= g holding the same channel
+                    float x = a;
+                    float y = __shfl_up(x, 16);
+                    if (g >= 1) x += y;
+                    y = __shfl_up(x, 32);
+                    if (g >= 2) x += y;
+                    const float ex = x - a;
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) gv[ks][4 * hh + m] += ex;  // G_t - R_s
+                    st[2 * ks + hh] = __shfl(x, 48 + lr);                   // sub-chunk total
+                }
+            Rs[0] = 0.f;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) Rs[s + 1] = Rs[s] + st[s];
+            float eN[4];  // e^{G_n - R_{s+1}}
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                eRs[s] = __expf(Rs[s]);
+                eN[s] = __expf(Rs[4] - Rs[s + 1]);
             }
-        Rs[c2][0] = 0.f;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) Rs[c2][s + 1] = Rs[c2][s] + st[s];
-        float eN[4];  // e^{G_n - R_{s+1}}
+            for (int ks = 0; ks < 2; ++ks) {
+                f16x8 kt;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            eRs[c2][s] = __expf(Rs[c2][s]);
-            eN[s] = __expf(Rs[c2][4] - Rs[c2][s + 1]);
-        }
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            f16x8 kt;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int s = 2 * ks + (e >> 2);
-                const int t = 32 * ks + 16 * (e >> 2) + 4 * g + (e & 3);
-                const float cs = gv[ks][e];
-                const float e1 = __expf(cs);
-                const float kf = (float)kb[ks][e];
-                const float cb = kf * __expf(st[s] - cs);  // k e^{R_{s+1} - G_t}
-                sm.a.E1[t * PE + ch] = e1;
-                sm.CB[t * PE + ch] = cb;
-                kt[e] = (_Float16)(cb * eN[s]);             // k e^{G_n - G_t}
-                kga[c2][ks][e] = (__bf16)(kf * (eRs[c2][s] * e1));
+                for (int e = 0; e < 8; ++e) {
+                    const int s = 2 * ks + (e >> 2);
+                    const int t = 32 * ks + 16 * (e >> 2) + 4 * g + (e & 3);
+                    const float cs = gv[ks][e];
+                    const float e1 = __expf(cs);
+                    const float kf = (float)kb[ks][e];
+                    const float cb = kf * __expf(st[s] - cs);  // k e^{R_{s+1} - G_t}
+                    sm.a.E1[t * PEH + chl] = e1;
+                    sm.CB[t * PEH + chl] = cb;
+                    kt[e] = (_Float16)(cb * eN[s]);             // k e^{G_n - G_t}
+                    kga[hf][ks][e] = (__bf16)(kf * (eRs[s] * e1));
+                }
+                *(f16x8 *)(blk + BO_KT + frag((4 * hf + w) * 2 + ks, l)) = kt;
             }
-            *(f16x8 *)(blk + BO_KT + frag((2 * w + c2) * 2 + ks, l)) = kt;
         }
-    }
-    if (g == 0) {
+        if (g == 0) {
 #pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-            const int ch = 32 * w + 16 * c2 + lr;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) sm.eR[s * D + ch] = eRs[c2][s];
+            for (int s = 0; s < 4; ++s) sm.eR[s * D + ch] = eRs[s];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int jj = 0; jj <= i; ++jj)
-                    sm.F[(i * (i + 1) / 2 + jj) * D + ch] = __expf(Rs[c2][i] - Rs[c2][jj + 1]);
-            ((float *)(blk + BO_GM))[ch] = __expf(Rs[c2][4]);
+                    sm.F[(i * (i + 1) / 2 + jj) * D + ch] = __expf(Rs[i] - Rs[jj + 1]);
+            ((float *)(blk + BO_GM))[ch] = __expf(Rs[4]);
+        }
+        __syncthreads();
+
+        // ---- phase 2 (this half): Gram tiles of sub-chunk i = w against j <= i, and Q~.
+        // Row operands x_r e^{G_r - R_i} (x = k, q) are formed once per 32-channel
+        // block; the column operand k_c e^{R_i - G_c} is CB_c e^{R_i - R_{j+1}}: CB
+        // lies in [e^-80, 1] |k|, the factor is <= 1 for j < i (an underflow drops
+        // only terms below e^-87) and in [1, e^80] for j = i.  The channel order
+        // inside each 32-block is perm32, shared by both operands and by Q~.
+        {
+            const int i = w, r = 16 * i + lr;
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh) {
+                __builtin_amdgcn_sched_barrier(0);  // one 32-channel block at a time
+                const int ks = 2 * hf + kh;
+                const int c0 = 32 * ks + 4 * g, cl = 32 * kh + 4 * g;  // global / in-half channel
+                const int ro = r * ph + 2 * c0;                         // rows past the end read as 0
+                const bf16x4 k0 = ld_bf16x4(rk, ro), k1 = ld_bf16x4(rk, ro + 32);
+                const bf16x4 q0 = ld_bf16x4(rq, ro), q1 = ld_bf16x4(rq, ro + 32);
+                const f32x4 ea = *(const f32x4 *)&sm.a.E1[r * PEH + cl], eb = *(const f32x4 *)&sm.a.E1[r * PEH + cl + 16];
+                const f32x4 pa = *(const f32x4 *)&sm.eR[i * D + c0], pb = *(const f32x4 *)&sm.eR[i * D + c0 + 16];
+                F8 xk, xq;
+                f16x8 qt;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    xk.v[m] = (float)k0[m] * ea[m];
+                    xk.v[4 + m] = (float)k1[m] * eb[m];
+                    xq.v[m] = (float)q0[m] * ea[m];
+                    xq.v[4 + m] = (float)q1[m] * eb[m];
+                    qt[m] = (_Float16)(xq.v[m] * pa[m]);
+                    qt[4 + m] = (_Float16)(xq.v[4 + m] * pb[m]);
+                }
+                *(f16x8 *)(blk + BO_QT + frag(4 * i + ks, l)) = qt;
+                const S8 rks = split8(xk), rqs = split8(xq);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (j > i) break;
+                    const int cc = 16 * j + lr;
+                    const float *cb = &sm.CB[cc * PEH + cl];
+                    const float *fij = &sm.F[(i * (i + 1) / 2 + j) * D + c0];
+                    const f32x4 ca = *(const f32x4 *)cb, cbv = *(const f32x4 *)(cb + 16);
+                    const f32x4 fa = *(const f32x4 *)fij, fb = *(const f32x4 *)(fij + 16);
+                    F8 xc;
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        xc.v[m] = ca[m] * fa[m];
+                        xc.v[4 + m] = cbv[m] * fb[m];
+                    }
+                    const S8 cs = split8(xc);
+                    a1[j] = mma_ss(a1[j], cs, rks);
+                    a2[j] = mma_ss(a2[j], cs, rqs);
+                }
+            }
         }
     }
-    __syncthreads();
-
-    // ---- phase 2: Gram tiles of sub-chunk i = w against sub-chunks j <= i, and Q~.
-    // Row operands x_r e^{G_r - R_i} (x = k, q) are formed once per 32-channel
-    // block; the column operand k_c e^{R_i - G_c} is CB_c e^{R_i - R_{j+1}}: CB
-    // lies in [e^-80, 1] |k|, the factor is <= 1 for j < i (an underflow drops
-    // only terms below e^-87) and in [1, e^80] for j = i.
-    // The channel order inside each 32-block is perm32, shared by both operands
-    // and by Q~.  Tiles come out transposed: lane (lr, g) holds row r = 16i + lr
-    // against columns 16j + 4g + m.
     f32x4 akk[4];
     {
         const int i = w, r = 16 * i + lr;
-        f32x4 a1[4], a2[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) a1[j] = a2[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            __builtin_amdgcn_sched_barrier(0);  // one 32-channel block at a time
-            const int c0 = 32 * ks + 4 * g;
-            const int ro = r * ph + 2 * c0;  // rows past the end read as 0
-            const bf16x4 k0 = ld_bf16x4(rk, ro), k1 = ld_bf16x4(rk, ro + 32);
-            const bf16x4 q0 = ld_bf16x4(rq, ro), q1 = ld_bf16x4(rq, ro + 32);
-            const f32x4 ea = *(const f32x4 *)&sm.a.E1[r * PE + c0], eb = *(const f32x4 *)&sm.a.E1[r * PE + c0 + 16];
-            const f32x4 pa = *(const f32x4 *)&sm.eR[i * D + c0], pb = *(const f32x4 *)&sm.eR[i * D + c0 + 16];
-            F8 xk, xq;
-            f16x8 qt;
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                xk.v[m] = (float)k0[m] * ea[m];
-                xk.v[4 + m] = (float)k1[m] * eb[m];
-                xq.v[m] = (float)q0[m] * ea[m];
-                xq.v[4 + m] = (float)q1[m] * eb[m];
-                qt[m] = (_Float16)(xq.v[m] * pa[m]);
-                qt[4 + m] = (_Float16)(xq.v[4 + m] * pb[m]);
-            }
-            *(f16x8 *)(blk + BO_QT + frag(4 * i + ks, l)) = qt;
-            const S8 rk = split8(xk), rq = split8(xq);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (j > i) break;
-                const int cc = 16 * j + lr;
-                // k_c e^{R_i - G_c} = CB_c e^{R_i - R_{j+1}} (rows past the end hold k = 0)
-                const float *cb = &sm.CB[cc * PE + c0];
-                const float *fij = &sm.F[(i * (i + 1) / 2 + j) * D + c0];
-                const f32x4 ca = *(const f32x4 *)cb, cbv = *(const f32x4 *)(cb + 16);
-                const f32x4 fa = *(const f32x4 *)fij, fb = *(const f32x4 *)(fij + 16);
-                F8 xc;
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    xc.v[m] = ca[m] * fa[m];
-                    xc.v[4 + m] = cbv[m] * fb[m];
-                }
-                const S8 cs = split8(xc);
-                a1[j] = mma_ss(a1[j], cs, rk);
-                a2[j] = mma_ss(a2[j], cs, rq);
-            }
-        }
         const float br = sm.beta[r];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -458,9 +459,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WY_WPE))) v
     }
 
     // ---- phase 4: W^T = (K * Gam)^T (T diag(beta))^T and U = T diag(beta) V on
-    // wave w's channels 32w .. 32w+31.  T diag(beta) rows are read in the perm32
-    // token order of the phase-1 registers.  W^T tiles for channel tiles 2w and
-    // 2w+1 form, lane for lane, the two halves of W's A tile (rt, s = w).
+    // wave w's channel tiles w and 4 + w.  T diag(beta) rows are read in the
+    // perm32 token order of the phase-1 registers.  A W^T tile of channel tile
+    // c is, lane for lane, one 8-byte half of W's A tile (rt, s = c / 2).
+    // V in the same operand layout as (K * Gam)^T, read again here (it is not
+    // kept in registers across the Gram phase, which keeps three workgroups on a CU)
+    bf16x8 vb[2][2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int tl = 4 * g + (e & 3), tu = 32 * ks + 16 * (e >> 2);
+                const int ch = 64 * hf + 16 * w + lr;
+                vb[hf][ks][e] = __builtin_bit_cast(
+                    __bf16, (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rv, tl * ph + 2 * ch, tu * ph, 0));
+            }
     {
         S8 tb[4][2];
 #pragma unroll
@@ -481,24 +496,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WY_WPE))) v
             }
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-            f16x8 wo;
 #pragma unroll
-            for (int c2 = 0; c2 < 2; ++c2) {
+            for (int hf = 0; hf < 2; ++hf) {
+                const int ctile = 4 * hf + w;  // channel tile of this wave's registers
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks)
-                    if (ks <= (rt >> 1)) acc = mma_1s(acc, kga[c2][ks], tb[rt][ks]);
+                    if (ks <= (rt >> 1)) acc = mma_1s(acc, kga[hf][ks], tb[rt][ks]);
+                f16x4 wo;
 #pragma unroll
-                for (int m = 0; m < 4; ++m) wo[4 * c2 + m] = (_Float16)(-acc[m]);  // stored negated
-            }
-            *(f16x8 *)(blk + BO_W + frag(4 * rt + w, l)) = wo;
-#pragma unroll
-            for (int c2 = 0; c2 < 2; ++c2) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                for (int m = 0; m < 4; ++m) wo[m] = (_Float16)(-acc[m]);  // stored negated
+                // W^T tile (channels of ctile) = one half of W's A tile (rt, s = ctile / 2)
+                *(f16x4 *)(blk + BO_W + frag(4 * rt + (ctile >> 1), l) + 8 * (ctile & 1)) = wo;
+                f32x4 u = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks)
-                    if (ks <= (rt >> 1)) acc = mma_s1(acc, tb[rt][ks], vb[c2][ks]);
-                *(f32x4 *)(blk + BO_U + frag(8 * rt + 2 * w + c2, l)) = acc;
+                    if (ks <= (rt >> 1)) u = mma_s1(u, tb[rt][ks], vb[hf][ks]);
+                *(f32x4 *)(blk + BO_U + frag(8 * rt + ctile, l)) = u;
             }
         }
     }
