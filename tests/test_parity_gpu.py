@@ -183,3 +183,26 @@ def test_decode_steps_continue_prefill():
     torch.cuda.synchronize()
     o = torch.cat(outs).cpu().numpy()
     assert err(o, o_ref) <= 1e-2 and err(S.cpu().numpy(), S_ref) <= 1e-2
+
+
+@pytest.mark.parametrize("H,T", [(32, 4096), (64, 1000), (1, 5000)])
+def test_head_counts(H, T):
+    """Other head counts change how many segments each head is cut into (about 256 in all)."""
+    d = synth.prefill_inputs(3800 + H, T, H, s0_std=0.02)
+    say(f"case heads H={H} T={T}")
+    o, Sf = run_prefill(d, S0=d["S0"])
+    check(d, o, Sf, label=f"H={H}")
+
+
+def test_serving_batch_mixed_lengths():
+    """Sixty sequences of seeded lengths 0..2500 packed with cu_seqlens (a serving-style batch)."""
+    rng = np.random.Generator(np.random.PCG64(3900))
+    lens = [int(x) for x in rng.integers(0, 2500, size=60)]
+    lens[7] = 0
+    lens[11] = 64
+    cu = synth.cu_seqlens(lens)
+    d = synth.prefill_inputs(3901, int(cu[-1]), 4, s0_std=0.02, n_seqs=len(lens))
+    say(f"case serving batch {len(lens)} sequences, {int(cu[-1])} tokens")
+    o, Sf = run_prefill(d, cu=cu, S0=d["S0"])
+    check(d, o, Sf, cu=cu, label="serving batch")
+    assert np.array_equal(Sf[7], d["S0"][7])
