@@ -47,6 +47,8 @@
 // enter the chain as single fp16; Delta as fp16 hi + lo; Aqk as fp16 hi + lo;
 // the Gram tiles and T diag(beta) as bf16 hi + lo (their column factors reach
 // e^80, beyond fp16 range).
+#include <utility>
+
 #include "kda_common.hpp"
 
 namespace kda {
@@ -79,7 +81,32 @@ __device__ __forceinline__ bf16x4 ld_bf16x4(__amdgpu_buffer_rsrc_t r, int off) {
     return __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }
 
+// fp16 hi/lo split of a pair of floats: hi = fp16(a), fp16(b), lo = fp16 of the
+// remainders.  a - fp32(hi) is exact in fp32, so one mixed-precision FMA per
+// element (fp16 hi and fp32 a as sources, fp16 result) gives the same lo as a
+// subtraction in fp32 followed by a conversion, in one instruction.
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+__device__ __forceinline__ void split_f16_pair(float a, float b, uint32_t &hi, uint32_t &lo) {
+    const f16x2 h = {(_Float16)a, (_Float16)b};
+    hi = __builtin_bit_cast(uint32_t, h);
+    asm("v_fma_mixlo_f16 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mixhi_f16 %0, -%1, 1.0, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+        : "=&v"(lo)
+        : "v"(hi), "v"(a), "v"(b));
+}
+
 constexpr int PTT = 68;  // pitch (floats) of T [64][64]
+
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, expanded at compile time.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 struct SegTable {
     int32_t *seg_off;    // [N+1] first segment of each sequence
@@ -528,8 +555,59 @@ struct ChainLds {
     static constexpr int KT = PASS_A ? 16384 : 32768;
     static constexpr int AQ = 49152;                 // pass B only
     static constexpr int GM = PASS_A ? 32768 : 61440;
-    static constexpr int BYTES = GM + 512;
+    static constexpr int BYTES = GM + 1024;  // gamma, then padding
 };
+
+// The operand stream of one chain step.  Pass A: 16 W tiles (k-step s
+// outermost), 8 gamma rows, 16 K~^T tiles; pass B: 16 (W, Q~) tile pairs, the
+// 6 (hi, lo) pairs of Aqk, 8 gamma rows, 16 K~^T tiles.  `off` is the byte
+// offset in the LDS image of lane 0's fragment (gamma: of row block rt).
+enum { CT_W, CT_Q, CT_AQ_HI, CT_AQ_LO, CT_GAMMA, CT_KT };
+struct ChainTile {
+    int kind, off, rt, s;
+};
+template <bool PASS_A>
+struct ChainTiles {
+    using Lo = ChainLds<PASS_A>;
+    static constexpr int N = PASS_A ? 40 : 68;
+    static constexpr int SPLIT_AFTER = PASS_A ? 15 : 31;  // last tile of Delta = U - W S
+    __device__ static constexpr ChainTile at(int i) {
+        if (PASS_A) {
+            if (i < 16) return {CT_W, Lo::W + 1024 * (4 * (i % 4) + i / 4), i % 4, i / 4};
+            if (i < 24) return {CT_GAMMA, Lo::GM + 64 * (i - 16), i - 16, 0};
+            const int k = i - 24;
+            return {CT_KT, Lo::KT + 1024 * (2 * (k % 8) + k / 8), k % 8, k / 8};
+        }
+        if (i < 32) {
+            const int it = i / 2, rt = it % 4, s = it / 4;
+            return {(i & 1) ? CT_Q : CT_W, ((i & 1) ? Lo::QT : Lo::W) + 1024 * (4 * rt + s), rt, s};
+        }
+        if (i < 44) {
+            const int p = (i - 32) / 2, s = p < 4 ? 0 : 1, rt = p < 4 ? p : p - 2;
+            const int tile = rt < 2 ? rt : 2 * rt - 2 + s;
+            return {(i & 1) ? CT_AQ_LO : CT_AQ_HI, Lo::AQ + 2048 * tile + 1024 * (i & 1), rt, s};
+        }
+        if (i < 52) return {CT_GAMMA, Lo::GM + 64 * (i - 44), i - 44, 0};
+        const int k = i - 52;
+        return {CT_KT, Lo::KT + 1024 * (2 * (k % 8) + k / 8), k % 8, k / 8};
+    }
+};
+
+#ifndef CHAIN_RING_A
+#define CHAIN_RING_A 6
+#endif
+#ifndef CHAIN_RING_B
+#define CHAIN_RING_B 6
+#endif
+#ifndef CHAIN_NBUF_A
+#define CHAIN_NBUF_A 3
+#endif
+// Image-copy instructions one wave issues per chunk in pass A (32 KB over 8
+// waves, and gamma).
+constexpr int CHAIN_DMA_OPS = 5;
+// Pass A's loop body: a common multiple of its image count and the two U
+// register sets.  The segment length L is a multiple of it.
+constexpr int CHAIN_UNROLL_A = CHAIN_NBUF_A == 3 ? 6 : 2;
 
 constexpr int CH_NW = 8;  // waves per chain workgroup
 constexpr int CH_NT = 64 * CH_NW;
@@ -537,23 +615,31 @@ constexpr int CH_NT = 64 * CH_NW;
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Copy one chunk's LDS image straight from its block into LDS
-// (global_load_lds_dwordx4: lane l of a wave lands at dst + 16 l, so each
+// (buffer_load_dwordx4 ... lds: lane l of a wave lands at dst + 16 l, so each
 // instruction moves 1 KB).  Completion is awaited with vmcnt by the caller.
+// A buffer load rather than its global twin: the compiler takes the global
+// form for an access of both memory and LDS, and while one is in flight it
+// waits for every LDS read to complete before the first use of any.
+// With `bytes` = 0 nothing is read and the copy writes zeros: issuing it
+// anyway keeps the number of copies in flight the same at every step.
 template <bool PASS_A>
-__device__ __forceinline__ void chain_dma(const char *__restrict__ blk, char *lds, int wv, int l) {
+__device__ __forceinline__ void chain_dma(const char *__restrict__ blk, int bytes, char *lds, int wv, int l) {
     using Lo = ChainLds<PASS_A>;
     constexpr int NKB = Lo::GM / 1024;
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void *)blk, 0, bytes, BUF_RSRC3);
 #pragma unroll
     for (int i = 0; i < (NKB + CH_NW - 1) / CH_NW; ++i) {
         const int kb = wv + CH_NW * i;
         if (kb < NKB) {
             const int x = 1024 * kb;
             const int src = (PASS_A && x >= Lo::KT) ? BO_KT + (x - Lo::KT) : x;
-            __builtin_amdgcn_global_load_lds((const void *)(blk + src + 16 * l), (lds_void *)(lds + x), 16, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(lds + x), 16, src + 16 * l, 0, 0, 0);
         }
     }
-    if (wv == NKB % CH_NW && l < 32)  // gamma: 512 B
-        __builtin_amdgcn_global_load_lds((const void *)(blk + BO_GM + 16 * l), (lds_void *)(lds + Lo::GM), 16, 0, 0);
+    // gamma (512 B) by every wave, so that each issues the same number of
+    // copies: the waves write the same values, and lanes 32-63 read past the
+    // block (zeros) into padding.
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(lds + Lo::GM), 16, BO_GM + 16 * l, 0, 0, 0);
 }
 
 // One workgroup (8 waves) per (segment, head).  Pass A: wave w owns columns
@@ -563,10 +649,13 @@ template <bool PASS_A>
 __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void seg_chain_kernel(
     int N, int H, SegTable tab, float *__restrict__ o, float *__restrict__ S_final) {
     using Lo = ChainLds<PASS_A>;
-    // Two distinct arrays (not one array indexed by parity): a read of one
-    // then provably does not alias a copy in flight into the other.
+    // Pass A rotates three LDS images (its image is small), pass B two.
+    // Distinct arrays (not one array indexed by step): a read of one then
+    // provably does not alias a copy in flight into another.
+    constexpr int NBUF = PASS_A ? CHAIN_NBUF_A : 2;
     __shared__ __align__(16) char buf0[Lo::BYTES];
     __shared__ __align__(16) char buf1[Lo::BYTES];
+    __shared__ __align__(16) char buf2[NBUF == 3 ? Lo::BYTES : 16];
     constexpr int NCT = PASS_A ? 2 : 1;
 
     const int x = blockIdx.x, h = blockIdx.y;
@@ -584,11 +673,14 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
 
     const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, g = l >> 4,
               lr = l & 15;
+    __builtin_assume(wv >= 0 && wv < CH_NW);
     const size_t HD = (size_t)H * D;
     const size_t sblk = ((size_t)x * H + h) * D * D;
     const int colw = 16 * NCT * wv;  // pass A: columns 0..127 are M, 128..255 are B
-    const bool has_u = !PASS_A || colw >= 128;
-    const int utile = PASS_A ? (colw - 128) / 16 : wv;
+    // U is read through a buffer resource that covers one block, or nothing for
+    // the waves of M (their loads then return 0 without touching memory).
+    const int u_records = (!PASS_A || colw >= 128) ? (int)BLK : 0;
+    const int utile = PASS_A ? max(colw - 128, 0) / 16 : wv;
 
     f32x4 X[8][NCT];
 #pragma unroll
@@ -604,13 +696,16 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
                     X[rt][ct][m] = tab.Sin[sblk + (size_t)r * D + col];
             }
 
+    // Past the segment's last chunk the copies read nothing (and U is 0).
     auto load_u = [&](int chunk, f32x4 (&u)[4][NCT]) {
-        const char *blk = blk0 + chunk * bstride;
+        const __amdgpu_buffer_rsrc_t ru = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(blk0 + (size_t)chunk * bstride), 0, chunk < cend ? u_records : 0, BUF_RSRC3);
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct)
-                u[rt][ct] = has_u ? *(const f32x4 *)(blk + BO_U + frag(8 * rt + utile + ct, l)) : f32x4{0.f, 0.f, 0.f, 0.f};
+                u[rt][ct] = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(ru, BO_U + frag(8 * rt + utile + ct, l), 0, 0));
     };
     // Output rows of chunk n leave at the start of chain step n + 1 and drain
     // during that whole step.
@@ -632,34 +727,52 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
         }
     };
 
-    f32x4 un[4][NCT];  // U of the next chunk, in flight
+    // U of a chunk is loaded one step ahead into one of two register sets; the
+    // set then serves in place as the Delta accumulator of its step.
+    f32x4 ua[4][NCT], ub[4][NCT];
     f32x4 O[4];
     int64_t t0_prev = 0;
     int len_prev = 0;
+    // Copies in flight: the images of the next NBUF - 1 chunks and the U of the
+    // next one.  Issue order (U of chunk n + 1, then the image of chunk
+    // n + NBUF - 1) lets a step wait for everything but the newest image.
+    auto dma = [&](int chunk, char *lds) __attribute__((always_inline)) {
+        chain_dma<PASS_A>(blk0 + (size_t)chunk * bstride, chunk < cend ? (int)BLK : 0, lds, wv, l);
+    };
     if (cbeg < cend) {
-        chain_dma<PASS_A>(blk0 + cbeg * bstride, buf0, wv, l);
-        load_u(cbeg, un);
+        dma(cbeg, buf0);
+        load_u(cbeg, ua);
+        // Keep the two copies in issue order: the first step waits for the
+        // older one only.
+        __builtin_amdgcn_sched_barrier(0);
+        if (NBUF == 3) dma(cbeg + 1, buf1);
     }
 
-    // One chain step on the image in `cur`, prefetching the next chunk into `nxt`.
-    auto step = [&](int chunk, const char *cur, char *nxt) __attribute__((always_inline)) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's copies and U have landed
-        __syncthreads();                                   // every wave's have; `nxt` is free
-        f32x4 Dl[4][NCT];  // Delta starts as U (C layout, rows = tokens)
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) Dl[rt][ct] = un[rt][ct];
+    // One chain step on the image in `cur` (Delta accumulates into Dl, which
+    // holds the chunk's U), prefetching into `nxt` (the image the previous
+    // step read) and `un`.
+    auto step = [&](int chunk, const char *cur, char *nxt, f32x4 (&Dl)[4][NCT], f32x4 (&un)[4][NCT])
+                    __attribute__((always_inline)) {
+        // This wave's copies of this chunk and its U have landed (waits in a
+        // form the compiler sees, so it adds none of its own for them), then
+        // every wave's have, and `nxt` is free.  With three images the newest
+        // copy (at most CHAIN_DMA_OPS instructions of this wave) may still run.
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (NBUF == 3 ? CHAIN_DMA_OPS : 0));
+        // The barrier is a bare s_barrier between compiler-only fences: the
+        // waits above are the only memory ordering needed (no wave writes LDS
+        // but by these copies, and every LDS read of the previous step has
+        // been consumed), and a workgroup fence would also wait for the
+        // newest copy.
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
         if constexpr (!PASS_A)
             if (chunk > cbeg) store_o(O, t0_prev, len_prev);
-        if (chunk + 1 < cend) {
-            chain_dma<PASS_A>(blk0 + (chunk + 1) * bstride, nxt, wv, l);
-            load_u(chunk + 1, un);
-        }
+        load_u(chunk + 1, un);
+        dma(chunk + NBUF - 1, nxt);
 
         const int64_t t0 = s0 + (int64_t)chunk * CH;
         const int len = (int)min((int64_t)CH, s1 - t0);
-        const float *gam = (const float *)(cur + Lo::GM);
         // The state as B operand: k-step s pairs the C tiles 2s and 2s+1.
         f16x8 sf[NCT][4];
 #pragma unroll
@@ -668,75 +781,100 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
             for (int s = 0; s < 4; ++s)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) sf[ct][s][e] = (_Float16)X[2 * s + (e >> 2)][ct][e & 3];
-        // Delta = U - W S and O = Q~ S: k-step outermost, so the accumulators of
-        // a step are independent and each A tile is read once.
+        if constexpr (!PASS_A)
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) O[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                const f16x8 wf = *(const f16x8 *)(cur + Lo::W + frag(4 * rt + s, l));
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) Dl[rt][ct] = mfma_f16(wf, sf[ct][s], Dl[rt][ct]);
-                if constexpr (!PASS_A) {
-                    const f16x8 qf = *(const f16x8 *)(cur + Lo::QT + frag(4 * rt + s, l));
-                    O[rt] = mfma_f16(qf, sf[0][s], O[rt]);
-                }
-            }
+            for (int rt = 0; rt < 4; ++rt) O[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
         f16x8 dh[NCT][2], dlo[NCT][2];  // Delta as B operand (tokens), fp16 hi + lo
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float d = Dl[2 * s + (e >> 2)][ct][e & 3];
-                    const _Float16 hh = (_Float16)d;
-                    dh[ct][s][e] = hh;
-                    dlo[ct][s][e] = (_Float16)(d - (float)hh);
-                }
-        if constexpr (!PASS_A) {  // O += (Aqk * Tril) Delta
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt) {
-                    if (s > (rt >> 1)) continue;
-                    const char *aq = cur + Lo::AQ + aq_tile(rt, s) * 2048;
-                    const f16x8 ah = *(const f16x8 *)(aq + l * 16);
-                    const f16x8 al = *(const f16x8 *)(aq + 1024 + l * 16);
-                    O[rt] = mfma_f16(al, dh[0][s], O[rt]);
-                    O[rt] = mfma_f16(ah, dlo[0][s], O[rt]);
-                    O[rt] = mfma_f16(ah, dh[0][s], O[rt]);
-                }
-            t0_prev = t0;
-            len_prev = len;
-        }
-        // S <- Diag(gamma) S + K~^T Delta, eight independent accumulators per k-step
-#pragma unroll
-        for (int rt = 0; rt < 8; ++rt) {
-            const f32x4 gm = *(const f32x4 *)&gam[16 * rt + 4 * g];
+        auto split_delta = [&]() __attribute__((always_inline)) {
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-                for (int m = 0; m < 4; ++m) X[rt][ct][m] *= gm[m];
-        }
+                for (int s = 0; s < 2; ++s) {
+                    uint32_t hw[4], lw[4];
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-            for (int rt = 0; rt < 8; ++rt) {
-                const f16x8 kf = *(const f16x8 *)(cur + Lo::KT + frag(2 * rt + s, l));
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) {
-                    X[rt][ct] = mfma_f16(kf, dlo[ct][s], X[rt][ct]);
-                    X[rt][ct] = mfma_f16(kf, dh[ct][s], X[rt][ct]);
+                    for (int p = 0; p < 4; ++p) {
+                        const f32x4 &d = Dl[2 * s + (p >> 1)][ct];
+                        split_f16_pair(d[2 * (p & 1)], d[2 * (p & 1) + 1], hw[p], lw[p]);
+                    }
+                    dh[ct][s] = __builtin_bit_cast(f16x8, u32x4{hw[0], hw[1], hw[2], hw[3]});
+                    dlo[ct][s] = __builtin_bit_cast(f16x8, u32x4{lw[0], lw[1], lw[2], lw[3]});
                 }
+        };
+        // Every 16-byte LDS operand of the step, in the order the products use
+        // them, is read RING tiles ahead of its use; a scheduling fence after
+        // every group of tiles keeps the reads there (left alone, the reads sink
+        // next to their products and each waits out the LDS latency).
+        constexpr int NT = ChainTiles<PASS_A>::N, RING = PASS_A ? CHAIN_RING_A : CHAIN_RING_B, GROUP = 4;
+        const char *lane_frag = cur + 16 * l, *lane_gam = cur + 16 * g;
+        auto ld = [&](int i) __attribute__((always_inline)) {
+            const ChainTile d = ChainTiles<PASS_A>::at(i);
+            return *(const u32x4 *)((d.kind == CT_GAMMA ? lane_gam : lane_frag) + d.off);
+        };
+        u32x4 ring[RING];
+#pragma unroll
+        for (int i = 0; i < RING; ++i) ring[i] = ld(i);
+        static_for<NT>([&](auto ic) __attribute__((always_inline)) {
+            constexpr int i = decltype(ic)::value;
+            constexpr ChainTile d = ChainTiles<PASS_A>::at(i);
+            constexpr int rt = d.rt, s = d.s;
+            const u32x4 t = ring[i % RING];
+            if constexpr (i + RING < NT) ring[i % RING] = ld(i + RING);
+            const f16x8 a = __builtin_bit_cast(f16x8, t);
+            if constexpr (d.kind == CT_W) {  // Delta = U - W S
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) Dl[rt][ct] = mfma_f16(a, sf[ct][s], Dl[rt][ct]);
+            } else if constexpr (d.kind == CT_Q) {  // O = Q~ S
+                O[rt] = mfma_f16(a, sf[0][s], O[rt]);
+            } else if constexpr (d.kind == CT_AQ_HI) {  // O += (Aqk * Tril) Delta
+                O[rt] = mfma_f16(a, dlo[0][s], O[rt]);
+                O[rt] = mfma_f16(a, dh[0][s], O[rt]);
+            } else if constexpr (d.kind == CT_AQ_LO) {
+                O[rt] = mfma_f16(a, dh[0][s], O[rt]);
+            } else if constexpr (d.kind == CT_GAMMA) {  // S <- Diag(gamma) S ...
+                const f32x4 gm = __builtin_bit_cast(f32x4, t);
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) X[rt][ct][m] *= gm[m];
+            } else {  // ... + K~^T Delta
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) X[rt][ct] = mfma_f16(a, dlo[ct][s], X[rt][ct]);
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) X[rt][ct] = mfma_f16(a, dh[ct][s], X[rt][ct]);
             }
+            if constexpr (i == ChainTiles<PASS_A>::SPLIT_AFTER) split_delta();
+            if constexpr (i % GROUP == GROUP - 1) __builtin_amdgcn_sched_barrier(0);
+        });
+        if constexpr (!PASS_A) {
+            t0_prev = t0;
+            len_prev = len;
+        }
     };
-    for (int chunk = cbeg; chunk < cend; chunk += 2) {
-        step(chunk, buf0, buf1);
-        if (chunk + 1 < cend) step(chunk + 1, buf1, buf0);
+    // Unrolled so that every step's image and U set are fixed arrays.
+    constexpr int UNROLL = PASS_A ? CHAIN_UNROLL_A : 2;
+    auto buf = [&](auto ic) -> char * {
+        constexpr int b = decltype(ic)::value % NBUF;
+        if constexpr (b == 0) return buf0;
+        else if constexpr (b == 1) return buf1;
+        else return buf2;
+    };
+    for (int chunk = cbeg; chunk < cend; chunk += UNROLL) {
+        static_for<UNROLL>([&](auto ic) __attribute__((always_inline)) {
+            constexpr int i = decltype(ic)::value;
+            // Every pass-A segment holds a whole number of unrolled groups (the
+            // host picks L so), so its steps need no bound check; a check would
+            // also cost the compiler its view of which image each copy writes.
+            if (PASS_A || chunk + i < cend) {
+                if constexpr (i % 2 == 0)
+                    step(chunk + i, buf(ic), buf(std::integral_constant<int, i + NBUF - 1>{}), ua, ub);
+                else
+                    step(chunk + i, buf(ic), buf(std::integral_constant<int, i + NBUF - 1>{}), ub, ua);
+            }
+        });
     }
+    // The copies issued past the last chunk still write LDS: let them land
+    // before the workgroup can end and its LDS be handed on.
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     if constexpr (!PASS_A)
         if (cbeg < cend) store_o(O, t0_prev, len_prev);
 
@@ -831,7 +969,8 @@ static inline int seg_len(int64_t T_total, int H) {
     const int64_t nc = (T_total + CH - 1) / CH;
     const int64_t per_head = SEG_TARGET_WGS / (H > 0 ? H : 1) > 0 ? SEG_TARGET_WGS / H : 1;
     int64_t L = (nc + per_head - 1) / per_head;
-    return (int)(L < 1 ? 1 : L);
+    L = (L + CHAIN_UNROLL_A - 1) / CHAIN_UNROLL_A * CHAIN_UNROLL_A;  // whole groups of pass-A steps
+    return (int)L;
 }
 static inline int64_t seg_chunks_max(int64_t T_total, int N) { return (T_total + CH - 1) / CH + N; }
 static inline int64_t seg_max(int64_t T_total, int N, int H) {
