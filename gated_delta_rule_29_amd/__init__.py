@@ -58,6 +58,8 @@ def load():
                                   sz, P]
     lib.kda_chunk_fwd.restype = ctypes.c_int
     lib.kda_chunk_fwd_timed.argtypes = lib.kda_chunk_fwd.argtypes + [P]
+    lib.kda_chunk_fwd_ckpt.argtypes = lib.kda_chunk_fwd.argtypes[:17] + [P, i64, i64] + lib.kda_chunk_fwd.argtypes[17:]
+    lib.kda_chunk_fwd_ckpt.restype = ctypes.c_int
     lib.kda_chunk_fwd_timed.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [P, P, P, ctypes.c_int, P, P, P, P, i32, i32, i32, i32, P, P]
     lib.kda_decode_step.restype = ctypes.c_int
@@ -100,8 +102,14 @@ def kda_chunk_fwd_workspace_bytes(T_total: int, n_seqs: int, H: int, dtype=torch
     return int(load().kda_chunk_fwd_workspace_bytes(int(T_total), int(n_seqs), int(H), code))
 
 
+def ckpt_count(lengths, stride: int) -> int:
+    """Snapshot slots kda_chunk_fwd needs for sequences of these lengths: sum of len // stride."""
+    return int(sum(int(n) // int(stride) for n in lengths))
+
+
 def kda_chunk_fwd(q, k, v, g_raw, beta, A, S0=None, cu_seqlens=None, *, o=None, S_final=None,
-                  workspace=None, stream=None, return_final_state=True, stage_events=None):
+                  workspace=None, stream=None, return_final_state=True, stage_events=None,
+                  S_ckpt=None, ckpt_stride=0):
     """Chunkwise KDA prefill.
 
     q, k, v: [B, T, H, 128] (or [T, H, 128]) bf16 or fp32; g_raw: same shape fp32 (the gate's z);
@@ -109,6 +117,9 @@ def kda_chunk_fwd(q, k, v, g_raw, beta, A, S0=None, cu_seqlens=None, *, o=None, 
     cu_seqlens: int32 device tensor [N+1] packing N sequences along T (then B must be 1).
     Returns (o [.., H, 128] fp32, S_final [N, H, 128, 128] fp32 or None).
     stage_events: optional ctypes array of six hipEvent_t recorded at the library's stage boundaries.
+    S_ckpt, ckpt_stride: optional state snapshots (kda_chunk_fwd_ckpt): S_ckpt is an fp32 tensor
+    [slots, H, 128, 128] (see ckpt_count), filled with the state after every ckpt_stride tokens of each
+    sequence, sequence after sequence.
     """
     lib = load()
     squeeze = q.dim() == 3
@@ -152,11 +163,20 @@ def kda_chunk_fwd(q, k, v, g_raw, beta, A, S0=None, cu_seqlens=None, *, o=None, 
     args = (_ptr(q), _ptr(k), _ptr(v), dtype, _ptr(g_raw), _ptr(beta), _ptr(A), _ptr(S0),
             _ptr(cu_seqlens), B, T, H, N, dk, dv, _ptr(o), _ptr(S_final), _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream(stream))
-    if stage_events is None:
+    if S_ckpt is not None:
+        if stage_events is not None:
+            raise ValueError("stage_events and S_ckpt cannot be combined")
+        _need(S_ckpt, "S_ckpt", (torch.float32,), dev)
+        if S_ckpt.dim() != 4 or S_ckpt.shape[1:] != (H, dk, dv):
+            raise ValueError(f"S_ckpt must be [slots, {H}, {dk}, {dv}]")
+        rc = lib.kda_chunk_fwd_ckpt(*args[:17], _ptr(S_ckpt), int(ckpt_stride), S_ckpt.shape[0], *args[17:])
+        _check(rc, "kda_chunk_fwd_ckpt")
+    elif stage_events is None:
         rc = lib.kda_chunk_fwd(*args)
+        _check(rc, "kda_chunk_fwd")
     else:
         rc = lib.kda_chunk_fwd_timed(*args, ctypes.cast(stage_events, ctypes.c_void_p))
-    _check(rc, "kda_chunk_fwd")
+        _check(rc, "kda_chunk_fwd")
     if squeeze:
         o = o.squeeze(0)
     return o, S_final

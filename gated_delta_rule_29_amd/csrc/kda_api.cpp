@@ -8,6 +8,7 @@
 #include <mutex>
 
 #include "kda.h"
+#include "kda_common.hpp"
 
 #define KDA_EXPORT extern "C" __attribute__((visibility("default")))
 
@@ -16,7 +17,7 @@ int launch_decode(const void *q, const void *k, const void *v, bool f32io, const
                   const float *A, float *S, int N, int H, float *o, hipStream_t stream);
 int launch_prefill(const void *q, const void *k, const void *v, bool f32io, const float *z, const float *beta,
                    const float *A, const float *S0, const int32_t *cu, int B, int64_t T, int H, int N,
-                   float *o, float *S_final, void *ws, hipStream_t stream, hipEvent_t *ev);
+                   float *o, float *S_final, const Ckpt &ck, void *ws, hipStream_t stream, hipEvent_t *ev);
 size_t prefill_workspace_bytes(int64_t T_total, int N, int H, bool f32io);
 int set_prefill_attributes();
 }  // namespace kda
@@ -63,11 +64,14 @@ KDA_EXPORT size_t kda_chunk_fwd_workspace_bytes(int64_t T_total, int32_t n_seqs,
     return kda::prefill_workspace_bytes(T_total, n_seqs, H, qkv_dtype == KDA_F32);
 }
 
-KDA_EXPORT int kda_chunk_fwd_timed(const void *q, const void *k, const void *v, kda_dtype qkv_dtype,
-                                   const float *g_raw, const float *beta, const float *A, const float *S0,
-                                   const int32_t *cu_seqlens, int32_t B, int64_t T, int32_t H, int32_t n_seqs,
-                                   int32_t dk, int32_t dv, float *o, float *S_final, void *workspace,
-                                   size_t workspace_bytes, void *stream, void *const *stage_events) {
+namespace {
+
+// Shared body of the prefill entry points.
+int chunk_fwd(const void *q, const void *k, const void *v, kda_dtype qkv_dtype, const float *g_raw,
+              const float *beta, const float *A, const float *S0, const int32_t *cu_seqlens, int32_t B, int64_t T,
+              int32_t H, int32_t n_seqs, int32_t dk, int32_t dv, float *o, float *S_final, void *workspace,
+              size_t workspace_bytes, void *stream, void *const *stage_events, float *S_ckpt, int64_t ckpt_stride,
+              int64_t ckpt_capacity) {
     if (dk != kD || dv != kD) return KDA_ERR_SHAPE;
     if (B < 0 || T < 0 || H < 0 || n_seqs < 0) return KDA_ERR_SHAPE;
     if (qkv_dtype != KDA_BF16 && qkv_dtype != KDA_F32) return KDA_ERR_DTYPE;
@@ -76,12 +80,16 @@ KDA_EXPORT int kda_chunk_fwd_timed(const void *q, const void *k, const void *v, 
     } else if (n_seqs != B) {
         return KDA_ERR_SEQLENS;
     }
+    if (S_ckpt && (ckpt_stride <= 0 || ckpt_stride % 64 != 0 || ckpt_stride / 64 > INT32_MAX || ckpt_capacity < 0))
+        return KDA_ERR_SHAPE;
     const int64_t T_total = (int64_t)B * T;
     if (T_total > INT32_MAX - 64 || (int64_t)n_seqs * H > INT32_MAX / 64) return KDA_ERR_SHAPE;
+    if (S_ckpt && ckpt_capacity > (int64_t)(SIZE_MAX / 2) / ((int64_t)(H > 0 ? H : 1) * kD * kD * 4))
+        return KDA_ERR_SHAPE;
     if (n_seqs == 0 || H == 0) return KDA_OK;  // nothing to compute
     if (!A) return KDA_ERR_NULL;
     if (T_total > 0 && (!q || !k || !v || !g_raw || !beta || !o)) return KDA_ERR_NULL;
-    const void *ptrs[] = {q, k, v, g_raw, beta, A, S0, o, S_final, workspace};
+    const void *ptrs[] = {q, k, v, g_raw, beta, A, S0, o, S_final, workspace, S_ckpt};
     for (const void *p : ptrs)
         if (misaligned(p)) return KDA_ERR_ALIGN;
     const size_t need = kda_chunk_fwd_workspace_bytes(T_total, n_seqs, H, qkv_dtype);
@@ -96,13 +104,34 @@ KDA_EXPORT int kda_chunk_fwd_timed(const void *q, const void *k, const void *v, 
         overlap(o, o_bytes, S0, st_bytes) || overlap(o, o_bytes, S_final, st_bytes) ||
         overlap(o, o_bytes, workspace, need))
         return KDA_ERR_ALIAS;
+    if (S_ckpt) {
+        const size_t ck_bytes = (size_t)ckpt_capacity * H * kD * kD * 4;
+        const void *others[] = {q, k, v, g_raw, beta, A, S0, o, S_final, workspace};
+        const size_t sizes[] = {tok * kD * esz, tok * kD * esz, tok * kD * esz, tok * kD * 4, tok * 4,
+                                (size_t)H * 4, st_bytes, o_bytes, st_bytes, need};
+        for (int i = 0; i < 10; ++i)
+            if (overlap(S_ckpt, ck_bytes, others[i], sizes[i])) return KDA_ERR_ALIAS;
+    }
 
     std::call_once(g_attr_once, [] { g_attr_status = kda::set_prefill_attributes(); });
     if (g_attr_status != 0) return KDA_ERR_HIP;
+    const kda::Ckpt ck{S_ckpt && ckpt_capacity > 0 ? S_ckpt : nullptr, nullptr, (int)(S_ckpt ? ckpt_stride / 64 : 1),
+                       ckpt_capacity};
     const int rc = kda::launch_prefill(q, k, v, qkv_dtype == KDA_F32, g_raw, beta, A, S0, cu_seqlens, B, T, H,
-                                       n_seqs, o, S_final, workspace, (hipStream_t)stream,
+                                       n_seqs, o, S_final, ck, workspace, (hipStream_t)stream,
                                        (hipEvent_t *)stage_events);
     return rc == 0 ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // namespace
+
+KDA_EXPORT int kda_chunk_fwd_timed(const void *q, const void *k, const void *v, kda_dtype qkv_dtype,
+                                   const float *g_raw, const float *beta, const float *A, const float *S0,
+                                   const int32_t *cu_seqlens, int32_t B, int64_t T, int32_t H, int32_t n_seqs,
+                                   int32_t dk, int32_t dv, float *o, float *S_final, void *workspace,
+                                   size_t workspace_bytes, void *stream, void *const *stage_events) {
+    return chunk_fwd(q, k, v, qkv_dtype, g_raw, beta, A, S0, cu_seqlens, B, T, H, n_seqs, dk, dv, o, S_final,
+                     workspace, workspace_bytes, stream, stage_events, nullptr, 0, 0);
 }
 
 KDA_EXPORT int kda_chunk_fwd(const void *q, const void *k, const void *v, kda_dtype qkv_dtype,
@@ -110,8 +139,19 @@ KDA_EXPORT int kda_chunk_fwd(const void *q, const void *k, const void *v, kda_dt
                              const int32_t *cu_seqlens, int32_t B, int64_t T, int32_t H, int32_t n_seqs,
                              int32_t dk, int32_t dv, float *o, float *S_final, void *workspace,
                              size_t workspace_bytes, void *stream) {
-    return kda_chunk_fwd_timed(q, k, v, qkv_dtype, g_raw, beta, A, S0, cu_seqlens, B, T, H, n_seqs, dk, dv, o,
-                               S_final, workspace, workspace_bytes, stream, nullptr);
+    return chunk_fwd(q, k, v, qkv_dtype, g_raw, beta, A, S0, cu_seqlens, B, T, H, n_seqs, dk, dv, o, S_final,
+                     workspace, workspace_bytes, stream, nullptr, nullptr, 0, 0);
+}
+
+KDA_EXPORT int kda_chunk_fwd_ckpt(const void *q, const void *k, const void *v, kda_dtype qkv_dtype,
+                                  const float *g_raw, const float *beta, const float *A, const float *S0,
+                                  const int32_t *cu_seqlens, int32_t B, int64_t T, int32_t H, int32_t n_seqs,
+                                  int32_t dk, int32_t dv, float *o, float *S_final, float *S_ckpt,
+                                  int64_t ckpt_stride, int64_t ckpt_capacity, void *workspace,
+                                  size_t workspace_bytes, void *stream) {
+    if (!S_ckpt) return KDA_ERR_NULL;
+    return chunk_fwd(q, k, v, qkv_dtype, g_raw, beta, A, S0, cu_seqlens, B, T, H, n_seqs, dk, dv, o, S_final,
+                     workspace, workspace_bytes, stream, nullptr, S_ckpt, ckpt_stride, ckpt_capacity);
 }
 
 KDA_EXPORT int kda_decode_step(const void *q, const void *k, const void *v, kda_dtype qkv_dtype,

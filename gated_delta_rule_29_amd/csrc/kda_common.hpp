@@ -26,6 +26,20 @@ constexpr float GMIN = -5.f;  // Kimi K3 lower bound of the log-decay
 
 __host__ __device__ constexpr size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// State snapshots at a chunk-aligned stride, for a KDA-aware prefix cache
+// (Kimi K3 paper review, Significance and Limitations paragraphs: the recurrent
+// state is kept only at sparse checkpoint boundaries).  Snapshot m of sequence
+// n is the state after its first (m + 1) * stride tokens, stored at slot
+// off[n] + m of S, where off is the exclusive prefix sum of floor(len / stride)
+// over the sequences; slots at or past `cap` are not written.  S == nullptr
+// turns snapshots off.
+struct Ckpt {
+    float *S;
+    const int64_t *off;  // [N + 1], built on the device by ckpt_prep_kernel
+    int stride_chunks;   // stride / 64
+    int64_t cap;
+};
+
 __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }

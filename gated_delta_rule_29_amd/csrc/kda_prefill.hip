@@ -57,11 +57,13 @@ struct Table {  // workspace header
     int32_t *chunk_off;  // [N+1] first chunk of each sequence; chunk_off[N] = total
     int64_t *seq_start;  // [N]
     int64_t *seq_end;    // [N]
+    int64_t *ckpt_off;   // [N+1] first snapshot slot of each sequence
     char *blocks;        // chain operands, block (c, h) at (c * H + h) * BLK_BYTES
+    Ckpt ck;
 };
 
 __host__ __device__ inline size_t table_bytes(int N) {
-    return align256(4 * (size_t)(N + 1)) + 2 * align256(8 * (size_t)N);
+    return align256(4 * (size_t)(N + 1)) + 2 * align256(8 * (size_t)N) + align256(8 * (size_t)(N + 1));
 }
 __host__ __device__ inline Table carve(void *ws, int N) {
     char *p = (char *)ws;
@@ -72,7 +74,10 @@ __host__ __device__ inline Table carve(void *ws, int N) {
     p += align256(8 * (size_t)N);
     t.seq_end = (int64_t *)p;
     p += align256(8 * (size_t)N);
+    t.ckpt_off = (int64_t *)p;
+    p += align256(8 * (size_t)(N + 1));
     t.blocks = p;
+    t.ck = Ckpt{nullptr, t.ckpt_off, 1, 0};
     return t;
 }
 __host__ inline int64_t max_chunks(int64_t T_total, int N) { return (T_total + CH - 1) / CH + N; }
@@ -136,6 +141,41 @@ __global__ __launch_bounds__(256) void prep_kernel(const int32_t *__restrict__ c
     }
 }
 
+// off[n] = sum over sequences m < n of floor(len_m / stride), n = 0 .. N: the
+// first snapshot slot of each sequence.  One workgroup, tiles of 256 with a
+// running sum.
+__global__ __launch_bounds__(256) void ckpt_prep_kernel(const int64_t *__restrict__ seq_start,
+                                                        const int64_t *__restrict__ seq_end, int N, int64_t stride,
+                                                        int64_t *__restrict__ off) {
+    __shared__ int64_t s_scan[256];
+    __shared__ int64_t s_prev;
+    const int tid = threadIdx.x;
+    if (tid == 0) s_prev = 0;
+    __syncthreads();
+    for (int base = 0; base <= N; base += 256) {
+        const int m = base + tid;  // off[m] sums sequences < m: exclusive scan
+        s_scan[tid] = (m >= 1 && m <= N) ? (seq_end[m - 1] - seq_start[m - 1]) / stride : 0;
+        __syncthreads();
+        for (int d = 1; d < 256; d <<= 1) {
+            const int64_t x = tid >= d ? s_scan[tid - d] : 0;
+            __syncthreads();
+            s_scan[tid] += x;
+            __syncthreads();
+        }
+        const int64_t incl = s_scan[tid] + s_prev;
+        if (m <= N) off[m] = incl;
+        __syncthreads();
+        if (tid == 255) s_prev = incl;
+        __syncthreads();
+    }
+}
+
+int launch_ckpt_prep(const int64_t *seq_start, const int64_t *seq_end, int N, int64_t stride, int64_t *off,
+                     hipStream_t stream) {
+    hipLaunchKernelGGL(ckpt_prep_kernel, dim3(1), dim3(256), 0, stream, seq_start, seq_end, N, stride, off);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 // locate chunk c: sequence n with chunk_off[n] <= c < chunk_off[n+1]
 __device__ inline int find_seq(const int32_t *chunk_off, int N, int c) {
     int lo = 0, hi = N - 1;
@@ -160,7 +200,7 @@ struct IntraSmem {
     float KG[D * PT];      // (K * Gam)^T  [channel][token]
     float Vt[D * PT];      // V^T          [channel][token]
     float Akk[CH * PT];    // Akk, then T = (I + Akk)^{-1} in place
-    float R[5 * D];        // R_s: cumulative log-decay before sub-chunk s (R_4 = G_n)
+    double R[5 * D];       // R_s: cumulative log-decay before sub-chunk s (R_4 = G_n)
     float PF[6 * D];       // e^{R_i - R_j} for the six sub-chunk pairs j < i
     float beta[CH];
 };
@@ -218,26 +258,30 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
     // ---- phase 1: gate, sub-chunk cumulative sums, elementwise operands ----
     const int ch = tid & (D - 1), half = tid >> 7;
     const float eA = __expf(A[h]);
-    float Gl[2][SUB];
+    // The running sums are kept in fp64: a log-decay difference formed from
+    // fp32 sums of up to 64 gates (|G| up to 320) loses ~1e-5 absolute, which
+    // the exponential turns into relative error of every decay factor.  Only
+    // the final argument of each exponential is rounded to fp32.
+    double Gl[2][SUB];
 #pragma unroll
     for (int si = 0; si < 2; ++si) {
         const int s = half + 2 * si;
-        float acc = 0.f;
+        double acc = 0.0;
 #pragma unroll
         for (int u = 0; u < SUB; ++u) {
             const int t = s * SUB + u;
             const float gt = t < len ? kda_gate(eA, z[tok(t) + ch]) : 0.f;
-            acc += gt;
+            acc += (double)gt;
             Gl[si][u] = acc;
-            sm.E1[t * PG + ch] = __expf(acc);
+            sm.E1[t * PG + ch] = __expf((float)acc);
         }
         sm.R[(s + 1) * D + ch] = acc;  // sub-chunk total, turned into R below
     }
     if (tid < CH) sm.beta[tid] = tid < len ? beta[(size_t)(t0 + tid) * H + h] : 0.f;
     __syncthreads();
     if (tid < D) {
-        float r = 0.f;
-        sm.R[tid] = 0.f;
+        double r = 0.0;
+        sm.R[tid] = 0.0;
 #pragma unroll
         for (int s = 1; s <= 4; ++s) {
             r += sm.R[s * D + tid];
@@ -249,21 +293,21 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
 #pragma unroll
         for (int i = 1; i < 4; ++i)
             for (int j = 0; j < i; ++j)
-                sm.PF[pair_index(i, j) * D + tid] = __expf(sm.R[i * D + tid] - sm.R[j * D + tid]);
+                sm.PF[pair_index(i, j) * D + tid] = __expf((float)(sm.R[i * D + tid] - sm.R[j * D + tid]));
     }
     {
-        const float Gn = sm.R[4 * D + ch];
+        const double Gn = sm.R[4 * D + ch];
         char *qt = blk + OFF_QT, *kt = blk + OFF_KT;
 #pragma unroll
         for (int si = 0; si < 2; ++si) {
             const int s = half + 2 * si;
-            const float Rs = sm.R[s * D + ch];
+            const double Rs = sm.R[s * D + ch];
             float kt_vals[SUB];
 #pragma unroll
             for (int u = 0; u < SUB; ++u) {
                 const int t = s * SUB + u;
-                const float Gt = Rs + Gl[si][u];
-                const float gam = __expf(Gt);
+                const double Gt = Rs + Gl[si][u];
+                const float gam = __expf((float)Gt);
                 const bool ok = t < len;
                 const float kv = ok ? to_f(k[tok(t) + ch]) : 0.f;
                 const float qv = ok ? to_f(q[tok(t) + ch]) : 0.f;
@@ -271,14 +315,14 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
                 sm.KG[ch * PT + t] = kv * gam;
                 sm.Vt[ch * PT + t] = vv;
                 st_split1<F32>(qt, CH * D, (size_t)t * D + ch, qv * gam);
-                kt_vals[u] = kv * __expf(Gn - Gt);
+                kt_vals[u] = kv * __expf((float)(Gn - Gt));
             }
 #pragma unroll
             for (int u = 0; u < SUB; u += 4)
                 st_split4<F32>(kt, D * CH, (size_t)ch * CH + s * SUB + u, kt_vals[u], kt_vals[u + 1],
                                kt_vals[u + 2], kt_vals[u + 3]);
         }
-        if (half == 0) ((float *)(blk + OFF_GM))[ch] = __expf(Gn);
+        if (half == 0) ((float *)(blk + OFF_GM))[ch] = __expf((float)Gn);
     }
     // the six tiles of Aqk above the diagonal are zero
     for (int e = tid; e < 6 * 64; e += 256) {
@@ -478,6 +522,7 @@ __global__ __launch_bounds__(256) void chain_kernel(const float *__restrict__ S0
     const int cbeg = tab.chunk_off[n], cend = tab.chunk_off[n + 1];
     const int64_t sstart = tab.seq_start[n], send = tab.seq_end[n];
     const int nks_aq = w < 2 ? 1 : 2;  // 32-token k-steps of Aqk row tile w
+    const int64_t ck_base = tab.ck.S ? tab.ck.off[n] : 0;
 
     for (int c = cbeg; c < cend; ++c) {
         const char *blk = tab.blocks + ((size_t)c * H + h) * BLK_BYTES;
@@ -594,6 +639,17 @@ __global__ __launch_bounds__(256) void chain_kernel(const float *__restrict__ S0
             }
             Sr[u] = acc;
         }
+        // (5b) snapshot after a full chunk that ends a stride
+        if (tab.ck.S && len == CH && (c - cbeg + 1) % tab.ck.stride_chunks == 0) {
+            const int64_t slot = ck_base + (c - cbeg + 1) / tab.ck.stride_chunks - 1;
+            if (slot < tab.ck.cap) {
+                float *dst = tab.ck.S + ((size_t)slot * H + h) * D * D;
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) dst[(size_t)(32 * w + 16 * u + 4 * g + m) * D + col0 + lr] = Sr[u][m];
+            }
+        }
         // (6) output rows of this chunk
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
@@ -615,7 +671,8 @@ __global__ __launch_bounds__(256) void chain_kernel(const float *__restrict__ S0
 size_t seg_workspace_bytes(int64_t T_total, int N, int H);
 int launch_segment_prefill(const __bf16 *q, const __bf16 *k, const __bf16 *v, const float *z, const float *beta,
                            const float *A, const float *S0, const int32_t *cu, int B, int64_t T, int H, int N,
-                           float *o, float *S_final, void *ws, hipStream_t stream, hipEvent_t *ev);
+                           float *o, float *S_final, const Ckpt &ck, void *ws, hipStream_t stream,
+                           hipEvent_t *ev);
 int set_segment_attributes();
 
 // bf16 q/k/v run the segment-parallel fused path (kda_segment.hip); fp32 q/k/v
@@ -625,16 +682,22 @@ size_t prefill_workspace_bytes(int64_t T_total, int N, int H, bool f32io) {
     return table_bytes(N) + (size_t)max_chunks(T_total, N) * (size_t)H * BLK_BYTES;
 }
 
+// ck.S == nullptr: no snapshots (ck.off is ignored; the launchers point it at
+// their workspace).
 int launch_prefill(const void *q, const void *k, const void *v, bool f32io, const float *z, const float *beta,
                    const float *A, const float *S0, const int32_t *cu, int B, int64_t T, int H, int N,
-                   float *o, float *S_final, void *ws, hipStream_t stream, hipEvent_t *ev) {
+                   float *o, float *S_final, const Ckpt &ck, void *ws, hipStream_t stream, hipEvent_t *ev) {
     if (!f32io)
         return launch_segment_prefill((const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, z, beta, A, S0, cu, B,
-                                      T, H, N, o, S_final, ws, stream, ev);
+                                      T, H, N, o, S_final, ck, ws, stream, ev);
     const int64_t T_total = (int64_t)B * T;
     Table tab = carve(ws, N);
+    tab.ck = Ckpt{ck.S, tab.ckpt_off, ck.stride_chunks, ck.cap};
     if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return -1;
     hipLaunchKernelGGL(prep_kernel, dim3(1), dim3(256), 0, stream, cu, N, T_total, cu ? (int64_t)0 : T, tab);
+    if (ck.S && launch_ckpt_prep(tab.seq_start, tab.seq_end, N, (int64_t)ck.stride_chunks * CH, tab.ckpt_off,
+                                 stream) != 0)
+        return -1;
     const int64_t nc = max_chunks(T_total, N);
     if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return -1;
     if (T_total > 0) {

@@ -118,6 +118,7 @@ struct SegTable {
     float *Bseg;         // [nseg][H][128][128] segment offsets
     float *Sin;          // [nseg][H][128][128] state entering each segment
     int L;               // chunks per segment
+    Ckpt ck;             // state snapshots (ck.S == nullptr: none)
 };
 
 // ------------------------------------------------------------------ prep --
@@ -707,6 +708,24 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
                 u[rt][ct] = __builtin_bit_cast(
                     f32x4, __builtin_amdgcn_raw_buffer_load_b128(ru, BO_U + frag(8 * rt + utile + ct, l), 0, 0));
     };
+    // A full state (this wave's columns) to dst [128][128]: buffer stores with
+    // the row offset as a scalar operand, so the lane offset is one register.
+    const int64_t ck_base = (!PASS_A && tab.ck.S) ? tab.ck.off[n] : 0;
+    auto store_state = [&](float *dst) {
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(dst + colw), 0, D * D * 4, BUF_RSRC3);
+        const int lane_off = (4 * g * D + lr) * 4;
+#pragma unroll
+        for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const float val = X[rt][ct][m];  // a value: a bit-cast of the element expression reads element 0
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val), rs, lane_off,
+                                                          ((16 * rt + m) * D + 16 * ct) * 4, 0);
+                }
+    };
     // Output rows of chunk n leave at the start of chain step n + 1 and drain
     // during that whole step.
     auto store_o = [&](const f32x4 (&O)[4], int64_t t0, int len) {
@@ -848,6 +867,11 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
         if constexpr (!PASS_A) {
             t0_prev = t0;
             len_prev = len;
+            // Snapshot after a full chunk that ends a stride.
+            if (tab.ck.S && len == CH && (chunk + 1) % tab.ck.stride_chunks == 0) {
+                const int64_t slot = ck_base + (chunk + 1) / tab.ck.stride_chunks - 1;
+                if (slot < tab.ck.cap) store_state(tab.ck.S + ((size_t)slot * H + h) * D * D);
+            }
         }
     };
     // Unrolled so that every step's image and U set are fixed arrays.
@@ -979,14 +1003,18 @@ static inline int64_t seg_max(int64_t T_total, int N, int H) {
 }
 
 size_t seg_workspace_bytes(int64_t T_total, int N, int H) {
-    const size_t tab = 2 * align_up(4 * (size_t)(N + 1)) + 2 * align_up(8 * (size_t)N);
+    const size_t tab = 2 * align_up(4 * (size_t)(N + 1)) + 2 * align_up(8 * (size_t)N) + align_up(8 * (size_t)(N + 1));
     return tab + (size_t)seg_chunks_max(T_total, N) * H * BLK +
            3 * (size_t)seg_max(T_total, N, H) * H * D * D * sizeof(float);
 }
 
+int launch_ckpt_prep(const int64_t *seq_start, const int64_t *seq_end, int N, int64_t stride, int64_t *off,
+                     hipStream_t stream);
+
 int launch_segment_prefill(const __bf16 *q, const __bf16 *k, const __bf16 *v, const float *z, const float *beta,
                            const float *A, const float *S0, const int32_t *cu, int B, int64_t T, int H, int N,
-                           float *o, float *S_final, void *ws, hipStream_t stream, hipEvent_t *ev) {
+                           float *o, float *S_final, const Ckpt &ck, void *ws, hipStream_t stream,
+                           hipEvent_t *ev) {
     const int64_t T_total = (int64_t)B * T;
     const int L = seg_len(T_total, H);
     const int64_t nsm = seg_max(T_total, N, H);
@@ -1001,6 +1029,9 @@ int launch_segment_prefill(const __bf16 *q, const __bf16 *k, const __bf16 *v, co
     p += align_up(8 * (size_t)N);
     tab.seq_end = (int64_t *)p;
     p += align_up(8 * (size_t)N);
+    int64_t *ckpt_off = (int64_t *)p;
+    p += align_up(8 * (size_t)(N + 1));
+    tab.ck = Ckpt{ck.S, ckpt_off, ck.stride_chunks, ck.cap};
     tab.blocks = p;
     p += (size_t)ncm * H * BLK;
     const size_t st = (size_t)nsm * H * D * D;
@@ -1010,6 +1041,8 @@ int launch_segment_prefill(const __bf16 *q, const __bf16 *k, const __bf16 *v, co
     tab.L = L;
     if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return -1;
     hipLaunchKernelGGL(seg_prep_kernel, dim3(1), dim3(256), 0, stream, cu, N, T_total, cu ? (int64_t)0 : T, tab);
+    if (ck.S && launch_ckpt_prep(tab.seq_start, tab.seq_end, N, (int64_t)ck.stride_chunks * CH, ckpt_off, stream) != 0)
+        return -1;
     if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return -1;
     if (T_total > 0)
         hipLaunchKernelGGL(wy_kernel, dim3((unsigned)(ncm * H)), dim3(256), 0, stream, q, k, v, z, beta, A, N, H,

@@ -136,6 +136,37 @@ int kda_chunk_fwd_timed(const void *q, const void *k, const void *v, kda_dtype q
                         size_t workspace_bytes, void *stream, void *const *stage_events);
 
 /*
+ * kda_chunk_fwd that also keeps state snapshots for a KDA-aware prefix cache
+ * (Kimi K3 paper review, Significance and Limitations paragraphs: the KDA
+ * recurrent state can be checkpointed only at sparse boundaries, up to 6,144
+ * tokens apart, and a unified prefix cache pages these checkpoints beside the
+ * MLA KV blocks).
+ *
+ *   ckpt_stride    tokens between snapshots: a positive multiple of 64 (the
+ *                  chunk size), else KDA_ERR_SHAPE.
+ *   S_ckpt         [ckpt_capacity, H, 128, 128] fp32 (output; must not overlap
+ *                  any other argument, else KDA_ERR_ALIAS; NULL gives
+ *                  KDA_ERR_NULL).  Snapshot m of sequence n (m = 0, 1, ...,
+ *                  floor(len_n / ckpt_stride) - 1) is the state after the
+ *                  sequence's first (m + 1) * ckpt_stride tokens, the state a
+ *                  later call would take as S0 to continue from there.  It is
+ *                  stored at slot off_n + m, where off_n = sum over sequences
+ *                  i < n of floor(len_i / ckpt_stride): sequence after
+ *                  sequence, in order.  A sequence shorter than the stride has
+ *                  none; one whose length is a multiple of the stride has its
+ *                  last snapshot equal to its S_final.
+ *   ckpt_capacity  slots in S_ckpt.  Slots at or past it are not written (the
+ *                  library does not read cu_seqlens on the host, so the caller,
+ *                  who knows the lengths, sizes S_ckpt); 0 writes nothing.
+ *
+ * o, S_final and everything else are exactly as kda_chunk_fwd (the same bits).
+ */
+int kda_chunk_fwd_ckpt(const void *q, const void *k, const void *v, kda_dtype qkv_dtype,
+                       const float *g_raw, const float *beta, const float *A, const float *S0,
+                       const int32_t *cu_seqlens, int32_t B, int64_t T, int32_t H, int32_t n_seqs,
+                       int32_t dk, int32_t dv, float *o, float *S_final, float *S_ckpt, int64_t ckpt_stride,
+                       int64_t ckpt_capacity, void *workspace, size_t workspace_bytes, void *stream);
+/*
  * One recurrent decode step for N independent sequences (Kimi Linear summary,
  * section 6.3: generation uses the recurrent update; each head keeps a fixed
  * 128 x 128 state).  For every (n, h): alpha from z, S' = Diag(alpha) S,

@@ -20,6 +20,8 @@ Functions and what pins them (tests/test_oracle_pins.py):
                       the gradient step of the delta rule, the Gated DeltaNet
                       special case, brute force and the chunk form;
 * ``recurrent_f32``   float32 twin, checked against ``recurrent``;
+* ``states_at``       prefix-cache snapshots: one full-prefix run per snapshot,
+                      the beta = 0 closed form, the slot order;
 * ``chunk``/``chunk_step``  the chunk form, checked against ``recurrent``;
 * ``bruteforce``      dense transition products, checked against ``recurrent``
                       and against the closed forms;
@@ -140,6 +142,32 @@ def recurrent_f32(q, k, v, z, beta, A, S0=None, cu_seqlens=None, threads: int = 
     _load().kdao_recurrent_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(beta), _ptr(A), _ptr(S0f),
                                _ptr(cu), N, H, dk, dv, _ptr(o), _ptr(Sf), int(threads))
     return o, Sf
+
+
+def states_at(q, k, v, z, beta, A, S0=None, cu_seqlens=None, stride: int = 64, threads: int = 0):
+    """State snapshots for a prefix cache (Kimi K3 paper review, Significance and
+    Limitations paragraphs: the KDA state is checkpointed at sparse boundaries).
+
+    Snapshot m of sequence n is the state after the sequence's first (m + 1) * stride
+    tokens, for m < len_n // stride; the snapshots of all sequences follow one another
+    in sequence order.  Returns an array [slots, H, dk, dv] in float64.  Each snapshot
+    is the recurrence run over the next stride tokens from the previous snapshot (the
+    state is all the recurrence carries from one token to the next).
+    """
+    q, k, v, z, beta, A = map(_f32, (q, k, v, z, beta, A))
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    cu = _cu(cu_seqlens, T)
+    N = len(cu) - 1
+    out = []
+    for n in range(N):
+        a, b = int(cu[n]), int(cu[n + 1])
+        S = np.zeros((1, H, dk, dv)) if S0 is None else _f64(S0)[n:n + 1]
+        for m in range((b - a) // stride):
+            t0, t1 = a + m * stride, a + (m + 1) * stride
+            _, S = recurrent(q[t0:t1], k[t0:t1], v[t0:t1], z[t0:t1], beta[t0:t1], A, S0=S, threads=threads)
+            out.append(S[0])
+    return np.array(out, dtype=np.float64).reshape(len(out), H, dk, dv)
 
 
 def decode_step(q, k, v, z, beta, A, S, threads: int = 0):

@@ -103,6 +103,34 @@ def test_prefill_empty_problem_is_ok_without_gpu():
     assert call_prefill(prefill_args(H=0)) == OK
 
 
+def call_prefill_ckpt(a, S_ckpt=fake(12), stride=128, cap=4):
+    lib = kda.load()
+    return lib.kda_chunk_fwd_ckpt(a["q"], a["k"], a["v"], a["dtype"], a["z"], a["beta"], a["A"], a["S0"], a["cu"],
+                                  a["B"], a["T"], a["H"], a["N"], a["dk"], a["dv"], a["o"], a["Sf"], S_ckpt,
+                                  stride, cap, a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("ck,code", [
+    (dict(S_ckpt=None), NULL), (dict(stride=0), SHAPE), (dict(stride=100), SHAPE), (dict(stride=-64), SHAPE),
+    (dict(cap=-1), SHAPE), (dict(S_ckpt=fake(12, 8)), ALIGN),
+    (dict(S_ckpt=fake(8)), ALIAS), (dict(S_ckpt=fake(7, 65536)), ALIAS), (dict(S_ckpt=fake(10, 256)), ALIAS),
+    (dict(S_ckpt=fake(1, 1024)), ALIAS),
+])
+def test_prefill_ckpt_rejects(ck, code):
+    assert call_prefill_ckpt(prefill_args(), **ck) == code
+
+
+def test_prefill_ckpt_checks_the_plain_arguments_too():
+    assert call_prefill_ckpt(prefill_args(dk=64)) == SHAPE
+    assert call_prefill_ckpt(prefill_args(ws=None)) == WORKSPACE
+    assert call_prefill_ckpt(prefill_args(B=0, N=0, T=0)) == OK
+
+
+def test_ckpt_count():
+    assert kda.ckpt_count([0, 63, 64, 6143, 6144, 20000], 6144) == 0 + 0 + 0 + 0 + 1 + 3
+    assert kda.ckpt_count([128, 129, 255, 256], 128) == 1 + 1 + 1 + 2
+
+
 def decode_args(**kw):
     a = dict(q=fake(1), k=fake(2), v=fake(3), dtype=0, z=fake(4), beta=fake(5), A=fake(6), S=fake(7), N=4, H=2,
              dk=128, dv=128, o=fake(8), stream=None)
