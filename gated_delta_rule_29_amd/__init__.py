@@ -35,6 +35,12 @@ class KDAError(RuntimeError):
     pass
 
 
+class LayerOpts(ctypes.Structure):
+    """kda_layer_opts (include/kda.h): the KDA layer's steps fused into the prefill."""
+    _fields_ = [("qk_l2norm", ctypes.c_int32), ("qk_eps", ctypes.c_float), ("out_gate", ctypes.c_void_p),
+                ("norm_weight", ctypes.c_void_p), ("norm_eps", ctypes.c_float)]
+
+
 def lib_path() -> str:
     return _LIB_PATH
 
@@ -60,6 +66,9 @@ def load():
     lib.kda_chunk_fwd_timed.argtypes = lib.kda_chunk_fwd.argtypes + [P]
     lib.kda_chunk_fwd_ckpt.argtypes = lib.kda_chunk_fwd.argtypes[:17] + [P, i64, i64] + lib.kda_chunk_fwd.argtypes[17:]
     lib.kda_chunk_fwd_ckpt.restype = ctypes.c_int
+    lib.kda_chunk_fwd_layer.argtypes = (lib.kda_chunk_fwd.argtypes[:15] + [ctypes.POINTER(LayerOpts), P, P, P, i64, i64]
+                                        + lib.kda_chunk_fwd.argtypes[17:])
+    lib.kda_chunk_fwd_layer.restype = ctypes.c_int
     lib.kda_chunk_fwd_timed.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [P, P, P, ctypes.c_int, P, P, P, P, i32, i32, i32, i32, P, P]
     lib.kda_decode_step.restype = ctypes.c_int
@@ -109,7 +118,8 @@ def ckpt_count(lengths, stride: int) -> int:
 
 def kda_chunk_fwd(q, k, v, g_raw, beta, A, S0=None, cu_seqlens=None, *, o=None, S_final=None,
                   workspace=None, stream=None, return_final_state=True, stage_events=None,
-                  S_ckpt=None, ckpt_stride=0):
+                  S_ckpt=None, ckpt_stride=0, qk_l2norm=False, qk_eps=1e-6, out_gate=None, norm_weight=None,
+                  norm_eps=1e-6):
     """Chunkwise KDA prefill.
 
     q, k, v: [B, T, H, 128] (or [T, H, 128]) bf16 or fp32; g_raw: same shape fp32 (the gate's z);
@@ -120,6 +130,9 @@ def kda_chunk_fwd(q, k, v, g_raw, beta, A, S0=None, cu_seqlens=None, *, o=None, 
     S_ckpt, ckpt_stride: optional state snapshots (kda_chunk_fwd_ckpt): S_ckpt is an fp32 tensor
     [slots, H, 128, 128] (see ckpt_count), filled with the state after every ckpt_stride tokens of each
     sequence, sequence after sequence.
+    qk_l2norm, out_gate, norm_weight (kda_chunk_fwd_layer): the KDA layer's steps fused in -- q and k
+    given raw and normalised to unit length inside; o returned as RMSNorm(o) * norm_weight *
+    sigmoid(out_gate) (out_gate: fp32, shaped like o; norm_weight: fp32 [128]).
     """
     lib = load()
     squeeze = q.dim() == 3
@@ -163,12 +176,29 @@ def kda_chunk_fwd(q, k, v, g_raw, beta, A, S0=None, cu_seqlens=None, *, o=None, 
     args = (_ptr(q), _ptr(k), _ptr(v), dtype, _ptr(g_raw), _ptr(beta), _ptr(A), _ptr(S0),
             _ptr(cu_seqlens), B, T, H, N, dk, dv, _ptr(o), _ptr(S_final), _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream(stream))
+    layer = qk_l2norm or out_gate is not None
     if S_ckpt is not None:
-        if stage_events is not None:
-            raise ValueError("stage_events and S_ckpt cannot be combined")
         _need(S_ckpt, "S_ckpt", (torch.float32,), dev)
         if S_ckpt.dim() != 4 or S_ckpt.shape[1:] != (H, dk, dv):
             raise ValueError(f"S_ckpt must be [slots, {H}, {dk}, {dv}]")
+    if layer:
+        if stage_events is not None:
+            raise ValueError("stage_events and the fused layer steps cannot be combined")
+        if out_gate is not None:
+            _need(out_gate, "out_gate", (torch.float32,), dev)
+            if norm_weight is None:
+                raise ValueError("out_gate needs norm_weight")
+            _need(norm_weight, "norm_weight", (torch.float32,), dev)
+            if out_gate.numel() != B * T * H * dv or norm_weight.shape != (dv,):
+                raise ValueError("out_gate must be shaped like o and norm_weight must be [128]")
+        opts = LayerOpts(int(bool(qk_l2norm)), float(qk_eps), None if out_gate is None else out_gate.data_ptr(),
+                         None if norm_weight is None else norm_weight.data_ptr(), float(norm_eps))
+        ck = (_ptr(S_ckpt), int(ckpt_stride), S_ckpt.shape[0]) if S_ckpt is not None else (None, 0, 0)
+        rc = lib.kda_chunk_fwd_layer(*args[:15], ctypes.byref(opts), args[15], args[16], *ck, *args[17:])
+        _check(rc, "kda_chunk_fwd_layer")
+    elif S_ckpt is not None:
+        if stage_events is not None:
+            raise ValueError("stage_events and S_ckpt cannot be combined")
         rc = lib.kda_chunk_fwd_ckpt(*args[:17], _ptr(S_ckpt), int(ckpt_stride), S_ckpt.shape[0], *args[17:])
         _check(rc, "kda_chunk_fwd_ckpt")
     elif stage_events is None:

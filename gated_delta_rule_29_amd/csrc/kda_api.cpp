@@ -17,7 +17,8 @@ int launch_decode(const void *q, const void *k, const void *v, bool f32io, const
                   const float *A, float *S, int N, int H, float *o, hipStream_t stream);
 int launch_prefill(const void *q, const void *k, const void *v, bool f32io, const float *z, const float *beta,
                    const float *A, const float *S0, const int32_t *cu, int B, int64_t T, int H, int N,
-                   float *o, float *S_final, const Ckpt &ck, void *ws, hipStream_t stream, hipEvent_t *ev);
+                   float *o, float *S_final, const Ckpt &ck, const Layer &ly, void *ws, hipStream_t stream,
+                   hipEvent_t *ev);
 size_t prefill_workspace_bytes(int64_t T_total, int N, int H, bool f32io);
 int set_prefill_attributes();
 }  // namespace kda
@@ -71,7 +72,7 @@ int chunk_fwd(const void *q, const void *k, const void *v, kda_dtype qkv_dtype, 
               const float *beta, const float *A, const float *S0, const int32_t *cu_seqlens, int32_t B, int64_t T,
               int32_t H, int32_t n_seqs, int32_t dk, int32_t dv, float *o, float *S_final, void *workspace,
               size_t workspace_bytes, void *stream, void *const *stage_events, float *S_ckpt, int64_t ckpt_stride,
-              int64_t ckpt_capacity) {
+              int64_t ckpt_capacity, const kda_layer_opts *lo) {
     if (dk != kD || dv != kD) return KDA_ERR_SHAPE;
     if (B < 0 || T < 0 || H < 0 || n_seqs < 0) return KDA_ERR_SHAPE;
     if (qkv_dtype != KDA_BF16 && qkv_dtype != KDA_F32) return KDA_ERR_DTYPE;
@@ -82,6 +83,8 @@ int chunk_fwd(const void *q, const void *k, const void *v, kda_dtype qkv_dtype, 
     }
     if (S_ckpt && (ckpt_stride <= 0 || ckpt_stride % 64 != 0 || ckpt_stride / 64 > INT32_MAX || ckpt_capacity < 0))
         return KDA_ERR_SHAPE;
+    const float *out_gate = lo ? lo->out_gate : nullptr, *norm_weight = lo ? lo->norm_weight : nullptr;
+    if (lo && (!(lo->qk_eps >= 0.f) || !(lo->norm_eps >= 0.f))) return KDA_ERR_SHAPE;  // NaN fails too
     const int64_t T_total = (int64_t)B * T;
     if (T_total > INT32_MAX - 64 || (int64_t)n_seqs * H > INT32_MAX / 64) return KDA_ERR_SHAPE;
     if (S_ckpt && ckpt_capacity > (int64_t)(SIZE_MAX / 2) / ((int64_t)(H > 0 ? H : 1) * kD * kD * 4))
@@ -89,7 +92,8 @@ int chunk_fwd(const void *q, const void *k, const void *v, kda_dtype qkv_dtype, 
     if (n_seqs == 0 || H == 0) return KDA_OK;  // nothing to compute
     if (!A) return KDA_ERR_NULL;
     if (T_total > 0 && (!q || !k || !v || !g_raw || !beta || !o)) return KDA_ERR_NULL;
-    const void *ptrs[] = {q, k, v, g_raw, beta, A, S0, o, S_final, workspace, S_ckpt};
+    if (out_gate && !norm_weight) return KDA_ERR_NULL;
+    const void *ptrs[] = {q, k, v, g_raw, beta, A, S0, o, S_final, workspace, S_ckpt, out_gate, norm_weight};
     for (const void *p : ptrs)
         if (misaligned(p)) return KDA_ERR_ALIGN;
     const size_t need = kda_chunk_fwd_workspace_bytes(T_total, n_seqs, H, qkv_dtype);
@@ -102,7 +106,8 @@ int chunk_fwd(const void *q, const void *k, const void *v, kda_dtype qkv_dtype, 
         overlap(o, o_bytes, v, tok * kD * esz) || overlap(o, o_bytes, g_raw, tok * kD * 4) ||
         overlap(o, o_bytes, beta, tok * 4) || overlap(o, o_bytes, A, (size_t)H * 4) ||
         overlap(o, o_bytes, S0, st_bytes) || overlap(o, o_bytes, S_final, st_bytes) ||
-        overlap(o, o_bytes, workspace, need))
+        overlap(o, o_bytes, workspace, need) || overlap(o, o_bytes, out_gate, o_bytes) ||
+        overlap(o, o_bytes, norm_weight, (size_t)kD * 4))
         return KDA_ERR_ALIAS;
     if (S_ckpt) {
         const size_t ck_bytes = (size_t)ckpt_capacity * H * kD * kD * 4;
@@ -117,8 +122,10 @@ int chunk_fwd(const void *q, const void *k, const void *v, kda_dtype qkv_dtype, 
     if (g_attr_status != 0) return KDA_ERR_HIP;
     const kda::Ckpt ck{S_ckpt && ckpt_capacity > 0 ? S_ckpt : nullptr, nullptr, (int)(S_ckpt ? ckpt_stride / 64 : 1),
                        ckpt_capacity};
+    const kda::Layer ly{lo && lo->qk_l2norm != 0, lo ? lo->qk_eps : 0.f, out_gate, norm_weight,
+                        lo ? lo->norm_eps : 0.f};
     const int rc = kda::launch_prefill(q, k, v, qkv_dtype == KDA_F32, g_raw, beta, A, S0, cu_seqlens, B, T, H,
-                                       n_seqs, o, S_final, ck, workspace, (hipStream_t)stream,
+                                       n_seqs, o, S_final, ck, ly, workspace, (hipStream_t)stream,
                                        (hipEvent_t *)stage_events);
     return rc == 0 ? KDA_OK : KDA_ERR_HIP;
 }
@@ -131,7 +138,7 @@ KDA_EXPORT int kda_chunk_fwd_timed(const void *q, const void *k, const void *v, 
                                    int32_t dk, int32_t dv, float *o, float *S_final, void *workspace,
                                    size_t workspace_bytes, void *stream, void *const *stage_events) {
     return chunk_fwd(q, k, v, qkv_dtype, g_raw, beta, A, S0, cu_seqlens, B, T, H, n_seqs, dk, dv, o, S_final,
-                     workspace, workspace_bytes, stream, stage_events, nullptr, 0, 0);
+                     workspace, workspace_bytes, stream, stage_events, nullptr, 0, 0, nullptr);
 }
 
 KDA_EXPORT int kda_chunk_fwd(const void *q, const void *k, const void *v, kda_dtype qkv_dtype,
@@ -140,7 +147,7 @@ KDA_EXPORT int kda_chunk_fwd(const void *q, const void *k, const void *v, kda_dt
                              int32_t dk, int32_t dv, float *o, float *S_final, void *workspace,
                              size_t workspace_bytes, void *stream) {
     return chunk_fwd(q, k, v, qkv_dtype, g_raw, beta, A, S0, cu_seqlens, B, T, H, n_seqs, dk, dv, o, S_final,
-                     workspace, workspace_bytes, stream, nullptr, nullptr, 0, 0);
+                     workspace, workspace_bytes, stream, nullptr, nullptr, 0, 0, nullptr);
 }
 
 KDA_EXPORT int kda_chunk_fwd_ckpt(const void *q, const void *k, const void *v, kda_dtype qkv_dtype,
@@ -151,7 +158,18 @@ KDA_EXPORT int kda_chunk_fwd_ckpt(const void *q, const void *k, const void *v, k
                                   size_t workspace_bytes, void *stream) {
     if (!S_ckpt) return KDA_ERR_NULL;
     return chunk_fwd(q, k, v, qkv_dtype, g_raw, beta, A, S0, cu_seqlens, B, T, H, n_seqs, dk, dv, o, S_final,
-                     workspace, workspace_bytes, stream, nullptr, S_ckpt, ckpt_stride, ckpt_capacity);
+                     workspace, workspace_bytes, stream, nullptr, S_ckpt, ckpt_stride, ckpt_capacity, nullptr);
+}
+
+KDA_EXPORT int kda_chunk_fwd_layer(const void *q, const void *k, const void *v, kda_dtype qkv_dtype,
+                                   const float *g_raw, const float *beta, const float *A, const float *S0,
+                                   const int32_t *cu_seqlens, int32_t B, int64_t T, int32_t H, int32_t n_seqs,
+                                   int32_t dk, int32_t dv, const kda_layer_opts *opts, float *o, float *S_final,
+                                   float *S_ckpt, int64_t ckpt_stride, int64_t ckpt_capacity, void *workspace,
+                                   size_t workspace_bytes, void *stream) {
+    if (!opts) return KDA_ERR_NULL;
+    return chunk_fwd(q, k, v, qkv_dtype, g_raw, beta, A, S0, cu_seqlens, B, T, H, n_seqs, dk, dv, o, S_final,
+                     workspace, workspace_bytes, stream, nullptr, S_ckpt, ckpt_stride, ckpt_capacity, opts);
 }
 
 KDA_EXPORT int kda_decode_step(const void *q, const void *k, const void *v, kda_dtype qkv_dtype,

@@ -40,6 +40,19 @@ struct Ckpt {
     int64_t cap;
 };
 
+// The KDA layer's steps on either side of the operator (Kimi Linear summary,
+// section 4), fused into the prefill: unit-length queries and keys
+// (x / sqrt(sum x^2 + qk_eps) per token and head), and the output's per-head
+// RMSNorm followed by the sigmoid output gate,
+// o <- o / sqrt(mean o^2 + norm_eps) * weight * sigmoid(gate).
+struct Layer {
+    bool qk_norm;
+    float qk_eps;
+    const float *gate;    // [tokens, H, 128] fp32 pre-activation, or nullptr: no output step
+    const float *weight;  // [128]
+    float norm_eps;
+};
+
 __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }

@@ -60,6 +60,7 @@ struct Table {  // workspace header
     int64_t *ckpt_off;   // [N+1] first snapshot slot of each sequence
     char *blocks;        // chain operands, block (c, h) at (c * H + h) * BLK_BYTES
     Ckpt ck;
+    Layer ly;
 };
 
 __host__ __device__ inline size_t table_bytes(int N) {
@@ -78,6 +79,7 @@ __host__ __device__ inline Table carve(void *ws, int N) {
     p += align256(8 * (size_t)(N + 1));
     t.blocks = p;
     t.ck = Ckpt{nullptr, t.ckpt_off, 1, 0};
+    t.ly = Layer{false, 0.f, nullptr, nullptr, 0.f};
     return t;
 }
 __host__ inline int64_t max_chunks(int64_t T_total, int N) { return (T_total + CH - 1) / CH + N; }
@@ -201,6 +203,7 @@ struct IntraSmem {
     float Vt[D * PT];      // V^T          [channel][token]
     float Akk[CH * PT];    // Akk, then T = (I + Akk)^{-1} in place
     double R[5 * D];       // R_s: cumulative log-decay before sub-chunk s (R_4 = G_n)
+    float nk[CH], nq[CH];  // 1 / |k_t|, 1 / |q_t| (or 1: inputs already unit length)
     float PF[6 * D];       // e^{R_i - R_j} for the six sub-chunk pairs j < i
     float beta[CH];
 };
@@ -254,6 +257,35 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
     const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63, g = l >> 4, lr = l & 15;
     const size_t HD = (size_t)H * D;
     auto tok = [&](int t) -> size_t { return (size_t)(t0 + t) * HD + (size_t)h * D; };
+
+    // ---- phase 0: inverse L2 norms of the key and query rows when the layer's
+    // normalisation is fused in (wave w: rows 16 w .. 16 w + 15, four lanes of 32
+    // channels per row); 1 otherwise.
+    {
+        const int tr = 16 * wv + (l >> 2), cq = 32 * (l & 3);
+        float nk = 1.f, nq = 1.f;
+        if (tab.ly.qk_norm) {
+            float sk = 0.f, sq = 0.f;
+            if (tr < len) {
+                for (int c2 = 0; c2 < 32; ++c2) {
+                    const float a = to_f(k[tok(tr) + cq + c2]), b = to_f(q[tok(tr) + cq + c2]);
+                    sk += a * a;
+                    sq += b * b;
+                }
+            }
+            sk += __shfl_xor(sk, 1);
+            sk += __shfl_xor(sk, 2);
+            sq += __shfl_xor(sq, 1);
+            sq += __shfl_xor(sq, 2);
+            nk = 1.f / __fsqrt_rn(sk + tab.ly.qk_eps);
+            nq = 1.f / __fsqrt_rn(sq + tab.ly.qk_eps);
+        }
+        if ((l & 3) == 0) {
+            sm.nk[tr] = nk;
+            sm.nq[tr] = nq;
+        }
+        __syncthreads();
+    }
 
     // ---- phase 1: gate, sub-chunk cumulative sums, elementwise operands ----
     const int ch = tid & (D - 1), half = tid >> 7;
@@ -309,8 +341,8 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
                 const double Gt = Rs + Gl[si][u];
                 const float gam = __expf((float)Gt);
                 const bool ok = t < len;
-                const float kv = ok ? to_f(k[tok(t) + ch]) : 0.f;
-                const float qv = ok ? to_f(q[tok(t) + ch]) : 0.f;
+                const float kv = ok ? to_f(k[tok(t) + ch]) * sm.nk[t] : 0.f;
+                const float qv = ok ? to_f(q[tok(t) + ch]) * sm.nq[t] : 0.f;
                 const float vv = ok ? to_f(v[tok(t) + ch]) : 0.f;
                 sm.KG[ch * PT + t] = kv * gam;
                 sm.Vt[ch * PT + t] = vv;
@@ -353,12 +385,13 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
             F8 a, b;
             const F8 kc = cr < len ? ld_io8(k + tok(cr) + c0) : F8{};
             const F8 xr = rr < len ? ld_io8(X + tok(rr) + c0) : F8{};
+            const float nc = sm.nk[cr], nr = mat == 0 ? sm.nk[rr] : sm.nq[rr];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 float inv = __frcp_rn(sm.E1[cr * PG + c0 + e]);  // e^{R_j - G_c}
                 if (j < i) inv *= sm.PF[pair_index(i, j) * D + c0 + e];
-                a.v[e] = kc.v[e] * inv;
-                b.v[e] = xr.v[e] * sm.E1[rr * PG + c0 + e];
+                a.v[e] = kc.v[e] * nc * inv;
+                b.v[e] = xr.v[e] * nr * sm.E1[rr * PG + c0 + e];
             }
             if constexpr (F32)
                 acc = mma_ff(acc, a, b);
@@ -666,13 +699,36 @@ __global__ __launch_bounds__(256) void chain_kernel(const float *__restrict__ S0
     }
 }
 
+// ------------------------------------------------------------ output step --
+
+// The layer's output step on fp32 rows of 128 values, in place (one wave per
+// (token, head) row; lane l holds values 2l, 2l+1):
+// o <- o / sqrt(mean o^2 + eps) * weight * sigmoid(gate).
+__global__ __launch_bounds__(256) void gated_rmsnorm_kernel(float *__restrict__ o, const float *__restrict__ gate,
+                                                            const float *__restrict__ weight, float eps,
+                                                            int64_t rows) {
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const int l = threadIdx.x & 63;
+    float2 *orow = (float2 *)(o + row * D);
+    const float2 x = orow[l];
+    const float2 gv = ((const float2 *)(gate + row * D))[l];
+    const float2 wv = ((const float2 *)weight)[l];
+    float s = x.x * x.x + x.y * x.y;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+    const float r = 1.f / __fsqrt_rn(s * (1.f / D) + eps);
+    const float sa = 1.f / (1.f + __expf(-gv.x)), sb = 1.f / (1.f + __expf(-gv.y));
+    orow[l] = make_float2(x.x * r * wv.x * sa, x.y * r * wv.y * sb);
+}
+
 // ------------------------------------------------------------------ host --
 
 size_t seg_workspace_bytes(int64_t T_total, int N, int H);
 int launch_segment_prefill(const __bf16 *q, const __bf16 *k, const __bf16 *v, const float *z, const float *beta,
                            const float *A, const float *S0, const int32_t *cu, int B, int64_t T, int H, int N,
-                           float *o, float *S_final, const Ckpt &ck, void *ws, hipStream_t stream,
-                           hipEvent_t *ev);
+                           float *o, float *S_final, const Ckpt &ck, const Layer &ly, void *ws,
+                           hipStream_t stream, hipEvent_t *ev);
 int set_segment_attributes();
 
 // bf16 q/k/v run the segment-parallel fused path (kda_segment.hip); fp32 q/k/v
@@ -686,13 +742,15 @@ size_t prefill_workspace_bytes(int64_t T_total, int N, int H, bool f32io) {
 // their workspace).
 int launch_prefill(const void *q, const void *k, const void *v, bool f32io, const float *z, const float *beta,
                    const float *A, const float *S0, const int32_t *cu, int B, int64_t T, int H, int N,
-                   float *o, float *S_final, const Ckpt &ck, void *ws, hipStream_t stream, hipEvent_t *ev) {
+                   float *o, float *S_final, const Ckpt &ck, const Layer &ly, void *ws, hipStream_t stream,
+                   hipEvent_t *ev) {
     if (!f32io)
         return launch_segment_prefill((const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, z, beta, A, S0, cu, B,
-                                      T, H, N, o, S_final, ck, ws, stream, ev);
+                                      T, H, N, o, S_final, ck, ly, ws, stream, ev);
     const int64_t T_total = (int64_t)B * T;
     Table tab = carve(ws, N);
     tab.ck = Ckpt{ck.S, tab.ckpt_off, ck.stride_chunks, ck.cap};
+    tab.ly = ly;
     if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return -1;
     hipLaunchKernelGGL(prep_kernel, dim3(1), dim3(256), 0, stream, cu, N, T_total, cu ? (int64_t)0 : T, tab);
     if (ck.S && launch_ckpt_prep(tab.seq_start, tab.seq_end, N, (int64_t)ck.stride_chunks * CH, tab.ckpt_off,
@@ -717,6 +775,9 @@ int launch_prefill(const void *q, const void *k, const void *v, bool f32io, cons
         hipLaunchKernelGGL(chain_kernel<float>, dim3(nwg), dim3(256), 0, stream, S0, N, H, tab, o, S_final);
     else
         hipLaunchKernelGGL(chain_kernel<__bf16>, dim3(nwg), dim3(256), 0, stream, S0, N, H, tab, o, S_final);
+    if (ly.gate && T_total > 0)
+        hipLaunchKernelGGL(gated_rmsnorm_kernel, dim3((unsigned)((T_total * H + 3) / 4)), dim3(256), 0, stream, o,
+                           ly.gate, ly.weight, ly.norm_eps, T_total * H);
     if (hipGetLastError() != hipSuccess) return -1;
     for (int e = 3; e < 6; ++e)
         if (ev && hipEventRecord(ev[e], stream) != hipSuccess) return -1;

@@ -119,6 +119,7 @@ struct SegTable {
     float *Sin;          // [nseg][H][128][128] state entering each segment
     int L;               // chunks per segment
     Ckpt ck;             // state snapshots (ck.S == nullptr: none)
+    Layer ly;            // fused layer steps around the operator
 };
 
 // ------------------------------------------------------------------ prep --
@@ -211,6 +212,7 @@ struct WySmem {
     float F[10 * D];         // e^{R_i - R_{j+1}} for j <= i, row i(i+1)/2 + j
     float eR[4 * D];         // e^{R_s}
     float beta[CH];
+    float nk[CH], nq[CH];    // 1 / |k_t|, 1 / |q_t| (or 1: inputs already unit length)
 };
 static_assert(PTT <= PEH, "T lives in the E1 region");
 
@@ -227,6 +229,9 @@ static_assert(PTT <= PEH, "T lives in the E1 region");
 #ifndef WY_WPE
 #define WY_WPE 3
 #endif
+// QKN: q and k arrive raw and are normalised to unit length here (the layer's
+// step fused in); a separate instantiation, so the plain path carries none of it.
+template <bool QKN>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WY_WPE))) void wy_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     const float *__restrict__ z, const float *__restrict__ beta, const float *__restrict__ A, int N, int H,
@@ -257,6 +262,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WY_WPE))) v
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)(k + base), 0, len * ph, BUF_RSRC3);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)(v + base), 0, len * ph, BUF_RSRC3);
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void *)(q + base), 0, len * ph, BUF_RSRC3);
+    // ---- phase 0 (QKN): the inverse L2 norms of the chunk's key and query rows
+    // (wave w: rows 16 w .. 16 w + 15, four lanes of 32 channels per row).
+    if constexpr (QKN) {
+        const int tr = 16 * w + (l >> 2), cq = 32 * (l & 3);
+        float nk, nq;
+        {
+            float sk = 0.f, sq = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int off = tr * (int)ph + 2 * (cq + 8 * i);  // rows past the end read as 0
+                const bf16x8 kx = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+                const bf16x8 qx = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float a = (float)kx[e], b = (float)qx[e];
+                    sk += a * a;
+                    sq += b * b;
+                }
+            }
+            sk += __shfl_xor(sk, 1);
+            sk += __shfl_xor(sk, 2);
+            sq += __shfl_xor(sq, 1);
+            sq += __shfl_xor(sq, 2);
+            nk = 1.f / __fsqrt_rn(sk + tab.ly.qk_eps);
+            nq = 1.f / __fsqrt_rn(sq + tab.ly.qk_eps);
+        }
+        if ((l & 3) == 0) {
+            sm.nk[tr] = nk;
+            sm.nq[tr] = nq;
+        }
+        __syncthreads();
+    }
     bf16x8 kga[2][2];  // [hf][ks]: channel tile 4 hf + w
     // Gram accumulators of sub-chunk i = w against sub-chunks j <= i; tiles come
     // out transposed: lane (lr, g) holds row r = 16i + lr against columns
@@ -325,7 +362,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WY_WPE))) v
                     const int t = 32 * ks + 16 * (e >> 2) + 4 * g + (e & 3);
                     const float cs = gv[ks][e];
                     const float e1 = __expf(cs);
-                    const float kf = (float)kb[ks][e];
+                    const float kf = QKN ? (float)kb[ks][e] * sm.nk[t] : (float)kb[ks][e];
                     const float cb = kf * __expf(st[s] - cs);  // k e^{R_{s+1} - G_t}
                     sm.a.E1[t * PEH + chl] = e1;
                     sm.CB[t * PEH + chl] = cb;
@@ -355,6 +392,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WY_WPE))) v
         // inside each 32-block is perm32, shared by both operands and by Q~.
         {
             const int i = w, r = 16 * i + lr;
+            const float nkr = QKN ? sm.nk[r] : 1.f, nqr = QKN ? sm.nq[r] : 1.f;
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh) {
                 __builtin_amdgcn_sched_barrier(0);  // one 32-channel block at a time
@@ -369,10 +407,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WY_WPE))) v
                 f16x8 qt;
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    xk.v[m] = (float)k0[m] * ea[m];
-                    xk.v[4 + m] = (float)k1[m] * eb[m];
-                    xq.v[m] = (float)q0[m] * ea[m];
-                    xq.v[4 + m] = (float)q1[m] * eb[m];
+                    xk.v[m] = (QKN ? (float)k0[m] * nkr : (float)k0[m]) * ea[m];
+                    xk.v[4 + m] = (QKN ? (float)k1[m] * nkr : (float)k1[m]) * eb[m];
+                    xq.v[m] = (QKN ? (float)q0[m] * nqr : (float)q0[m]) * ea[m];
+                    xq.v[4 + m] = (QKN ? (float)q1[m] * nqr : (float)q1[m]) * eb[m];
                     qt[m] = (_Float16)(xq.v[m] * pa[m]);
                     qt[4 + m] = (_Float16)(xq.v[4 + m] * pb[m]);
                 }
@@ -657,6 +695,10 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     __shared__ __align__(16) char buf0[Lo::BYTES];
     __shared__ __align__(16) char buf1[Lo::BYTES];
     __shared__ __align__(16) char buf2[NBUF == 3 ? Lo::BYTES : 16];
+    // Fused output step of pass B (see store_o): per-row partial sums of
+    // squares [parity][wave][row], and each wave's gate tile [wave][row][16].
+    __shared__ __align__(16) float opart[PASS_A ? 4 : 2 * CH_NW * CH];
+    __shared__ __align__(16) char ogate[PASS_A ? 16 : CH_NW * CH * 64];
     constexpr int NCT = PASS_A ? 2 : 1;
 
     const int x = blockIdx.x, h = blockIdx.y;
@@ -728,22 +770,81 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     };
     // Output rows of chunk n leave at the start of chain step n + 1 and drain
     // during that whole step.
-    auto store_o = [&](const f32x4 (&O)[4], int64_t t0, int len) {
+    //
+    // With the layer's output step fused in (pass B, gate != nullptr) a row is
+    // scaled by the inverse RMS of its 128 values, by weight and by
+    // sigmoid(gate).  A row's values are spread over the eight waves (16
+    // columns each): at the end of its step a wave leaves its per-row sum of
+    // squares in LDS, and the deferred store adds the eight partials in wave
+    // order (so the result does not depend on timing).  The gate tile of the
+    // wave's columns is copied into LDS during the step before.
+    const bool ep = !PASS_A && tab.ly.gate != nullptr;
+    const float wcol = ep ? tab.ly.weight[colw + lr] : 1.f;
+    auto store_o = [&](const f32x4 (&O)[4], int64_t t0, int len, int par) {
+        f32x4 Y[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) Y[rt] = O[rt];
+        if (ep) {
+            const float *pp = opart + par * CH_NW * CH;
+            const float *gt = (const float *)(ogate + wv * CH * 64);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                f32x4 ss = *(const f32x4 *)&pp[16 * rt + 4 * g];
+#pragma unroll
+                for (int ww = 1; ww < CH_NW; ++ww) {
+                    const f32x4 p4 = *(const f32x4 *)&pp[ww * CH + 16 * rt + 4 * g];
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) ss[m] += p4[m];
+                }
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const float gv = gt[(16 * rt + 4 * g + m) * 16 + lr];
+                    const float sig = __builtin_amdgcn_rcpf(1.f + __expf(-gv));
+                    Y[rt][m] = O[rt][m] * __builtin_amdgcn_rsqf(ss[m] * (1.f / D) + tab.ly.norm_eps) * wcol * sig;
+                }
+            }
+        }
         float *orow = o + ((size_t)t0 * HD + (size_t)h * D + colw + lr);
         if (len == CH) {
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-                for (int m = 0; m < 4; ++m) orow[(size_t)(16 * rt + 4 * g + m) * HD] = O[rt][m];
+                for (int m = 0; m < 4; ++m) orow[(size_t)(16 * rt + 4 * g + m) * HD] = Y[rt][m];
         } else {
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const int t = 16 * rt + 4 * g + m;
-                    if (t < len) orow[(size_t)t * HD] = O[rt][m];
+                    if (t < len) orow[(size_t)t * HD] = Y[rt][m];
                 }
         }
+    };
+    // The gate rows of a chunk, this wave's 16 columns, into its LDS tile: four
+    // copies of 16 rows (lane l: row 16 q + l / 4, columns 4 (l % 4) ..).  Rows
+    // past the sequence end read as 0.
+    auto dma_gate = [&](int chunk) {
+        const int64_t t0c = s0 + (int64_t)chunk * CH;
+        const int lenc = (int)min((int64_t)CH, s1 - t0c);
+        char *dst = ogate + wv * CH * 64;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t rows = max(0, lenc - 16 * q);
+            const int64_t bytes = min(rows * (int64_t)HD * 4, (int64_t)0x7FFFFFFF);
+            const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(tab.ly.gate + ((size_t)(t0c + 16 * q) * HD + (size_t)h * D + colw)), 0, (int)bytes,
+                BUF_RSRC3);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rg, (lds_void *)(dst + 1024 * q), 16,
+                                                     ((l >> 2) * (int)HD + 4 * (l & 3)) * 4, 0, 0, 0);
+        }
+    };
+    // A 16-lane sum (one DPP row: lanes with equal g), the result in every lane.
+    auto row_sum16 = [](float x) {
+        x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+        x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+        x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
+        x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false));
+        return x;
     };
 
     // U of a chunk is loaded one step ahead into one of two register sets; the
@@ -776,7 +877,8 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
         // form the compiler sees, so it adds none of its own for them), then
         // every wave's have, and `nxt` is free.  With three images the newest
         // copy (at most CHAIN_DMA_OPS instructions of this wave) may still run.
-        __builtin_amdgcn_s_waitcnt(0x0F70 | (NBUF == 3 ? CHAIN_DMA_OPS : 0));
+        // (Pass B also waits for its LDS writes: the output-step partials.)
+        __builtin_amdgcn_s_waitcnt(PASS_A ? 0x0F70 | (NBUF == 3 ? CHAIN_DMA_OPS : 0) : 0x0070);
         // The barrier is a bare s_barrier between compiler-only fences: the
         // waits above are the only memory ordering needed (no wave writes LDS
         // but by these copies, and every LDS read of the previous step has
@@ -785,8 +887,10 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __builtin_amdgcn_s_barrier();
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        if constexpr (!PASS_A)
-            if (chunk > cbeg) store_o(O, t0_prev, len_prev);
+        if constexpr (!PASS_A) {
+            if (chunk > cbeg) store_o(O, t0_prev, len_prev, (chunk - 1) & 1);
+            if (ep) dma_gate(chunk);
+        }
         load_u(chunk + 1, un);
         dma(chunk + NBUF - 1, nxt);
 
@@ -867,6 +971,19 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
         if constexpr (!PASS_A) {
             t0_prev = t0;
             len_prev = len;
+            if (ep) {  // this wave's per-row sums of squares of O
+                float *pp = opart + (chunk & 1) * CH_NW * CH + wv * CH;
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) {
+                    f32x4 sq;
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const float x2 = O[rt][m] * O[rt][m];
+                        sq[m] = row_sum16(x2);
+                    }
+                    if (lr == 0) *(f32x4 *)&pp[16 * rt + 4 * g] = sq;
+                }
+            }
             // Snapshot after a full chunk that ends a stride.
             if (tab.ck.S && len == CH && (chunk + 1) % tab.ck.stride_chunks == 0) {
                 const int64_t slot = ck_base + (chunk + 1) / tab.ck.stride_chunks - 1;
@@ -899,8 +1016,10 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     // The copies issued past the last chunk still write LDS: let them land
     // before the workgroup can end and its LDS be handed on.
     __builtin_amdgcn_s_waitcnt(0x0F70);
-    if constexpr (!PASS_A)
-        if (cbeg < cend) store_o(O, t0_prev, len_prev);
+    if constexpr (!PASS_A) {
+        if (ep) __syncthreads();  // every wave's partials of the last chunk
+        if (cbeg < cend) store_o(O, t0_prev, len_prev, (cend - 1) & 1);
+    }
 
     // ---- segment end
     if constexpr (PASS_A) {
@@ -1013,8 +1132,8 @@ int launch_ckpt_prep(const int64_t *seq_start, const int64_t *seq_end, int N, in
 
 int launch_segment_prefill(const __bf16 *q, const __bf16 *k, const __bf16 *v, const float *z, const float *beta,
                            const float *A, const float *S0, const int32_t *cu, int B, int64_t T, int H, int N,
-                           float *o, float *S_final, const Ckpt &ck, void *ws, hipStream_t stream,
-                           hipEvent_t *ev) {
+                           float *o, float *S_final, const Ckpt &ck, const Layer &ly, void *ws,
+                           hipStream_t stream, hipEvent_t *ev) {
     const int64_t T_total = (int64_t)B * T;
     const int L = seg_len(T_total, H);
     const int64_t nsm = seg_max(T_total, N, H);
@@ -1032,6 +1151,7 @@ int launch_segment_prefill(const __bf16 *q, const __bf16 *k, const __bf16 *v, co
     int64_t *ckpt_off = (int64_t *)p;
     p += align_up(8 * (size_t)(N + 1));
     tab.ck = Ckpt{ck.S, ckpt_off, ck.stride_chunks, ck.cap};
+    tab.ly = ly;
     tab.blocks = p;
     p += (size_t)ncm * H * BLK;
     const size_t st = (size_t)nsm * H * D * D;
@@ -1044,9 +1164,14 @@ int launch_segment_prefill(const __bf16 *q, const __bf16 *k, const __bf16 *v, co
     if (ck.S && launch_ckpt_prep(tab.seq_start, tab.seq_end, N, (int64_t)ck.stride_chunks * CH, ckpt_off, stream) != 0)
         return -1;
     if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return -1;
-    if (T_total > 0)
-        hipLaunchKernelGGL(wy_kernel, dim3((unsigned)(ncm * H)), dim3(256), 0, stream, q, k, v, z, beta, A, N, H,
-                           tab);
+    if (T_total > 0) {
+        if (ly.qk_norm)
+            hipLaunchKernelGGL(wy_kernel<true>, dim3((unsigned)(ncm * H)), dim3(256), 0, stream, q, k, v, z, beta, A,
+                               N, H, tab);
+        else
+            hipLaunchKernelGGL(wy_kernel<false>, dim3((unsigned)(ncm * H)), dim3(256), 0, stream, q, k, v, z, beta,
+                               A, N, H, tab);
+    }
     if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return -1;
     hipLaunchKernelGGL(seg_chain_kernel<true>, dim3((unsigned)nsm, (unsigned)H), dim3(CH_NT), 0, stream, N, H, tab,
                        o, S_final);

@@ -167,6 +167,43 @@ int kda_chunk_fwd_ckpt(const void *q, const void *k, const void *v, kda_dtype qk
                        int32_t dk, int32_t dv, float *o, float *S_final, float *S_ckpt, int64_t ckpt_stride,
                        int64_t ckpt_capacity, void *workspace, size_t workspace_bytes, void *stream);
 /*
+ * The KDA layer's steps on either side of the operator, fused into the prefill
+ * (Kimi Linear summary, section 4: queries and keys are normalised to unit
+ * length; the output gets a per-head RMSNorm and then a data-dependent sigmoid
+ * output gate).  Values are device pointers owned by the caller.
+ *
+ *   qk_l2norm    nonzero: q and k are raw; each (token, head) row x of 128
+ *                values is used as x / sqrt(sum_j x_j^2 + qk_eps).
+ *   out_gate     [tokens, H, 128] fp32, the output gate's pre-activation (the
+ *                caller's low-rank projection), or NULL for no output step.
+ *                With it, each output row becomes
+ *                o / sqrt(mean_j o_j^2 + norm_eps) * norm_weight * sigmoid(out_gate).
+ *   norm_weight  [128] fp32, the RMSNorm weight shared by all heads (required
+ *                with out_gate).
+ *   qk_eps, norm_eps  >= 0 (else KDA_ERR_SHAPE); 1e-6 is a usual choice.
+ */
+typedef struct kda_layer_opts {
+    int32_t qk_l2norm;
+    float qk_eps;
+    const float *out_gate;
+    const float *norm_weight;
+    float norm_eps;
+} kda_layer_opts;
+/*
+ * kda_chunk_fwd with the layer's steps fused in (opts, NULL gives KDA_ERR_NULL)
+ * and optional state snapshots (S_ckpt may be NULL; otherwise as
+ * kda_chunk_fwd_ckpt).  o holds the gated, normalised output when
+ * opts->out_gate is set; S_final and the snapshots are the operator's states
+ * either way.  out_gate and norm_weight must not overlap o (KDA_ERR_ALIAS) and
+ * must be 16-byte aligned.
+ */
+int kda_chunk_fwd_layer(const void *q, const void *k, const void *v, kda_dtype qkv_dtype,
+                        const float *g_raw, const float *beta, const float *A, const float *S0,
+                        const int32_t *cu_seqlens, int32_t B, int64_t T, int32_t H, int32_t n_seqs,
+                        int32_t dk, int32_t dv, const kda_layer_opts *opts, float *o, float *S_final,
+                        float *S_ckpt, int64_t ckpt_stride, int64_t ckpt_capacity, void *workspace,
+                        size_t workspace_bytes, void *stream);
+/*
  * One recurrent decode step for N independent sequences (Kimi Linear summary,
  * section 6.3: generation uses the recurrent update; each head keeps a fixed
  * 128 x 128 state).  For every (n, h): alpha from z, S' = Diag(alpha) S,

@@ -22,6 +22,9 @@ Functions and what pins them (tests/test_oracle_pins.py):
 * ``recurrent_f32``   float32 twin, checked against ``recurrent``;
 * ``states_at``       prefix-cache snapshots: one full-prefix run per snapshot,
                       the beta = 0 closed form, the slot order;
+* ``l2_normalize``, ``gated_rmsnorm``  the KDA layer's steps around the operator:
+                      Pythagorean triples, constant vectors, the logistic
+                      function's closed values and limits;
 * ``chunk``/``chunk_step``  the chunk form, checked against ``recurrent``;
 * ``bruteforce``      dense transition products, checked against ``recurrent``
                       and against the closed forms;
@@ -246,3 +249,20 @@ def gdn(q, k, v, alpha, beta, S0=None):
     _load().kdao_gdn(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S0d), T, dk, dv,
                      _ptr(o), _ptr(Sf))
     return o, Sf
+
+
+def l2_normalize(x, eps: float = 1e-6):
+    """The unit-length step the KDA layer applies to queries and keys before the operator
+    (Kimi Linear summary, section 4): x / sqrt(sum_j x_j^2 + eps) over the last axis, in float64."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)
+
+
+def gated_rmsnorm(o, gate, weight, eps: float = 1e-6):
+    """The output steps of the KDA layer (Kimi Linear summary, section 4): a per-head RMSNorm
+    over the value channels, then a data-dependent sigmoid gate.  o, gate: [..., dv];
+    weight: [dv].  Returns o / sqrt(mean_j o_j^2 + eps) * weight * sigmoid(gate), in float64."""
+    o = np.asarray(o, dtype=np.float64)
+    g = np.asarray(gate, dtype=np.float64)
+    r = 1.0 / np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps)
+    return o * r * np.asarray(weight, dtype=np.float64) * (1.0 / (1.0 + np.exp(-g)))

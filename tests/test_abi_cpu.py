@@ -126,6 +126,30 @@ def test_prefill_ckpt_checks_the_plain_arguments_too():
     assert call_prefill_ckpt(prefill_args(B=0, N=0, T=0)) == OK
 
 
+Opts = kda.LayerOpts
+
+
+def call_prefill_layer(a, opts, S_ckpt=None, stride=0, cap=0):
+    lib = kda.load()
+    return lib.kda_chunk_fwd_layer(a["q"], a["k"], a["v"], a["dtype"], a["z"], a["beta"], a["A"], a["S0"],
+                                   a["cu"], a["B"], a["T"], a["H"], a["N"], a["dk"], a["dv"],
+                                   None if opts is None else ctypes.byref(opts), a["o"], a["Sf"], S_ckpt, stride,
+                                   cap, a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_prefill_layer_rejects():
+    gate, w = fake(13).value, fake(14).value
+    assert call_prefill_layer(prefill_args(), None) == NULL
+    assert call_prefill_layer(prefill_args(), Opts(1, 1e-6, gate, None, 1e-6)) == NULL
+    assert call_prefill_layer(prefill_args(), Opts(1, -1.0, None, None, 0.0)) == SHAPE
+    assert call_prefill_layer(prefill_args(), Opts(0, 0.0, gate, w, float("nan"))) == SHAPE
+    assert call_prefill_layer(prefill_args(), Opts(0, 0.0, gate + 4, w, 0.0)) == ALIGN
+    assert call_prefill_layer(prefill_args(o=fake(13, 256)), Opts(0, 0.0, gate, w, 0.0)) == ALIAS
+    assert call_prefill_layer(prefill_args(), Opts(0, 0.0, gate, w, 0.0), S_ckpt=fake(12), stride=100,
+                              cap=1) == SHAPE
+    assert call_prefill_layer(prefill_args(B=0, N=0, T=0), Opts(1, 1e-6, gate, w, 1e-6)) == OK
+
+
 def test_ckpt_count():
     assert kda.ckpt_count([0, 63, 64, 6143, 6144, 20000], 6144) == 0 + 0 + 0 + 0 + 1 + 3
     assert kda.ckpt_count([128, 129, 255, 256], 128) == 1 + 1 + 1 + 2
