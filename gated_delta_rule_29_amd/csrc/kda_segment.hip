@@ -262,38 +262,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WY_WPE))) v
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)(k + base), 0, len * ph, BUF_RSRC3);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)(v + base), 0, len * ph, BUF_RSRC3);
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void *)(q + base), 0, len * ph, BUF_RSRC3);
-    // ---- phase 0 (QKN): the inverse L2 norms of the chunk's key and query rows
-    // (wave w: rows 16 w .. 16 w + 15, four lanes of 32 channels per row).
-    if constexpr (QKN) {
-        const int tr = 16 * w + (l >> 2), cq = 32 * (l & 3);
-        float nk, nq;
-        {
-            float sk = 0.f, sq = 0.f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int off = tr * (int)ph + 2 * (cq + 8 * i);  // rows past the end read as 0
-                const bf16x8 kx = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
-                const bf16x8 qx = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float a = (float)kx[e], b = (float)qx[e];
-                    sk += a * a;
-                    sq += b * b;
-                }
-            }
-            sk += __shfl_xor(sk, 1);
-            sk += __shfl_xor(sk, 2);
-            sq += __shfl_xor(sq, 1);
-            sq += __shfl_xor(sq, 2);
-            nk = 1.f / __fsqrt_rn(sk + tab.ly.qk_eps);
-            nq = 1.f / __fsqrt_rn(sq + tab.ly.qk_eps);
-        }
-        if ((l & 3) == 0) {
-            sm.nk[tr] = nk;
-            sm.nq[tr] = nq;
-        }
-        __syncthreads();
-    }
     bf16x8 kga[2][2];  // [hf][ks]: channel tile 4 hf + w
     // Gram accumulators of sub-chunk i = w against sub-chunks j <= i; tiles come
     // out transposed: lane (lr, g) holds row r = 16i + lr against columns
@@ -322,6 +290,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WY_WPE))) v
                     gv[ks][e] = kda_gate(eA, ok ? zv : -__builtin_inff());  // z = -inf gives g = 0
                     kb[ks][e] = __builtin_bit_cast(__bf16, kv);
                 }
+            // ---- phase 0 (QKN, first half only): the inverse L2 norms of the
+            // chunk's key and query rows (wave w: rows 16 w .. 16 w + 15, four
+            // lanes of 32 channels per row), issued after this phase's own loads
+            // and exchanged through LDS behind a bare barrier, so those loads
+            // stay in flight meanwhile.
+            if constexpr (QKN) {
+                if (hf == 0) {
+                    const int tr = 16 * w + (l >> 2), cq = 32 * (l & 3);
+                    float sk = 0.f, sq = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int off = tr * (int)ph + 2 * (cq + 8 * i);  // rows past the end read as 0
+                        const bf16x8 kx =
+                            __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+                        const bf16x8 qx =
+                            __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const float a = (float)kx[e], b = (float)qx[e];
+                            sk += a * a;
+                            sq += b * b;
+                        }
+                    }
+                    sk += __shfl_xor(sk, 1);
+                    sk += __shfl_xor(sk, 2);
+                    sq += __shfl_xor(sq, 1);
+                    sq += __shfl_xor(sq, 2);
+                    if ((l & 3) == 0) {
+                        sm.nk[tr] = 1.f / __fsqrt_rn(sk + tab.ly.qk_eps);
+                        sm.nq[tr] = 1.f / __fsqrt_rn(sq + tab.ly.qk_eps);
+                    }
+                    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
+                    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                    __builtin_amdgcn_s_barrier();
+                    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                }
+            }
+
             float st[4];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
