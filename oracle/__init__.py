@@ -22,6 +22,9 @@ Functions and what pins them (tests/test_oracle_pins.py):
 * ``recurrent_f32``   float32 twin, checked against ``recurrent``;
 * ``states_at``       prefix-cache snapshots: one full-prefix run per snapshot,
                       the beta = 0 closed form, the slot order;
+* ``recurrent_g``     the recurrence with given log-decays: equals ``recurrent``
+                      with the K3 gate, the beta = 0 closed form;
+* ``softplus_gate``   the unbounded decay: softplus closed values and limits;
 * ``l2_normalize``, ``gated_rmsnorm``  the KDA layer's steps around the operator:
                       Pythagorean triples, constant vectors, the logistic
                       function's closed values and limits;
@@ -72,6 +75,8 @@ def _load():
         lib.kdao_gate.restype = None
         lib.kdao_recurrent.argtypes = [P] * 8 + [i32] * 4 + [P, P, i32]
         lib.kdao_recurrent.restype = i32
+        lib.kdao_recurrent_g.argtypes = [P] * 7 + [i32] * 4 + [P, P, i32]
+        lib.kdao_recurrent_g.restype = i32
         lib.kdao_recurrent_f32.argtypes = [P] * 8 + [i32] * 4 + [P, P, i32]
         lib.kdao_recurrent_f32.restype = i32
         lib.kdao_chunk.argtypes = [P] * 8 + [i32] * 7 + [P, P, i32]
@@ -130,6 +135,33 @@ def recurrent(q, k, v, z, beta, A, S0=None, cu_seqlens=None, threads: int = 0, r
     n = _load().kdao_recurrent(_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(beta), _ptr(A), _ptr(S0d),
                                _ptr(cu), N, H, dk, dv, _ptr(o), _ptr(Sf), int(threads))
     return (o, Sf, n) if return_threads else (o, Sf)
+
+
+def recurrent_g(q, k, v, g, beta, S0=None, cu_seqlens=None, threads: int = 0):
+    """The recurrence with the log-decays given directly: g [T, H, dk] float64, alpha = e^g
+    (for decay parameterisations other than the K3 gate).  Same outputs as ``recurrent``."""
+    q, k, v, beta = map(_f32, (q, k, v, beta))
+    g = _f64(g)
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    cu = _cu(cu_seqlens, T)
+    N = len(cu) - 1
+    S0d = None if S0 is None else _f64(S0)
+    o = np.zeros((T, H, dv), dtype=np.float64)
+    Sf = np.zeros((N, H, dk, dv), dtype=np.float64)
+    _load().kdao_recurrent_g(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0d), _ptr(cu), N, H, dk, dv,
+                             _ptr(o), _ptr(Sf), int(threads))
+    return o, Sf
+
+
+def softplus_gate(z, A):
+    """Kimi Linear's unbounded negative-softplus decay, the parameterisation K3 replaces (Kimi K3
+    paper review, Method paragraph; the Kimi K3 architecture page, sequence-bottleneck section).
+    Reading: g = -e^{A_h} * softplus(z), per (token, head, key channel), in float64; z: [T, H, dk],
+    A: [H].  softplus is evaluated as max(z, 0) + log1p(e^{-|z|})."""
+    z = np.asarray(z, dtype=np.float64)
+    sp = np.maximum(z, 0.0) + np.log1p(np.exp(-np.abs(z)))
+    return -np.exp(np.asarray(A, dtype=np.float64))[None, :, None] * sp
 
 
 def recurrent_f32(q, k, v, z, beta, A, S0=None, cu_seqlens=None, threads: int = 0):

@@ -131,6 +131,7 @@ typedef struct {
     const int64_t *cu;
     int N, H, dk, dv;
     double *o, *S_final;
+    const double *g; /* non-NULL: log-decays given directly ([T, H, dk]), z and A unused */
 } rec_args;
 
 /* [KL 3] one (sequence, head): for every token, in order,
@@ -154,17 +155,22 @@ static void rec_task_f64(void *vctx, int64_t task)
         memcpy(S, a->S0 + sidx, sizeof(double) * (size_t)dk * dv);
     else
         memset(S, 0, sizeof(double) * (size_t)dk * dv);
-    const double expA = exp((double)a->A[h]);
+    const double expA = a->A ? exp((double)a->A[h]) : 0.0;
 
     for (int64_t t = a->cu[n]; t < a->cu[n + 1]; ++t) {
         const float *qt = a->q + ((size_t)t * H + h) * dk;
         const float *kt = a->k + ((size_t)t * H + h) * dk;
-        const float *zt = a->z + ((size_t)t * H + h) * dk;
+        const float *zt = a->z ? a->z + ((size_t)t * H + h) * dk : NULL;
         const float *vt = a->v + ((size_t)t * H + h) * dv;
         const double bt = (double)a->beta[(size_t)t * H + h];
         double *ot = a->o + ((size_t)t * H + h) * dv;
 
-        for (int i = 0; i < dk; ++i) alpha[i] = exp(gate_one(expA, (double)zt[i]));
+        if (a->g) {
+            const double *gt = a->g + ((size_t)t * H + h) * dk;
+            for (int i = 0; i < dk; ++i) alpha[i] = exp(gt[i]);
+        } else {
+            for (int i = 0; i < dk; ++i) alpha[i] = exp(gate_one(expA, (double)zt[i]));
+        }
         for (int i = 0; i < dk; ++i)
             for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] *= alpha[i];
         for (int j = 0; j < dv; ++j) p[j] = 0.0;
@@ -190,7 +196,17 @@ int kdao_recurrent(const float *q, const float *k, const float *v, const float *
                    const float *beta, const float *A, const double *S0, const int64_t *cu,
                    int N, int H, int dk, int dv, double *o, double *S_final, int nthreads)
 {
-    rec_args a = {q, k, v, z, beta, A, S0, cu, N, H, dk, dv, o, S_final};
+    rec_args a = {q, k, v, z, beta, A, S0, cu, N, H, dk, dv, o, S_final, NULL};
+    return run_pool((int64_t)N * H, nthreads, &a, rec_task_f64);
+}
+
+/* The same recurrence with the log-decays g given directly (any decay
+ * parameterisation: alpha = e^g).  Returns the number of threads used. */
+int kdao_recurrent_g(const float *q, const float *k, const float *v, const double *g, const float *beta,
+                     const double *S0, const int64_t *cu, int N, int H, int dk, int dv, double *o,
+                     double *S_final, int nthreads)
+{
+    rec_args a = {q, k, v, NULL, beta, NULL, S0, cu, N, H, dk, dv, o, S_final, g};
     return run_pool((int64_t)N * H, nthreads, &a, rec_task_f64);
 }
 
