@@ -22,7 +22,7 @@ import os
 import torch
 
 __all__ = ["kda_chunk_fwd", "kda_decode_step", "kda_chunk_fwd_workspace_bytes", "KDAError", "lib_path",
-           "HEAD_DIM", "status_str", "load"]
+           "HEAD_DIM", "status_str", "load", "LayerOpts", "GATES"]
 
 HEAD_DIM = 128
 KDA_BF16, KDA_F32 = 0, 1
@@ -36,9 +36,14 @@ class KDAError(RuntimeError):
 
 
 class LayerOpts(ctypes.Structure):
-    """kda_layer_opts (include/kda.h): the KDA layer's steps fused into the prefill."""
+    """kda_layer_opts (include/kda.h): the KDA layer's steps fused into the prefill and decode, and
+    the decay parameterisation."""
     _fields_ = [("qk_l2norm", ctypes.c_int32), ("qk_eps", ctypes.c_float), ("out_gate", ctypes.c_void_p),
-                ("norm_weight", ctypes.c_void_p), ("norm_eps", ctypes.c_float)]
+                ("norm_weight", ctypes.c_void_p), ("norm_eps", ctypes.c_float), ("gate_kind", ctypes.c_int32),
+                ("gate_per_head", ctypes.c_int32)]
+
+
+GATES = {"k3": 0, "softplus": 1}  # kda_layer_opts::gate_kind
 
 
 def lib_path() -> str:
@@ -72,6 +77,9 @@ def load():
     lib.kda_chunk_fwd_timed.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [P, P, P, ctypes.c_int, P, P, P, P, i32, i32, i32, i32, P, P]
     lib.kda_decode_step.restype = ctypes.c_int
+    lib.kda_decode_step_layer.argtypes = (lib.kda_decode_step.argtypes[:12] + [ctypes.POINTER(LayerOpts)]
+                                          + lib.kda_decode_step.argtypes[12:])
+    lib.kda_decode_step_layer.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -119,7 +127,7 @@ def ckpt_count(lengths, stride: int) -> int:
 def kda_chunk_fwd(q, k, v, g_raw, beta, A, S0=None, cu_seqlens=None, *, o=None, S_final=None,
                   workspace=None, stream=None, return_final_state=True, stage_events=None,
                   S_ckpt=None, ckpt_stride=0, qk_l2norm=False, qk_eps=1e-6, out_gate=None, norm_weight=None,
-                  norm_eps=1e-6):
+                  norm_eps=1e-6, gate="k3"):
     """Chunkwise KDA prefill.
 
     q, k, v: [B, T, H, 128] (or [T, H, 128]) bf16 or fp32; g_raw: same shape fp32 (the gate's z);
@@ -133,6 +141,8 @@ def kda_chunk_fwd(q, k, v, g_raw, beta, A, S0=None, cu_seqlens=None, *, o=None, 
     qk_l2norm, out_gate, norm_weight (kda_chunk_fwd_layer): the KDA layer's steps fused in -- q and k
     given raw and normalised to unit length inside; o returned as RMSNorm(o) * norm_weight *
     sigmoid(out_gate) (out_gate: fp32, shaped like o; norm_weight: fp32 [128]).
+    gate: "k3" (g = -5 Sigmoid(e^A z)) or "softplus" (g = -e^A softplus(z), unbounded); g_raw shaped
+    [B, T, H] (or [T, H]) gives one gate value per (token, head) for all 128 channels.
     """
     lib = load()
     squeeze = q.dim() == 3
@@ -150,8 +160,12 @@ def kda_chunk_fwd(q, k, v, g_raw, beta, A, S0=None, cu_seqlens=None, *, o=None, 
     _need(g_raw, "g_raw", (torch.float32,), dev)
     _need(beta, "beta", (torch.float32,), dev)
     _need(A, "A", (torch.float32,), dev)
-    if k.shape != q.shape or g_raw.shape != q.shape or v.shape[:3] != q.shape[:3] or beta.shape != (B, T, H):
+    per_head = g_raw.shape == q.shape[:3]
+    if k.shape != q.shape or (g_raw.shape != q.shape and not per_head) or v.shape[:3] != q.shape[:3] \
+            or beta.shape != (B, T, H):
         raise ValueError("inconsistent shapes")
+    if gate not in GATES:
+        raise ValueError(f"gate must be one of {sorted(GATES)}")
     if A.shape != (H,):
         raise ValueError("A must be [H]")
     if cu_seqlens is not None:
@@ -176,7 +190,7 @@ def kda_chunk_fwd(q, k, v, g_raw, beta, A, S0=None, cu_seqlens=None, *, o=None, 
     args = (_ptr(q), _ptr(k), _ptr(v), dtype, _ptr(g_raw), _ptr(beta), _ptr(A), _ptr(S0),
             _ptr(cu_seqlens), B, T, H, N, dk, dv, _ptr(o), _ptr(S_final), _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream(stream))
-    layer = qk_l2norm or out_gate is not None
+    layer = qk_l2norm or out_gate is not None or gate != "k3" or per_head
     if S_ckpt is not None:
         _need(S_ckpt, "S_ckpt", (torch.float32,), dev)
         if S_ckpt.dim() != 4 or S_ckpt.shape[1:] != (H, dk, dv):
@@ -192,7 +206,8 @@ def kda_chunk_fwd(q, k, v, g_raw, beta, A, S0=None, cu_seqlens=None, *, o=None, 
             if out_gate.numel() != B * T * H * dv or norm_weight.shape != (dv,):
                 raise ValueError("out_gate must be shaped like o and norm_weight must be [128]")
         opts = LayerOpts(int(bool(qk_l2norm)), float(qk_eps), None if out_gate is None else out_gate.data_ptr(),
-                         None if norm_weight is None else norm_weight.data_ptr(), float(norm_eps))
+                         None if norm_weight is None else norm_weight.data_ptr(), float(norm_eps), GATES[gate],
+                         int(per_head))
         ck = (_ptr(S_ckpt), int(ckpt_stride), S_ckpt.shape[0]) if S_ckpt is not None else (None, 0, 0)
         rc = lib.kda_chunk_fwd_layer(*args[:15], ctypes.byref(opts), args[15], args[16], *ck, *args[17:])
         _check(rc, "kda_chunk_fwd_layer")
@@ -212,9 +227,12 @@ def kda_chunk_fwd(q, k, v, g_raw, beta, A, S0=None, cu_seqlens=None, *, o=None, 
     return o, S_final
 
 
-def kda_decode_step(q, k, v, g_raw, beta, A, S, *, o=None, stream=None):
-    """One recurrent step for N sequences: q, k, v, g_raw [N, H, 128]; beta [N, H]; A [H];
-    S [N, H, 128, 128] fp32 updated in place.  Returns o [N, H, 128] fp32."""
+def kda_decode_step(q, k, v, g_raw, beta, A, S, *, o=None, stream=None, qk_l2norm=False, qk_eps=1e-6,
+                    out_gate=None, norm_weight=None, norm_eps=1e-6, gate="k3"):
+    """One recurrent step for N sequences: q, k, v [N, H, 128]; g_raw [N, H, 128] (or [N, H]: one
+    value per head); beta [N, H]; A [H]; S [N, H, 128, 128] fp32 updated in place.  Returns o
+    [N, H, 128] fp32.  qk_l2norm, out_gate, norm_weight, norm_eps, gate: as kda_chunk_fwd
+    (kda_decode_step_layer)."""
     lib = load()
     N, H, dk = q.shape
     dv = v.shape[-1]
@@ -226,12 +244,30 @@ def kda_decode_step(q, k, v, g_raw, beta, A, S, *, o=None, stream=None):
     _need(beta, "beta", (torch.float32,), dev)
     _need(A, "A", (torch.float32,), dev)
     _need(S, "S", (torch.float32,), dev)
-    if k.shape != q.shape or g_raw.shape != q.shape or beta.shape != (N, H) or S.shape != (N, H, dk, dv):
+    per_head = g_raw.shape == (N, H)
+    if k.shape != q.shape or (g_raw.shape != q.shape and not per_head) or beta.shape != (N, H) \
+            or S.shape != (N, H, dk, dv):
         raise ValueError("inconsistent shapes")
+    if gate not in GATES:
+        raise ValueError(f"gate must be one of {sorted(GATES)}")
     if o is None:
         o = torch.empty((N, H, dv), dtype=torch.float32, device=dev)
     dtype = KDA_BF16 if q.dtype == torch.bfloat16 else KDA_F32
-    rc = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), dtype, _ptr(g_raw), _ptr(beta), _ptr(A), _ptr(S), N, H,
-                             dk, dv, _ptr(o), _stream(stream))
-    _check(rc, "kda_decode_step")
+    args = (_ptr(q), _ptr(k), _ptr(v), dtype, _ptr(g_raw), _ptr(beta), _ptr(A), _ptr(S), N, H, dk, dv)
+    if qk_l2norm or out_gate is not None or gate != "k3" or per_head:
+        if out_gate is not None:
+            _need(out_gate, "out_gate", (torch.float32,), dev)
+            if norm_weight is None:
+                raise ValueError("out_gate needs norm_weight")
+            _need(norm_weight, "norm_weight", (torch.float32,), dev)
+            if out_gate.numel() != N * H * dv or norm_weight.shape != (dv,):
+                raise ValueError("out_gate must be shaped like o and norm_weight must be [128]")
+        opts = LayerOpts(int(bool(qk_l2norm)), float(qk_eps), None if out_gate is None else out_gate.data_ptr(),
+                         None if norm_weight is None else norm_weight.data_ptr(), float(norm_eps), GATES[gate],
+                         int(per_head))
+        rc = lib.kda_decode_step_layer(*args, ctypes.byref(opts), _ptr(o), _stream(stream))
+        _check(rc, "kda_decode_step_layer")
+    else:
+        rc = lib.kda_decode_step(*args, _ptr(o), _stream(stream))
+        _check(rc, "kda_decode_step")
     return o

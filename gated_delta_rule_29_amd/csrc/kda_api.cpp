@@ -14,7 +14,7 @@
 
 namespace kda {
 int launch_decode(const void *q, const void *k, const void *v, bool f32io, const float *z, const float *beta,
-                  const float *A, float *S, int N, int H, float *o, hipStream_t stream);
+                  const float *A, float *S, int N, int H, float *o, const Layer &ly, hipStream_t stream);
 int launch_prefill(const void *q, const void *k, const void *v, bool f32io, const float *z, const float *beta,
                    const float *A, const float *S0, const int32_t *cu, int B, int64_t T, int H, int N,
                    float *o, float *S_final, const Ckpt &ck, const Layer &ly, void *ws, hipStream_t stream,
@@ -85,6 +85,8 @@ int chunk_fwd(const void *q, const void *k, const void *v, kda_dtype qkv_dtype, 
         return KDA_ERR_SHAPE;
     const float *out_gate = lo ? lo->out_gate : nullptr, *norm_weight = lo ? lo->norm_weight : nullptr;
     if (lo && (!(lo->qk_eps >= 0.f) || !(lo->norm_eps >= 0.f))) return KDA_ERR_SHAPE;  // NaN fails too
+    if (lo && lo->gate_kind != KDA_GATE_K3 && lo->gate_kind != KDA_GATE_SOFTPLUS) return KDA_ERR_SHAPE;
+    const size_t z_row = lo && lo->gate_per_head ? 1 : kD;  // g_raw values per (token, head)
     const int64_t T_total = (int64_t)B * T;
     if (T_total > INT32_MAX - 64 || (int64_t)n_seqs * H > INT32_MAX / 64) return KDA_ERR_SHAPE;
     if (S_ckpt && ckpt_capacity > (int64_t)(SIZE_MAX / 2) / ((int64_t)(H > 0 ? H : 1) * kD * kD * 4))
@@ -103,7 +105,7 @@ int chunk_fwd(const void *q, const void *k, const void *v, kda_dtype qkv_dtype, 
     const size_t o_bytes = tok * kD * 4;
     const size_t st_bytes = (size_t)n_seqs * H * kD * kD * 4;
     if (overlap(o, o_bytes, q, tok * kD * esz) || overlap(o, o_bytes, k, tok * kD * esz) ||
-        overlap(o, o_bytes, v, tok * kD * esz) || overlap(o, o_bytes, g_raw, tok * kD * 4) ||
+        overlap(o, o_bytes, v, tok * kD * esz) || overlap(o, o_bytes, g_raw, tok * z_row * 4) ||
         overlap(o, o_bytes, beta, tok * 4) || overlap(o, o_bytes, A, (size_t)H * 4) ||
         overlap(o, o_bytes, S0, st_bytes) || overlap(o, o_bytes, S_final, st_bytes) ||
         overlap(o, o_bytes, workspace, need) || overlap(o, o_bytes, out_gate, o_bytes) ||
@@ -112,7 +114,7 @@ int chunk_fwd(const void *q, const void *k, const void *v, kda_dtype qkv_dtype, 
     if (S_ckpt) {
         const size_t ck_bytes = (size_t)ckpt_capacity * H * kD * kD * 4;
         const void *others[] = {q, k, v, g_raw, beta, A, S0, o, S_final, workspace};
-        const size_t sizes[] = {tok * kD * esz, tok * kD * esz, tok * kD * esz, tok * kD * 4, tok * 4,
+        const size_t sizes[] = {tok * kD * esz, tok * kD * esz, tok * kD * esz, tok * z_row * 4, tok * 4,
                                 (size_t)H * 4, st_bytes, o_bytes, st_bytes, need};
         for (int i = 0; i < 10; ++i)
             if (overlap(S_ckpt, ck_bytes, others[i], sizes[i])) return KDA_ERR_ALIAS;
@@ -123,7 +125,7 @@ int chunk_fwd(const void *q, const void *k, const void *v, kda_dtype qkv_dtype, 
     const kda::Ckpt ck{S_ckpt && ckpt_capacity > 0 ? S_ckpt : nullptr, nullptr, (int)(S_ckpt ? ckpt_stride / 64 : 1),
                        ckpt_capacity};
     const kda::Layer ly{lo && lo->qk_l2norm != 0, lo ? lo->qk_eps : 0.f, out_gate, norm_weight,
-                        lo ? lo->norm_eps : 0.f};
+                        lo ? lo->norm_eps : 0.f, lo ? lo->gate_kind : KDA_GATE_K3, lo && lo->gate_per_head != 0};
     const int rc = kda::launch_prefill(q, k, v, qkv_dtype == KDA_F32, g_raw, beta, A, S0, cu_seqlens, B, T, H,
                                        n_seqs, o, S_final, ck, ly, workspace, (hipStream_t)stream,
                                        (hipEvent_t *)stage_events);
@@ -172,27 +174,54 @@ KDA_EXPORT int kda_chunk_fwd_layer(const void *q, const void *k, const void *v, 
                      workspace, workspace_bytes, stream, nullptr, S_ckpt, ckpt_stride, ckpt_capacity, opts);
 }
 
-KDA_EXPORT int kda_decode_step(const void *q, const void *k, const void *v, kda_dtype qkv_dtype,
-                               const float *g_raw, const float *beta, const float *A, float *S, int32_t N,
-                               int32_t H, int32_t dk, int32_t dv, float *o, void *stream) {
+namespace {
+
+// Shared body of the decode entry points.
+int decode_step(const void *q, const void *k, const void *v, kda_dtype qkv_dtype, const float *g_raw,
+                const float *beta, const float *A, float *S, int32_t N, int32_t H, int32_t dk, int32_t dv, float *o,
+                void *stream, const kda_layer_opts *lo) {
     if (dk != kD || dv != kD) return KDA_ERR_SHAPE;
     if (N < 0 || H < 0) return KDA_ERR_SHAPE;
     if (qkv_dtype != KDA_BF16 && qkv_dtype != KDA_F32) return KDA_ERR_DTYPE;
     if ((int64_t)N * H > INT32_MAX) return KDA_ERR_SHAPE;
+    if (lo && (!(lo->qk_eps >= 0.f) || !(lo->norm_eps >= 0.f))) return KDA_ERR_SHAPE;  // NaN fails too
+    if (lo && lo->gate_kind != KDA_GATE_K3 && lo->gate_kind != KDA_GATE_SOFTPLUS) return KDA_ERR_SHAPE;
     if (N == 0 || H == 0) return KDA_OK;
     if (!q || !k || !v || !g_raw || !beta || !A || !S || !o) return KDA_ERR_NULL;
-    const void *ptrs[] = {q, k, v, g_raw, beta, A, S, o};
+    const float *out_gate = lo ? lo->out_gate : nullptr, *norm_weight = lo ? lo->norm_weight : nullptr;
+    if (out_gate && !norm_weight) return KDA_ERR_NULL;
+    const void *ptrs[] = {q, k, v, g_raw, beta, A, S, o, out_gate, norm_weight};
     for (const void *p : ptrs)
         if (misaligned(p)) return KDA_ERR_ALIGN;
     const size_t esz = qkv_dtype == KDA_F32 ? 4 : 2;
     const size_t nh = (size_t)N * H;
     const size_t o_bytes = nh * kD * 4;
+    const size_t z_row = lo && lo->gate_per_head ? 1 : kD;
     if (overlap(o, o_bytes, S, nh * kD * kD * 4) || overlap(o, o_bytes, q, nh * kD * esz) ||
         overlap(o, o_bytes, k, nh * kD * esz) || overlap(o, o_bytes, v, nh * kD * esz) ||
-        overlap(o, o_bytes, g_raw, nh * kD * 4) || overlap(o, o_bytes, beta, nh * 4) ||
-        overlap(o, o_bytes, A, (size_t)H * 4))
+        overlap(o, o_bytes, g_raw, nh * z_row * 4) || overlap(o, o_bytes, beta, nh * 4) ||
+        overlap(o, o_bytes, A, (size_t)H * 4) || overlap(o, o_bytes, out_gate, o_bytes) ||
+        overlap(o, o_bytes, norm_weight, (size_t)kD * 4))
         return KDA_ERR_ALIAS;
-    const int rc = kda::launch_decode(q, k, v, qkv_dtype == KDA_F32, g_raw, beta, A, S, N, H, o,
+    const kda::Layer ly{lo && lo->qk_l2norm != 0, lo ? lo->qk_eps : 0.f, out_gate, norm_weight,
+                        lo ? lo->norm_eps : 0.f, lo ? lo->gate_kind : KDA_GATE_K3, lo && lo->gate_per_head != 0};
+    const int rc = kda::launch_decode(q, k, v, qkv_dtype == KDA_F32, g_raw, beta, A, S, N, H, o, ly,
                                       (hipStream_t)stream);
     return rc == 0 ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // namespace
+
+KDA_EXPORT int kda_decode_step(const void *q, const void *k, const void *v, kda_dtype qkv_dtype,
+                               const float *g_raw, const float *beta, const float *A, float *S, int32_t N,
+                               int32_t H, int32_t dk, int32_t dv, float *o, void *stream) {
+    return decode_step(q, k, v, qkv_dtype, g_raw, beta, A, S, N, H, dk, dv, o, stream, nullptr);
+}
+
+KDA_EXPORT int kda_decode_step_layer(const void *q, const void *k, const void *v, kda_dtype qkv_dtype,
+                                     const float *g_raw, const float *beta, const float *A, float *S, int32_t N,
+                                     int32_t H, int32_t dk, int32_t dv, const kda_layer_opts *opts, float *o,
+                                     void *stream) {
+    if (!opts) return KDA_ERR_NULL;
+    return decode_step(q, k, v, qkv_dtype, g_raw, beta, A, S, N, H, dk, dv, o, stream, opts);
 }

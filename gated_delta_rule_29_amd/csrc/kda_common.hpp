@@ -51,6 +51,8 @@ struct Layer {
     const float *gate;    // [tokens, H, 128] fp32 pre-activation, or nullptr: no output step
     const float *weight;  // [128]
     float norm_eps;
+    int gate_kind;        // GATE_K3 or GATE_SOFTPLUS
+    bool gate_per_head;   // z is [tokens, H]: one gate value per (token, head)
 };
 
 __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -146,6 +148,27 @@ __device__ __forceinline__ float to_f(__bf16 x) { return (float)x; }
 __device__ __forceinline__ float kda_gate(float expA, float z) {
     const float x = expA * z;
     return GMIN * __builtin_amdgcn_rcpf(1.f + __expf(-x));
+}
+// Kimi Linear's unbounded negative-softplus decay, the parameterisation the K3
+// gate replaces (Kimi K3 architecture, sequence-bottleneck section; K3 paper
+// review, Method): g = -e^A softplus(z), softplus(z) = max(z, 0) + log(1 + e^-|z|).
+// z = -inf gives 0 (alpha = 1).  A step's log-decay is floored at SP_G_FLOOR:
+// e^-104 lies below fp32's smallest subnormal (e^-103.3), so alpha is zero in
+// fp32 either way, and the floor keeps the chunk form's running sums finite
+// (z = +inf would otherwise give differences -inf - (-inf)).  NaN propagates.
+constexpr float SP_G_FLOOR = -104.f;
+__device__ __forceinline__ float softplus_gate(float expA, float z) {
+    const float g = -expA * (fmaxf(z, 0.f) + __logf(1.f + __expf(-fabsf(z))));
+    return g < SP_G_FLOOR ? SP_G_FLOOR : g;
+}
+// Decay parameterisations (kda_layer_opts::gate_kind).
+enum { GATE_K3 = 0, GATE_SOFTPLUS = 1 };
+template <int GK>
+__device__ __forceinline__ float gate_of(float expA, float z) {
+    if constexpr (GK == GATE_K3)
+        return kda_gate(expA, z);
+    else
+        return softplus_gate(expA, z);
 }
 
 }  // namespace kda

@@ -290,6 +290,11 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
     // ---- phase 1: gate, sub-chunk cumulative sums, elementwise operands ----
     const int ch = tid & (D - 1), half = tid >> 7;
     const float eA = __expf(A[h]);
+    // Unbounded softplus decay: E1 holds the logs G_t - R_s rather than their
+    // exponentials (1 / E1 would overflow), and the diagonal Gram tiles are
+    // formed position pair by position pair in phase 2.
+    const bool sp = tab.ly.gate_kind == GATE_SOFTPLUS;
+    const bool zh = tab.ly.gate_per_head;  // z is [tokens, H]
     // The running sums are kept in fp64: a log-decay difference formed from
     // fp32 sums of up to 64 gates (|G| up to 320) loses ~1e-5 absolute, which
     // the exponential turns into relative error of every decay factor.  Only
@@ -302,10 +307,14 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
 #pragma unroll
         for (int u = 0; u < SUB; ++u) {
             const int t = s * SUB + u;
-            const float gt = t < len ? kda_gate(eA, z[tok(t) + ch]) : 0.f;
+            float gt = 0.f;
+            if (t < len) {
+                const float zv = zh ? z[(size_t)(t0 + t) * H + h] : z[tok(t) + ch];
+                gt = sp ? softplus_gate(eA, zv) : kda_gate(eA, zv);
+            }
             acc += (double)gt;
             Gl[si][u] = acc;
-            sm.E1[t * PG + ch] = __expf((float)acc);
+            sm.E1[t * PG + ch] = sp ? (float)acc : __expf((float)acc);
         }
         sm.R[(s + 1) * D + ch] = acc;  // sub-chunk total, turned into R below
     }
@@ -379,6 +388,21 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
         const int cr = 16 * j + lr;  // column-side token (A operand row)
         const int rr = 16 * i + lr;  // row-side token (B operand column)
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (sp && j == i) {
+            // Position pairs (rr, c = 16 i + 4 g + m): sum_ch x_rr k_c e^{L_rr - L_c}
+            // with L = G - R_i; the exponent is clamped at 0 (c > rr is masked below).
+            const float nr = mat == 0 ? sm.nk[rr] : sm.nq[rr];
+            const int c0 = 16 * i + 4 * g;
+            for (int e = 0; e < D; ++e) {
+                const float xr = rr < len ? to_f(X[tok(rr) + e]) * nr : 0.f, lrr = sm.E1[rr * PG + e];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int cc = c0 + m;
+                    const float kc = cc < len ? to_f(k[tok(cc) + e]) * sm.nk[cc] : 0.f;
+                    acc[m] += xr * kc * __expf(fminf(lrr - sm.E1[cc * PG + e], 0.f));
+                }
+            }
+        } else
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const int c0 = 32 * ks + 8 * g;
@@ -388,10 +412,17 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
             const float nc = sm.nk[cr], nr = mat == 0 ? sm.nk[rr] : sm.nq[rr];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                float inv = __frcp_rn(sm.E1[cr * PG + c0 + e]);  // e^{R_j - G_c}
-                if (j < i) inv *= sm.PF[pair_index(i, j) * D + c0 + e];
+                float inv, er;
+                if (sp) {  // e^{(R_i - R_j) - (G_c - R_j)} <= 1 for j < i
+                    inv = __expf((float)(sm.R[i * D + c0 + e] - sm.R[j * D + c0 + e]) - sm.E1[cr * PG + c0 + e]);
+                    er = __expf(sm.E1[rr * PG + c0 + e]);
+                } else {
+                    inv = __frcp_rn(sm.E1[cr * PG + c0 + e]);  // e^{R_j - G_c}
+                    if (j < i) inv *= sm.PF[pair_index(i, j) * D + c0 + e];
+                    er = sm.E1[rr * PG + c0 + e];
+                }
                 a.v[e] = kc.v[e] * nc * inv;
-                b.v[e] = xr.v[e] * nr * sm.E1[rr * PG + c0 + e];
+                b.v[e] = xr.v[e] * nr * er;
             }
             if constexpr (F32)
                 acc = mma_ff(acc, a, b);

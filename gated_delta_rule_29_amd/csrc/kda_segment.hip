@@ -231,8 +231,14 @@ static_assert(PTT <= PEH, "T lives in the E1 region");
 #endif
 // QKN: q and k arrive raw and are normalised to unit length here (the layer's
 // step fused in); a separate instantiation, so the plain path carries none of it.
-template <bool QKN>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WY_WPE))) void wy_kernel(
+// GK: the decay parameterisation.  With the K3 gate every factor of a 16-token
+// tile lies in [e^-80, e^80] and the diagonal Gram tiles are dense MFMA
+// products like the others.  With the unbounded softplus decay a factor
+// e^{G_r - G_c} of a diagonal tile cannot be split into a row and a column part
+// without overflow, so those tiles are formed position pair by position pair
+// on the VALU, in the log domain (the cost the K3 bound removes).
+template <bool QKN, int GK>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GK == GATE_K3 ? WY_WPE : 2))) void wy_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     const float *__restrict__ z, const float *__restrict__ beta, const float *__restrict__ A, int N, int H,
     SegTable tab) {
@@ -257,8 +263,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WY_WPE))) v
     // channels 64 hf + 16 w + lr.  Buffer loads: the resource of each input
     // covers this chunk's rows, so a row past the end reads as 0 and the row
     // part of every offset is a scalar.
-    const uint32_t pz = (uint32_t)(HD * 4), ph = (uint32_t)(HD * 2);  // row pitches in bytes
-    const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc((void *)(z + base), 0, len * pz, BUF_RSRC3);
+    // z is [tokens, H, 128], or [tokens, H] with one gate value per (token, head).
+    const bool zh = tab.ly.gate_per_head;
+    const uint32_t pz = zh ? (uint32_t)(H * 4) : (uint32_t)(HD * 4), ph = (uint32_t)(HD * 2);  // row pitches, bytes
+    const int zcs = zh ? 0 : 4;                                                                // channel pitch
+    const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(z + (zh ? (size_t)t0 * H + h : base)), 0, len * pz, BUF_RSRC3);
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)(k + base), 0, len * ph, BUF_RSRC3);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)(v + base), 0, len * ph, BUF_RSRC3);
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void *)(q + base), 0, len * ph, BUF_RSRC3);
@@ -285,9 +295,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WY_WPE))) v
                     const int tl = 4 * g + (e & 3), tu = 32 * ks + 16 * (e >> 2);  // row = tu (scalar) + tl
                     const bool ok = tu + tl < len;
                     const float zv = __builtin_bit_cast(
-                        float, __builtin_amdgcn_raw_buffer_load_b32(rz, tl * pz + 4 * ch, tu * pz, 0));
+                        float, __builtin_amdgcn_raw_buffer_load_b32(rz, tl * pz + zcs * ch, tu * pz, 0));
                     const uint16_t kv = __builtin_amdgcn_raw_buffer_load_b16(rk, tl * ph + 2 * ch, tu * ph, 0);
-                    gv[ks][e] = kda_gate(eA, ok ? zv : -__builtin_inff());  // z = -inf gives g = 0
+                    gv[ks][e] = gate_of<GK>(eA, ok ? zv : -__builtin_inff());  // z = -inf gives g = 0
                     kb[ks][e] = __builtin_bit_cast(__bf16, kv);
                 }
             // ---- phase 0 (QKN, first half only): the inverse L2 norms of the
@@ -370,8 +380,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WY_WPE))) v
                     const float e1 = __expf(cs);
                     const float kf = QKN ? (float)kb[ks][e] * sm.nk[t] : (float)kb[ks][e];
                     const float cb = kf * __expf(st[s] - cs);  // k e^{R_{s+1} - G_t}
-                    sm.a.E1[t * PEH + chl] = e1;
-                    sm.CB[t * PEH + chl] = cb;
+                    // softplus decay: the log G_t - R_s and raw k instead (phase 2)
+                    sm.a.E1[t * PEH + chl] = GK == GATE_K3 ? e1 : cs;
+                    sm.CB[t * PEH + chl] = GK == GATE_K3 ? cb : kf;
                     kt[e] = (_Float16)(cb * eN[s]);             // k e^{G_n - G_t}
                     kga[hf][ks][e] = (__bf16)(kf * (eRs[s] * e1));
                 }
@@ -381,11 +392,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WY_WPE))) v
         if (g == 0) {
 #pragma unroll
             for (int s = 0; s < 4; ++s) sm.eR[s * D + ch] = eRs[s];
+            if constexpr (GK == GATE_K3) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+                for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int jj = 0; jj <= i; ++jj)
-                    sm.F[(i * (i + 1) / 2 + jj) * D + ch] = __expf(Rs[i] - Rs[jj + 1]);
+                    for (int jj = 0; jj <= i; ++jj)
+                        sm.F[(i * (i + 1) / 2 + jj) * D + ch] = __expf(Rs[i] - Rs[jj + 1]);
+            } else {  // the references R_s themselves, as logs
+#pragma unroll
+                for (int s = 0; s < 4; ++s) sm.F[s * D + ch] = Rs[s];
+            }
             ((float *)(blk + BO_GM))[ch] = __expf(Rs[4]);
         }
         __syncthreads();
@@ -407,7 +423,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WY_WPE))) v
                 const int ro = r * ph + 2 * c0;                         // rows past the end read as 0
                 const bf16x4 k0 = ld_bf16x4(rk, ro), k1 = ld_bf16x4(rk, ro + 32);
                 const bf16x4 q0 = ld_bf16x4(rq, ro), q1 = ld_bf16x4(rq, ro + 32);
-                const f32x4 ea = *(const f32x4 *)&sm.a.E1[r * PEH + cl], eb = *(const f32x4 *)&sm.a.E1[r * PEH + cl + 16];
+                f32x4 ea = *(const f32x4 *)&sm.a.E1[r * PEH + cl], eb = *(const f32x4 *)&sm.a.E1[r * PEH + cl + 16];
+                const f32x4 la = ea, lb = eb;  // softplus decay: logs G_r - R_i
+                if constexpr (GK != GATE_K3)
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        ea[m] = __expf(la[m]);
+                        eb[m] = __expf(lb[m]);
+                    }
                 const f32x4 pa = *(const f32x4 *)&sm.eR[i * D + c0], pb = *(const f32x4 *)&sm.eR[i * D + c0 + 16];
                 F8 xk, xq;
                 f16x8 qt;
@@ -425,21 +448,61 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WY_WPE))) v
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     if (j > i) break;
+                    if (GK != GATE_K3 && j == i) break;  // position pairs, below
                     const int cc = 16 * j + lr;
                     const float *cb = &sm.CB[cc * PEH + cl];
-                    const float *fij = &sm.F[(i * (i + 1) / 2 + j) * D + c0];
                     const f32x4 ca = *(const f32x4 *)cb, cbv = *(const f32x4 *)(cb + 16);
-                    const f32x4 fa = *(const f32x4 *)fij, fb = *(const f32x4 *)(fij + 16);
                     F8 xc;
+                    if constexpr (GK == GATE_K3) {
+                        const float *fij = &sm.F[(i * (i + 1) / 2 + j) * D + c0];
+                        const f32x4 fa = *(const f32x4 *)fij, fb = *(const f32x4 *)(fij + 16);
 #pragma unroll
-                    for (int m = 0; m < 4; ++m) {
-                        xc.v[m] = ca[m] * fa[m];
-                        xc.v[4 + m] = cbv[m] * fb[m];
+                        for (int m = 0; m < 4; ++m) {
+                            xc.v[m] = ca[m] * fa[m];
+                            xc.v[4 + m] = cbv[m] * fb[m];
+                        }
+                    } else {  // k_c e^{R_i - G_c} = k_c e^{(R_i - R_j) - (G_c - R_j)} <= |k_c|
+                        const f32x4 ri = *(const f32x4 *)&sm.F[i * D + c0], ri2 = *(const f32x4 *)&sm.F[i * D + c0 + 16];
+                        const f32x4 rj = *(const f32x4 *)&sm.F[j * D + c0], rj2 = *(const f32x4 *)&sm.F[j * D + c0 + 16];
+                        const f32x4 lc = *(const f32x4 *)&sm.a.E1[cc * PEH + cl];
+                        const f32x4 lc2 = *(const f32x4 *)&sm.a.E1[cc * PEH + cl + 16];
+#pragma unroll
+                        for (int m = 0; m < 4; ++m) {
+                            xc.v[m] = ca[m] * __expf(ri[m] - rj[m] - lc[m]);
+                            xc.v[4 + m] = cbv[m] * __expf(ri2[m] - rj2[m] - lc2[m]);
+                        }
                     }
                     const S8 cs = split8(xc);
                     a1[j] = mma_ss(a1[j], cs, rks);
                     a2[j] = mma_ss(a2[j], cs, rqs);
                 }
+            }
+            if constexpr (GK != GATE_K3) {
+                // Diagonal tile, position pair by position pair: lane (lr, g) forms
+                // its four pairs (r, c = 16 i + 4 g + m) over this half's 64
+                // channels, sum_ch k_r k_c e^{L_r - L_c} (and q_r), L = G - R_i
+                // from LDS; the exponent is clamped at 0 (c > r is masked later).
+                const float *rowl = &sm.a.E1[r * PEH], *rowk = &sm.CB[r * PEH];
+                const float *coll = &sm.a.E1[(16 * i + 4 * g) * PEH], *colk = &sm.CB[(16 * i + 4 * g) * PEH];
+                f32x4 ak = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+                for (int cg = 0; cg < 64; cg += 4) {
+                    const f32x4 l4 = *(const f32x4 *)(rowl + cg), k4 = *(const f32x4 *)(rowk + cg);
+                    const bf16x4 qv = ld_bf16x4(rq, r * (int)ph + 2 * (64 * hf + cg));
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const f32x4 lc = *(const f32x4 *)(coll + m * PEH + cg);
+                        const f32x4 kc = *(const f32x4 *)(colk + m * PEH + cg);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float f = kc[e] * __expf(fminf(l4[e] - lc[e], 0.f));
+                            ak[m] += k4[e] * f;
+                            aq[m] += (QKN ? (float)qv[e] * nqr : (float)qv[e]) * f;
+                        }
+                    }
+                }
+                a1[i] += ak;
+                a2[i] += aq;
             }
         }
     }
@@ -1171,12 +1234,18 @@ int launch_segment_prefill(const __bf16 *q, const __bf16 *k, const __bf16 *v, co
         return -1;
     if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return -1;
     if (T_total > 0) {
-        if (ly.qk_norm)
-            hipLaunchKernelGGL(wy_kernel<true>, dim3((unsigned)(ncm * H)), dim3(256), 0, stream, q, k, v, z, beta, A,
-                               N, H, tab);
-        else
-            hipLaunchKernelGGL(wy_kernel<false>, dim3((unsigned)(ncm * H)), dim3(256), 0, stream, q, k, v, z, beta,
-                               A, N, H, tab);
+        const dim3 grid((unsigned)(ncm * H)), blk(256);
+        if (ly.gate_kind == GATE_SOFTPLUS) {
+            if (ly.qk_norm)
+                hipLaunchKernelGGL((wy_kernel<true, GATE_SOFTPLUS>), grid, blk, 0, stream, q, k, v, z, beta, A, N, H, tab);
+            else
+                hipLaunchKernelGGL((wy_kernel<false, GATE_SOFTPLUS>), grid, blk, 0, stream, q, k, v, z, beta, A, N, H,
+                                   tab);
+        } else if (ly.qk_norm) {
+            hipLaunchKernelGGL((wy_kernel<true, GATE_K3>), grid, blk, 0, stream, q, k, v, z, beta, A, N, H, tab);
+        } else {
+            hipLaunchKernelGGL((wy_kernel<false, GATE_K3>), grid, blk, 0, stream, q, k, v, z, beta, A, N, H, tab);
+        }
     }
     if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return -1;
     hipLaunchKernelGGL(seg_chain_kernel<true>, dim3((unsigned)nsm, (unsigned)H), dim3(CH_NT), 0, stream, N, H, tab,

@@ -181,13 +181,33 @@ int kda_chunk_fwd_ckpt(const void *q, const void *k, const void *v, kda_dtype qk
  *   norm_weight  [128] fp32, the RMSNorm weight shared by all heads (required
  *                with out_gate).
  *   qk_eps, norm_eps  >= 0 (else KDA_ERR_SHAPE); 1e-6 is a usual choice.
+ *   gate_kind    the decay parameterisation (else KDA_ERR_SHAPE):
+ *                KDA_GATE_K3: g = -5 * Sigmoid(exp(A_h) z), the lower-bounded
+ *                  gate of the operator above (Kimi K3 architecture,
+ *                  sequence-bottleneck section);
+ *                KDA_GATE_SOFTPLUS: g = -exp(A_h) softplus(z), Kimi Linear's
+ *                  unbounded negative-softplus decay that the bound replaces
+ *                  (Kimi K3 architecture, sequence-bottleneck section; K3 paper review, Method).
+ *                  With no lower bound on g the 16 x 16 diagonal Gram tiles
+ *                  are formed position pair by position pair instead of on
+ *                  MFMA, which costs the prefill time.  z = -inf gives g = 0;
+ *                  a step's g is floored at -104 (alpha = e^-104 is below
+ *                  fp32's smallest subnormal, so it acts as 0, which z = +inf
+ *                  gives); NaN propagates.
+ *   gate_per_head  nonzero: g_raw is [tokens, H], one value per (token, head)
+ *                applied to all 128 key channels (the scalar per-head gate of
+ *                Gated DeltaNet that KDA refines channel-wise, Kimi Linear
+ *                summary, section 3).  Zero: g_raw is [tokens, H, 128].
  */
+enum { KDA_GATE_K3 = 0, KDA_GATE_SOFTPLUS = 1 };
 typedef struct kda_layer_opts {
     int32_t qk_l2norm;
     float qk_eps;
     const float *out_gate;
     const float *norm_weight;
     float norm_eps;
+    int32_t gate_kind;
+    int32_t gate_per_head;
 } kda_layer_opts;
 /*
  * kda_chunk_fwd with the layer's steps fused in (opts, NULL gives KDA_ERR_NULL)
@@ -217,6 +237,19 @@ int kda_chunk_fwd_layer(const void *q, const void *k, const void *v, kda_dtype q
 int kda_decode_step(const void *q, const void *k, const void *v, kda_dtype qkv_dtype,
                     const float *g_raw, const float *beta, const float *A, float *S, int32_t N,
                     int32_t H, int32_t dk, int32_t dv, float *o, void *stream);
+/*
+ * kda_decode_step with the layer's steps and gate options of kda_layer_opts
+ * (opts, NULL gives KDA_ERR_NULL): q and k normalised to unit length inside
+ * (qk_l2norm), o returned as RMSNorm(o) * norm_weight * sigmoid(out_gate)
+ * (out_gate [N, H, 128] fp32, or NULL), the decay chosen by gate_kind, and
+ * g_raw of [N, H] when gate_per_head is set.  The state update is the
+ * operator's own either way; the same validation as kda_decode_step, plus the
+ * option checks of kda_chunk_fwd_layer.
+ */
+int kda_decode_step_layer(const void *q, const void *k, const void *v, kda_dtype qkv_dtype,
+                          const float *g_raw, const float *beta, const float *A, float *S, int32_t N,
+                          int32_t H, int32_t dk, int32_t dv, const kda_layer_opts *opts, float *o,
+                          void *stream);
 
 #ifdef __cplusplus
 }

@@ -150,6 +150,16 @@ def test_prefill_layer_rejects():
     assert call_prefill_layer(prefill_args(B=0, N=0, T=0), Opts(1, 1e-6, gate, w, 1e-6)) == OK
 
 
+def test_prefill_gate_options_are_checked():
+    gate, w = fake(13).value, fake(14).value
+    for kind in (-1, 2, 7):
+        assert call_prefill_layer(prefill_args(), Opts(0, 0.0, None, None, 0.0, kind, 0)) == SHAPE
+    # g_raw spans [tokens, H, 128] floats, or [tokens, H] with the per-head gate (256 tokens x heads here)
+    assert call_prefill_layer(prefill_args(o=fake(4, 2048)), Opts(0, 0.0, None, None, 0.0, 1, 0)) == ALIAS
+    assert call_prefill_layer(prefill_args(o=fake(4, 512)), Opts(0, 0.0, None, None, 0.0, 1, 1)) == ALIAS
+    assert call_prefill_layer(prefill_args(B=0, N=0, T=0), Opts(0, 0.0, gate, w, 0.0, 1, 1)) == OK
+
+
 def test_ckpt_count():
     assert kda.ckpt_count([0, 63, 64, 6143, 6144, 20000], 6144) == 0 + 0 + 0 + 0 + 1 + 3
     assert kda.ckpt_count([128, 129, 255, 256], 128) == 1 + 1 + 1 + 2
@@ -186,3 +196,24 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(kda, "_LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(kda.KDAError):
         kda.load()
+
+
+def call_decode_layer(a, opts):
+    lib = kda.load()
+    return lib.kda_decode_step_layer(a["q"], a["k"], a["v"], a["dtype"], a["z"], a["beta"], a["A"], a["S"],
+                                     a["N"], a["H"], a["dk"], a["dv"], None if opts is None else ctypes.byref(opts),
+                                     a["o"], a["stream"])
+
+
+def test_decode_layer_rejects():
+    gate, w = fake(13).value, fake(14).value
+    assert call_decode_layer(decode_args(), None) == NULL
+    assert call_decode_layer(decode_args(), Opts(0, 0.0, gate, None, 0.0)) == NULL
+    assert call_decode_layer(decode_args(), Opts(0, -1.0, None, None, 0.0)) == SHAPE
+    assert call_decode_layer(decode_args(), Opts(0, 0.0, None, None, 0.0, 5, 0)) == SHAPE
+    assert call_decode_layer(decode_args(), Opts(0, 0.0, gate + 8, w, 0.0)) == ALIGN
+    assert call_decode_layer(decode_args(o=fake(13, 256)), Opts(0, 0.0, gate, w, 0.0)) == ALIAS
+    # g_raw is [N, H] floats with the per-head gate (8 values here), [N, H, 128] otherwise
+    assert call_decode_layer(decode_args(o=fake(4, 1024)), Opts(0, 0.0, None, None, 0.0, 0, 0)) == ALIAS
+    assert call_decode_layer(decode_args(o=fake(4, 16)), Opts(0, 0.0, None, None, 0.0, 0, 1)) == ALIAS
+    assert call_decode_layer(decode_args(N=0), Opts(1, 1e-6, gate, w, 1e-6, 1, 1)) == OK

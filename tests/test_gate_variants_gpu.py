@@ -1,0 +1,230 @@
+"""GPU parity of the decay variants sharing the kernels, against the oracle's
+recurrence with the log-decays given directly (recurrent_g):
+
+* Kimi Linear's unbounded negative-softplus decay g = -e^A softplus(z) (Kimi K3
+  architecture, sequence-bottleneck section; K3 paper review, Method), whose diagonal 16 x 16 Gram tiles the
+  kernels form position pair by position pair, at mild and at steep decay (per-step
+  log-decays down to about -80, far below the K3 bound of -5, where a sub-chunk's
+  decay range leaves fp32);
+* the per-head scalar gate of Gated DeltaNet (one z per token and head for all 128
+  key channels), with either parameterisation;
+* the same options in the decode step (kda_decode_step_layer), with and without the
+  layer's normalisation and output steps.
+
+Bars as for the operator: max|Δ|/RMS <= 1e-2 (bf16 q/k/v) and <= 1e-4 (fp32 q/k/v)."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_helpers import DEV, err, say, to_dev
+
+import gated_delta_rule_29_amd as kda
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 1e-2, "f32": 1e-4}
+EPS = 1e-6
+LENS = [100, 0, 640, 17, 64, 383]
+
+
+def log_decays(z, A, gate, per_head):
+    """g [T, H, 128] float64 for the oracle: per-head z is broadcast over the channels."""
+    zz = np.repeat(z[:, :, None], 128, axis=2) if per_head else z
+    if gate == "softplus":
+        return oracle.softplus_gate(zz, A)
+    return np.stack([oracle.gate(zz[:, h], A[h]) for h in range(zz.shape[1])], axis=1)
+
+
+def variant_inputs(seed, io, gate, per_head, steep=False, lens=LENS, H=3):
+    cu = synth.cu_seqlens(lens)
+    T = int(cu[-1])
+    d = synth.prefill_inputs(seed, T, H, dtype=io, z_scale=1.5, s0_std=0.02, n_seqs=len(lens))
+    z = d["z"][:, :, 0].copy() if per_head else d["z"]
+    if steep:  # softplus(z) ~ z for large z: per-step log-decays of -e^A (3 .. 30)
+        z = (z * 6.0 + 16.0).astype(np.float32)
+    d["z"] = np.ascontiguousarray(z, dtype=np.float32)
+    d["g"] = log_decays(d["z"], d["A"].astype(np.float64), gate, per_head)
+    return d, cu
+
+
+def upload(d, io, cu):
+    dt = torch.bfloat16 if io == "bf16" else torch.float32
+    t = {n: to_dev(d[n], dt) for n in ("q", "k", "v")}
+    for n in ("z", "beta", "A", "S0"):
+        t[n] = to_dev(d[n], torch.float32)
+    t["cu"] = None if cu is None else to_dev(np.asarray(cu, np.int32), torch.int32)
+    return t
+
+
+def run_and_check(d, cu, io, gate, label):
+    t = upload(d, io, cu)
+    say(f"case {label}")
+    o, Sf = kda.kda_chunk_fwd(t["q"], t["k"], t["v"], t["z"], t["beta"], t["A"], t["S0"], t["cu"], gate=gate)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.recurrent_g(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], cu)
+    o_np, S_np = o.cpu().numpy(), Sf.cpu().numpy()
+    assert np.isfinite(o_np).all() and np.isfinite(S_np).all()
+    eo, es = err(o_np, o_ref), err(S_np, S_ref)
+    say(f"  {label} err_o={eo:.3e} err_S={es:.3e} min g={d['g'].min():.1f}")
+    assert eo <= TOL[io] and es <= TOL[io], (eo, es)
+    return o, Sf
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("steep", [False, True])
+def test_softplus_decay(io, steep):
+    d, cu = variant_inputs(5300 + steep, io, "softplus", per_head=False, steep=steep)
+    if steep:
+        assert d["g"].min() < -40.0  # sub-chunk decay ranges far beyond e^-87
+    run_and_check(d, cu, io, "softplus", f"softplus io={io} steep={steep}")
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_softplus_infinite_z(io):
+    """z = +inf (alpha = 0: the state restarts) and z = -inf (alpha = 1) at scattered positions,
+    among them whole rows and the first and last token of a chunk."""
+    d, cu = variant_inputs(5305, io, "softplus", per_head=False)
+    rng = np.random.Generator(np.random.PCG64(5305))
+    z = d["z"]
+    T = z.shape[0]
+    for val in (np.inf, -np.inf):
+        idx = rng.integers(0, z.size, size=z.size // 50)
+        z.reshape(-1)[idx] = val
+    z[63], z[64, 1], z[127, 2, :64] = np.inf, -np.inf, np.inf
+    z[min(T - 1, 700), 0] = np.inf
+    d["g"] = log_decays(z, d["A"].astype(np.float64), "softplus", False)
+    assert np.isneginf(d["g"]).any()
+    run_and_check(d, cu, io, "softplus", f"softplus +-inf io={io}")
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("gate", ["k3", "softplus"])
+def test_per_head_gate(io, gate):
+    d, cu = variant_inputs(5310, io, gate, per_head=True)
+    run_and_check(d, cu, io, gate, f"per-head gate={gate} io={io}")
+
+
+def test_per_head_gate_equals_broadcast_channels():
+    """The per-head form and the same value written to all 128 channels run the same kernels
+    on the same decays: identical bits."""
+    d, cu = variant_inputs(5320, "bf16", "softplus", per_head=True)
+    t = upload(d, "bf16", cu)
+    zb = t["z"][:, :, None].expand(-1, -1, 128).contiguous()
+    say("case per-head vs broadcast")
+    for gate in ("k3", "softplus"):
+        o1, S1 = kda.kda_chunk_fwd(t["q"], t["k"], t["v"], t["z"], t["beta"], t["A"], t["S0"], t["cu"], gate=gate)
+        o2, S2 = kda.kda_chunk_fwd(t["q"], t["k"], t["v"], zb, t["beta"], t["A"], t["S0"], t["cu"], gate=gate)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(S1, S2), gate
+
+
+def test_softplus_long_sequence_several_segments():
+    """One 4096-token sequence (several chain segments) at steep decay, bf16."""
+    d, cu = variant_inputs(5330, "bf16", "softplus", per_head=False, steep=True, lens=[4096], H=2)
+    run_and_check(d, cu, "bf16", "softplus", "softplus T=4096 steep")
+
+
+def test_softplus_with_layer_steps_and_snapshots():
+    """The variant composes with the fused layer steps and the prefix-cache snapshots: the
+    snapshots equal separate prefills of the prefixes."""
+    lens = [300, 64, 257]
+    d, cu = variant_inputs(5340, "bf16", "softplus", per_head=False, steep=True, lens=lens, H=2)
+    t = upload(d, "bf16", cu)
+    stride = 128
+    ck = torch.empty((kda.ckpt_count(lens, stride), 2, 128, 128), dtype=torch.float32, device=DEV)
+    say("case softplus + qk_l2norm + snapshots")
+    o, Sf = kda.kda_chunk_fwd(t["q"], t["k"], t["v"], t["z"], t["beta"], t["A"], t["S0"], t["cu"], gate="softplus",
+                              qk_l2norm=True, qk_eps=EPS, S_ckpt=ck, ckpt_stride=stride)
+    torch.cuda.synchronize()
+    qn, kn = oracle.l2_normalize(d["q"], EPS), oracle.l2_normalize(d["k"], EPS)
+    o_ref, S_ref = oracle.recurrent_g(qn, kn, d["v"], d["g"], d["beta"], d["S0"], cu)
+    eo, es = err(o.cpu().numpy(), o_ref), err(Sf.cpu().numpy(), S_ref)
+    say(f"  err_o={eo:.3e} err_S={es:.3e}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+    slot = 0
+    for n, L in enumerate(lens):
+        for m in range(L // stride):
+            end = int(cu[n]) + (m + 1) * stride
+            sl = slice(int(cu[n]), end)
+            _, S_m = oracle.recurrent_g(qn[sl], kn[sl], d["v"][sl], d["g"][sl], d["beta"][sl], d["S0"][n:n + 1])
+            e = err(ck[slot].cpu().numpy(), S_m[0])
+            assert e <= TOL["bf16"], (n, m, e)
+            slot += 1
+
+
+# ---------------------------------------------------------------- decode --
+
+def decode_inputs(seed, io, N=5, H=3, per_head=False, steep=False):
+    d = synth.decode_tokens(seed, 0, N, H, dtype=io)
+    d["A"] = synth.head_params(seed, H)
+    d["S"] = synth.initial_state(seed, N, H, 0.05)
+    rng = np.random.Generator(np.random.PCG64(seed + 11))
+    for n in ("q", "k"):  # raw rows for the layer's normalisation
+        x = d[n] * rng.uniform(0.3, 3.0, size=(N, H, 1)).astype(np.float32)
+        d[n + "_raw"] = (synth.bf16_round(x) if io == "bf16" else x).astype(np.float32)
+    z = d["z"][:, :, 0].copy() if per_head else d["z"]
+    if steep:
+        z = z * 6.0 + 16.0
+    d["z"] = np.ascontiguousarray(z, dtype=np.float32)
+    d["gate"] = (2.0 * rng.standard_normal((N, H, 128))).astype(np.float32)
+    d["weight"] = rng.uniform(0.5, 1.5, size=128).astype(np.float32)
+    return d
+
+
+def decode_reference(d, g, layer):
+    q, k = (d["q_raw"], d["k_raw"]) if layer else (d["q"], d["k"])
+    if layer:
+        q, k = oracle.l2_normalize(q, EPS), oracle.l2_normalize(k, EPS)
+    N = q.shape[0]
+    cu = np.arange(N + 1, dtype=np.int64)  # N sequences of one token, each from its own state
+    o, S = oracle.recurrent_g(q, k, d["v"], g, d["beta"], d["S"], cu)
+    if layer:
+        o = oracle.gated_rmsnorm(o, d["gate"], d["weight"], EPS)
+    return o, S
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("gate,per_head,steep,layer", [
+    ("softplus", False, False, False), ("softplus", False, True, False), ("k3", True, False, False),
+    ("softplus", True, False, True), ("k3", False, False, True),
+])
+def test_decode_variants(io, gate, per_head, steep, layer):
+    d = decode_inputs(5400 + 2 * per_head + steep + 4 * layer, io, per_head=per_head, steep=steep)
+    g = log_decays(d["z"], d["A"].astype(np.float64), gate, per_head)
+    dt = torch.bfloat16 if io == "bf16" else torch.float32
+    q = to_dev(d["q_raw"] if layer else d["q"], dt)
+    k = to_dev(d["k_raw"] if layer else d["k"], dt)
+    v = to_dev(d["v"], dt)
+    z, beta, A, S = (to_dev(d[n], torch.float32) for n in ("z", "beta", "A", "S"))
+    kw = dict(qk_l2norm=True, qk_eps=EPS, out_gate=to_dev(d["gate"], torch.float32),
+              norm_weight=to_dev(d["weight"], torch.float32), norm_eps=EPS) if layer else {}
+    say(f"case decode io={io} gate={gate} per_head={per_head} steep={steep} layer={layer}")
+    o = kda.kda_decode_step(q, k, v, z, beta, A, S, gate=gate, **kw)
+    torch.cuda.synchronize()
+    o_ref, S_ref = decode_reference(d, g, layer)
+    eo, es = err(o.cpu().numpy(), o_ref), err(S.cpu().numpy(), S_ref)
+    say(f"  err_o={eo:.3e} err_S={es:.3e}")
+    assert eo <= TOL[io] and es <= TOL[io], (eo, es)
+
+
+def test_decode_plain_options_are_the_plain_step():
+    """kda_decode_step_layer with every option off gives the bits of kda_decode_step."""
+    d = decode_inputs(5450, "bf16")
+    q, k, v = (to_dev(d[n], torch.bfloat16) for n in ("q", "k", "v"))
+    z, beta, A = (to_dev(d[n], torch.float32) for n in ("z", "beta", "A"))
+    S1, S2 = to_dev(d["S"], torch.float32), to_dev(d["S"], torch.float32)
+    say("case decode layer-off bits")
+    o1 = kda.kda_decode_step(q, k, v, z, beta, A, S1)
+    opts = kda.LayerOpts(0, 0.0, None, None, 0.0, 0, 0)
+    o2 = torch.empty_like(o1)
+    lib = kda.load()
+    rc = lib.kda_decode_step_layer(q.data_ptr(), k.data_ptr(), v.data_ptr(), 0, z.data_ptr(), beta.data_ptr(),
+                                   A.data_ptr(), S2.data_ptr(), 5, 3, 128, 128, ctypes.byref(opts), o2.data_ptr(),
+                                   torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert rc == 0
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
