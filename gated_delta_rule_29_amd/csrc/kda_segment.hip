@@ -46,7 +46,11 @@
 // Operand precision (chosen against the fp64 oracle): W, Q~, K~ and the state
 // enter the chain as single fp16; Delta as fp16 hi + lo; Aqk as fp16 hi + lo;
 // the Gram tiles and T diag(beta) as bf16 hi + lo (their column factors reach
-// e^80, beyond fp16 range).
+// e^80, beyond fp16 range).  U is stored in 16-bit fixed point with a
+// power-of-two scale per 4 x 16 block (error <= 2^-14 of the block's largest
+// value): U enters the state, so its rounding accumulates along the chain, and
+// single fp16 (relative 2^-11 per value) doubled the error of o; the block
+// format costs the bytes of fp16 and keeps the error of fp32 U.
 #include <utility>
 
 #include "kda_common.hpp"
@@ -56,6 +60,7 @@ namespace kda {
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
 
 __device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -66,9 +71,11 @@ constexpr int BO_W = 0;        // -W   A tiles (token tile rt 0..3, key block s 
 constexpr int BO_QT = 16384;   // Q~   same layout as W
 constexpr int BO_KT = 32768;   // K~^T A tiles (key tile rt 0..7, token block s 0..1), fp16, k = perm32(token)
 constexpr int BO_AQ = 49152;   // Aqk  A tiles (rt, s <= rt/2): fp16 hi tile then lo tile, k = perm32(token)
-constexpr int BO_U = 61440;    // U    C tiles (token tile rt 0..3, value tile ct 0..7), fp32
-constexpr int BO_GM = 94208;   // gamma = e^{G_n}, 128 fp32
-constexpr size_t BLK = 94720;  // multiple of 256
+constexpr int BO_U = 61440;    // U    C tiles (token tile rt 0..3, value tile ct 0..7), 16-bit fixed point (UBlk)
+constexpr int U_TILE = 512;    // bytes of one U tile: 8 per lane
+constexpr int BO_US = 77824;   // U scales: fp32 per (tile, lane group g), each for 4 rows x 16 columns
+constexpr int BO_GM = 78336;   // gamma = e^{G_n}, 128 fp32
+constexpr size_t BLK = 78848;  // multiple of 256
 
 __device__ __forceinline__ int aq_tile(int rt, int s) { return rt < 2 ? rt : 2 * rt - 2 + s; }
 __device__ __forceinline__ int frag(int tile, int lane) { return (tile * 64 + lane) * 16; }
@@ -99,6 +106,45 @@ __device__ __forceinline__ void split_f16_pair(float a, float b, uint32_t &hi, u
 constexpr int PTT = 68;  // pitch (floats) of T [64][64]
 
 // f(std::integral_constant<int, i>) for i = 0 .. N-1, expanded at compile time.
+// Maximum over one DPP row (16 lanes with equal lane / 16), in every lane.
+__device__ __forceinline__ float row_max16(float x) {
+    x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false)));
+    x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false)));
+    x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false)));
+    x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false)));
+    return x;
+}
+
+// U in 16-bit fixed point: each block of 4 rows x 16 columns (one lane group of
+// a C tile) shares a power-of-two scale sc with max|u| / sc < 2^14, so a value
+// is stored to within sc / 2 <= 2^-14 max|u| of the block, and |q| <= 2^14
+// needs no clamp.  Decoding, q * sc, is exact.  A block holding inf or NaN
+// gets that value as its scale and decodes to inf / NaN.
+struct UBlk {
+    uint32_t q01, q23;
+    float sc;
+};
+__device__ __forceinline__ UBlk u_encode(f32x4 u, float bmax) {
+    const uint32_t eb = (__builtin_bit_cast(uint32_t, bmax) >> 23) & 0xFF;  // bmax < 2^(eb - 126)
+    const uint32_t e2 = max(eb, 14u) - 13;                                   // sc = 2^(e2 - 127)
+    const bool fin = eb != 0xFF;
+    const float sc = fin ? __builtin_bit_cast(float, e2 << 23) : bmax;
+    const float inv = fin ? __builtin_bit_cast(float, (254 - e2) << 23) : 0.f;
+    int qv[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) qv[m] = (int)rintf(u[m] * inv);
+    return {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pk_i16(qv[0], qv[1])),
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pk_i16(qv[2], qv[3])), sc};
+}
+__device__ __forceinline__ f32x4 u_decode(UBlk b) {
+    f32x4 u;
+    u[0] = (float)(int)(int16_t)(b.q01 & 0xFFFF) * b.sc;
+    u[1] = (float)((int)b.q01 >> 16) * b.sc;
+    u[2] = (float)(int)(int16_t)(b.q23 & 0xFFFF) * b.sc;
+    u[3] = (float)((int)b.q23 >> 16) * b.sc;
+    return u;
+}
+
 template <typename F, int... I>
 __device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
     (f(std::integral_constant<int, I>{}), ...);
@@ -238,7 +284,7 @@ static_assert(PTT <= PEH, "T lives in the E1 region");
 // without overflow, so those tiles are formed position pair by position pair
 // on the VALU, in the log domain (the cost the K3 bound removes).
 template <bool QKN, int GK>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GK == GATE_K3 ? WY_WPE : 2))) void wy_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WY_WPE))) void wy_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     const float *__restrict__ z, const float *__restrict__ beta, const float *__restrict__ A, int N, int H,
     SegTable tab) {
@@ -387,6 +433,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GK == GATE_
                     kga[hf][ks][e] = (__bf16)(kf * (eRs[s] * e1));
                 }
                 *(f16x8 *)(blk + BO_KT + frag((4 * hf + w) * 2 + ks, l)) = kt;
+                // K * Gam formed here and kept (else the compiler defers it to
+                // phase 4 and spills its inputs instead)
+                {
+                    u32x4 kg = __builtin_bit_cast(u32x4, kga[hf][ks]);
+                    __asm__ volatile("" : "+v"(kg));
+                    kga[hf][ks] = __builtin_bit_cast(bf16x8, kg);
+                }
             }
         }
         if (g == 0) {
@@ -647,7 +700,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GK == GATE_
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks)
                     if (ks <= (rt >> 1)) u = mma_s1(u, tb[rt][ks], vb[hf][ks]);
-                *(f32x4 *)(blk + BO_U + frag(8 * rt + ctile, l)) = u;
+                {
+                    const float bm = row_max16(fmaxf(fmaxf(fabsf(u[0]), fabsf(u[1])), fmaxf(fabsf(u[2]), fabsf(u[3]))));
+                    const UBlk ub = u_encode(u, bm);
+                    *(uint2 *)(blk + BO_U + U_TILE * (8 * rt + ctile) + 8 * l) = make_uint2(ub.q01, ub.q23);
+                    if (lr == 0) *(float *)(blk + BO_US + 16 * (8 * rt + ctile) + 4 * g) = ub.sc;
+                }
+                __builtin_amdgcn_sched_barrier(0);  // one tile's encode at a time
             }
         }
     }
@@ -809,15 +868,23 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
             }
 
     // Past the segment's last chunk the copies read nothing (and U is 0).
-    auto load_u = [&](int chunk, f32x4 (&u)[4][NCT]) {
+    using UReg = UBlk;  // as stored: decoded at the start of the step that uses it
+    auto load_u = [&](int chunk, UReg (&u)[4][NCT]) {
         const __amdgpu_buffer_rsrc_t ru = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(blk0 + (size_t)chunk * bstride), 0, chunk < cend ? u_records : 0, BUF_RSRC3);
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct)
-                u[rt][ct] = __builtin_bit_cast(
-                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(ru, BO_U + frag(8 * rt + utile + ct, l), 0, 0));
+            for (int ct = 0; ct < NCT; ++ct) {
+                // lane part as the register offset, the tile part (wave-uniform) as the scalar one
+                const int tile = 8 * rt + utile + ct;
+                const u32x2 qq = __builtin_bit_cast(
+                    u32x2, __builtin_amdgcn_raw_buffer_load_b64(ru, 8 * l, BO_U + U_TILE * tile, 0));
+                u[rt][ct].q01 = qq[0];
+                u[rt][ct].q23 = qq[1];
+                u[rt][ct].sc =
+                    __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ru, 4 * g, BO_US + 16 * tile, 0));
+            }
     };
     // A full state (this wave's columns) to dst [128][128]: buffer stores with
     // the row offset as a scalar operand, so the lane offset is one register.
@@ -916,9 +983,9 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
         return x;
     };
 
-    // U of a chunk is loaded one step ahead into one of two register sets; the
-    // set then serves in place as the Delta accumulator of its step.
-    f32x4 ua[4][NCT], ub[4][NCT];
+    // U of a chunk is loaded one step ahead, as stored, into one of two register
+    // sets; the step that uses it decodes it into its Delta accumulator.
+    UReg ua[4][NCT], ub[4][NCT];
     f32x4 O[4];
     int64_t t0_prev = 0;
     int len_prev = 0;
@@ -940,7 +1007,7 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     // One chain step on the image in `cur` (Delta accumulates into Dl, which
     // holds the chunk's U), prefetching into `nxt` (the image the previous
     // step read) and `un`.
-    auto step = [&](int chunk, const char *cur, char *nxt, f32x4 (&Dl)[4][NCT], f32x4 (&un)[4][NCT])
+    auto step = [&](int chunk, const char *cur, char *nxt, UReg (&Dcur)[4][NCT], UReg (&un)[4][NCT])
                     __attribute__((always_inline)) {
         // This wave's copies of this chunk and its U have landed (waits in a
         // form the compiler sees, so it adds none of its own for them), then
@@ -956,6 +1023,11 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __builtin_amdgcn_s_barrier();
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        f32x4 Dl[4][NCT];  // Delta = U - W S accumulates onto this chunk's U
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) Dl[rt][ct] = u_decode(Dcur[rt][ct]);
         if constexpr (!PASS_A) {
             if (chunk > cbeg) store_o(O, t0_prev, len_prev, (chunk - 1) & 1);
             if (ep) dma_gate(chunk);
