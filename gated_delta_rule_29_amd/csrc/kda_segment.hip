@@ -106,26 +106,39 @@ __device__ __forceinline__ void split_f16_pair(float a, float b, uint32_t &hi, u
 constexpr int PTT = 68;  // pitch (floats) of T [64][64]
 
 // f(std::integral_constant<int, i>) for i = 0 .. N-1, expanded at compile time.
-// Maximum over one DPP row (16 lanes with equal lane / 16), in every lane.
-__device__ __forceinline__ float row_max16(float x) {
-    x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false)));
-    x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false)));
-    x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false)));
-    x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false)));
+// Unsigned maximum over one DPP row (16 lanes with equal lane / 16), in every lane.
+__device__ __forceinline__ uint32_t row_umax16(uint32_t x) {
+    x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x141, 0xF, 0xF, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x140, 0xF, 0xF, false));
     return x;
+}
+// max |u| over a lane's four values as the bits of a non-negative float: as
+// unsigned integers these order like the values, and NaN orders above inf, so
+// a NaN is kept (fmaxf would drop it).
+__device__ __forceinline__ uint32_t abs_max_bits(f32x4 u) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float x = u[i];  // a value: a bit-cast of the element expression reads element 0
+        m = max(m, __builtin_bit_cast(uint32_t, x) & 0x7FFFFFFFu);
+    }
+    return m;
 }
 
 // U in 16-bit fixed point: each block of 4 rows x 16 columns (one lane group of
 // a C tile) shares a power-of-two scale sc with max|u| / sc < 2^14, so a value
 // is stored to within sc / 2 <= 2^-14 max|u| of the block, and |q| <= 2^14
 // needs no clamp.  Decoding, q * sc, is exact.  A block holding inf or NaN
-// gets that value as its scale and decodes to inf / NaN.
+// gets that value as its scale and q = 0, so all of it decodes to NaN.
 struct UBlk {
     uint32_t q01, q23;
     float sc;
 };
-__device__ __forceinline__ UBlk u_encode(f32x4 u, float bmax) {
-    const uint32_t eb = (__builtin_bit_cast(uint32_t, bmax) >> 23) & 0xFF;  // bmax < 2^(eb - 126)
+__device__ __forceinline__ UBlk u_encode(f32x4 u, uint32_t bmax_bits) {
+    const float bmax = __builtin_bit_cast(float, bmax_bits);
+    const uint32_t eb = bmax_bits >> 23;  // bmax < 2^(eb - 126); 0xFF: inf or NaN
     const uint32_t e2 = max(eb, 14u) - 13;                                   // sc = 2^(e2 - 127)
     const bool fin = eb != 0xFF;
     const float sc = fin ? __builtin_bit_cast(float, e2 << 23) : bmax;
@@ -249,13 +262,17 @@ __device__ inline int seg_find(const int32_t *off, int N, int x) {
 
 constexpr int PEH = 68;  // pitch (floats) of the half-width arrays [64 tokens][64 channels]
 
+template <int GK>
 struct WySmem {
     union {
         float E1[CH * PEH];  // e^{G_t - R_s}, s = sub-chunk of t, one 64-channel half (phases 1-2)
         float T[CH * PTT];   // Akk, then T = (I + Akk)^{-1} (phases 2-4)
     } a;
     float CB[CH * PEH];      // k_t e^{R_{s+1} - G_t}, in [e^-80, 1] |k_t|, same half (phases 1-2)
-    float F[10 * D];         // e^{R_i - R_{j+1}} for j <= i, row i(i+1)/2 + j
+    // K3 gate: e^{R_i - R_{j+1}} for j <= i, row i(i+1)/2 + j.  Softplus decay:
+    // R_s, s = 0..3, as logs (the factors are formed when used, and the smaller
+    // table lets four workgroups share a CU).
+    float F[(GK == GATE_K3 ? 10 : 4) * D];
     float eR[4 * D];         // e^{R_s}
     float beta[CH];
     float nk[CH], nq[CH];    // 1 / |k_t|, 1 / |q_t| (or 1: inputs already unit length)
@@ -275,6 +292,9 @@ static_assert(PTT <= PEH, "T lives in the E1 region");
 #ifndef WY_WPE
 #define WY_WPE 3
 #endif
+#ifndef WY_WPE_SP
+#define WY_WPE_SP 4
+#endif
 // QKN: q and k arrive raw and are normalised to unit length here (the layer's
 // step fused in); a separate instantiation, so the plain path carries none of it.
 // GK: the decay parameterisation.  With the K3 gate every factor of a 16-token
@@ -284,11 +304,11 @@ static_assert(PTT <= PEH, "T lives in the E1 region");
 // without overflow, so those tiles are formed position pair by position pair
 // on the VALU, in the log domain (the cost the K3 bound removes).
 template <bool QKN, int GK>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WY_WPE))) void wy_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GK == GATE_K3 ? WY_WPE : WY_WPE_SP))) void wy_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     const float *__restrict__ z, const float *__restrict__ beta, const float *__restrict__ A, int N, int H,
     SegTable tab) {
-    __shared__ WySmem sm;
+    __shared__ WySmem<GK> sm;
     const int c = (int)(blockIdx.x / (unsigned)H), h = (int)(blockIdx.x % (unsigned)H);
     if (c >= tab.chunk_off[N]) return;
     const int n = seg_find(tab.chunk_off, N, c);
@@ -436,7 +456,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WY_WPE))) v
                 // K * Gam formed here and kept (else the compiler defers it to
                 // phase 4 and spills its inputs instead)
                 {
-                    u32x4 kg = __builtin_bit_cast(u32x4, kga[hf][ks]);
+                    const bf16x8 kv = kga[hf][ks];
+                    u32x4 kg = __builtin_bit_cast(u32x4, kv);
                     __asm__ volatile("" : "+v"(kg));
                     kga[hf][ks] = __builtin_bit_cast(bf16x8, kg);
                 }
@@ -506,7 +527,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WY_WPE))) v
                     const float *cb = &sm.CB[cc * PEH + cl];
                     const f32x4 ca = *(const f32x4 *)cb, cbv = *(const f32x4 *)(cb + 16);
                     F8 xc;
-                    if constexpr (GK == GATE_K3) {
+                    if constexpr (GK == GATE_K3) {  // CB_c e^{R_i - R_{j+1}}
                         const float *fij = &sm.F[(i * (i + 1) / 2 + j) * D + c0];
                         const f32x4 fa = *(const f32x4 *)fij, fb = *(const f32x4 *)(fij + 16);
 #pragma unroll
@@ -701,8 +722,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WY_WPE))) v
                 for (int ks = 0; ks < 2; ++ks)
                     if (ks <= (rt >> 1)) u = mma_s1(u, tb[rt][ks], vb[hf][ks]);
                 {
-                    const float bm = row_max16(fmaxf(fmaxf(fabsf(u[0]), fabsf(u[1])), fmaxf(fabsf(u[2]), fabsf(u[3]))));
-                    const UBlk ub = u_encode(u, bm);
+                    const UBlk ub = u_encode(u, row_umax16(abs_max_bits(u)));
                     *(uint2 *)(blk + BO_U + U_TILE * (8 * rt + ctile) + 8 * l) = make_uint2(ub.q01, ub.q23);
                     if (lr == 0) *(float *)(blk + BO_US + 16 * (8 * rt + ctile) + 4 * g) = ub.sc;
                 }
