@@ -40,7 +40,7 @@ class LayerOpts(ctypes.Structure):
     the decay parameterisation."""
     _fields_ = [("qk_l2norm", ctypes.c_int32), ("qk_eps", ctypes.c_float), ("out_gate", ctypes.c_void_p),
                 ("norm_weight", ctypes.c_void_p), ("norm_eps", ctypes.c_float), ("gate_kind", ctypes.c_int32),
-                ("gate_per_head", ctypes.c_int32)]
+                ("gate_per_head", ctypes.c_int32), ("reverse_order", ctypes.c_int32)]
 
 
 GATES = {"k3": 0, "softplus": 1}  # kda_layer_opts::gate_kind
@@ -228,11 +228,12 @@ def kda_chunk_fwd(q, k, v, g_raw, beta, A, S0=None, cu_seqlens=None, *, o=None, 
 
 
 def kda_decode_step(q, k, v, g_raw, beta, A, S, *, o=None, stream=None, qk_l2norm=False, qk_eps=1e-6,
-                    out_gate=None, norm_weight=None, norm_eps=1e-6, gate="k3"):
+                    out_gate=None, norm_weight=None, norm_eps=1e-6, gate="k3", reverse_order=False):
     """One recurrent step for N sequences: q, k, v [N, H, 128]; g_raw [N, H, 128] (or [N, H]: one
     value per head); beta [N, H]; A [H]; S [N, H, 128, 128] fp32 updated in place.  Returns o
     [N, H, 128] fp32.  qk_l2norm, out_gate, norm_weight, norm_eps, gate: as kda_chunk_fwd
-    (kda_decode_step_layer)."""
+    (kda_decode_step_layer).  reverse_order: visit the (sequence, head) states last to first (same
+    results); alternate it over consecutive steps so each starts with the states still in cache."""
     lib = load()
     N, H, dk = q.shape
     dv = v.shape[-1]
@@ -254,7 +255,7 @@ def kda_decode_step(q, k, v, g_raw, beta, A, S, *, o=None, stream=None, qk_l2nor
         o = torch.empty((N, H, dv), dtype=torch.float32, device=dev)
     dtype = KDA_BF16 if q.dtype == torch.bfloat16 else KDA_F32
     args = (_ptr(q), _ptr(k), _ptr(v), dtype, _ptr(g_raw), _ptr(beta), _ptr(A), _ptr(S), N, H, dk, dv)
-    if qk_l2norm or out_gate is not None or gate != "k3" or per_head:
+    if qk_l2norm or out_gate is not None or gate != "k3" or per_head or reverse_order:
         if out_gate is not None:
             _need(out_gate, "out_gate", (torch.float32,), dev)
             if norm_weight is None:
@@ -264,7 +265,7 @@ def kda_decode_step(q, k, v, g_raw, beta, A, S, *, o=None, stream=None, qk_l2nor
                 raise ValueError("out_gate must be shaped like o and norm_weight must be [128]")
         opts = LayerOpts(int(bool(qk_l2norm)), float(qk_eps), None if out_gate is None else out_gate.data_ptr(),
                          None if norm_weight is None else norm_weight.data_ptr(), float(norm_eps), GATES[gate],
-                         int(per_head))
+                         int(per_head), int(bool(reverse_order)))
         rc = lib.kda_decode_step_layer(*args, ctypes.byref(opts), _ptr(o), _stream(stream))
         _check(rc, "kda_decode_step_layer")
     else:

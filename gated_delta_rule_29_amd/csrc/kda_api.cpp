@@ -86,6 +86,7 @@ int chunk_fwd(const void *q, const void *k, const void *v, kda_dtype qkv_dtype, 
     const float *out_gate = lo ? lo->out_gate : nullptr, *norm_weight = lo ? lo->norm_weight : nullptr;
     if (lo && (!(lo->qk_eps >= 0.f) || !(lo->norm_eps >= 0.f))) return KDA_ERR_SHAPE;  // NaN fails too
     if (lo && lo->gate_kind != KDA_GATE_K3 && lo->gate_kind != KDA_GATE_SOFTPLUS) return KDA_ERR_SHAPE;
+    if (lo && lo->reverse_order != 0) return KDA_ERR_SHAPE;  // a decode option
     const size_t z_row = lo && lo->gate_per_head ? 1 : kD;  // g_raw values per (token, head)
     const int64_t T_total = (int64_t)B * T;
     if (T_total > INT32_MAX - 64 || (int64_t)n_seqs * H > INT32_MAX / 64) return KDA_ERR_SHAPE;
@@ -125,7 +126,8 @@ int chunk_fwd(const void *q, const void *k, const void *v, kda_dtype qkv_dtype, 
     const kda::Ckpt ck{S_ckpt && ckpt_capacity > 0 ? S_ckpt : nullptr, nullptr, (int)(S_ckpt ? ckpt_stride / 64 : 1),
                        ckpt_capacity};
     const kda::Layer ly{lo && lo->qk_l2norm != 0, lo ? lo->qk_eps : 0.f, out_gate, norm_weight,
-                        lo ? lo->norm_eps : 0.f, lo ? lo->gate_kind : KDA_GATE_K3, lo && lo->gate_per_head != 0};
+                        lo ? lo->norm_eps : 0.f, lo ? lo->gate_kind : KDA_GATE_K3, lo && lo->gate_per_head != 0,
+                        false};
     const int rc = kda::launch_prefill(q, k, v, qkv_dtype == KDA_F32, g_raw, beta, A, S0, cu_seqlens, B, T, H,
                                        n_seqs, o, S_final, ck, ly, workspace, (hipStream_t)stream,
                                        (hipEvent_t *)stage_events);
@@ -204,7 +206,8 @@ int decode_step(const void *q, const void *k, const void *v, kda_dtype qkv_dtype
         overlap(o, o_bytes, norm_weight, (size_t)kD * 4))
         return KDA_ERR_ALIAS;
     const kda::Layer ly{lo && lo->qk_l2norm != 0, lo ? lo->qk_eps : 0.f, out_gate, norm_weight,
-                        lo ? lo->norm_eps : 0.f, lo ? lo->gate_kind : KDA_GATE_K3, lo && lo->gate_per_head != 0};
+                        lo ? lo->norm_eps : 0.f, lo ? lo->gate_kind : KDA_GATE_K3, lo && lo->gate_per_head != 0,
+                        lo && lo->reverse_order != 0};
     const int rc = kda::launch_decode(q, k, v, qkv_dtype == KDA_F32, g_raw, beta, A, S, N, H, o, ly,
                                       (hipStream_t)stream);
     return rc == 0 ? KDA_OK : KDA_ERR_HIP;

@@ -53,6 +53,7 @@ struct Layer {
     float norm_eps;
     int gate_kind;        // GATE_K3 or GATE_SOFTPLUS
     bool gate_per_head;   // z is [tokens, H]: one gate value per (token, head)
+    bool reverse_order;   // decode: visit (sequence, head) pairs last to first
 };
 
 __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {

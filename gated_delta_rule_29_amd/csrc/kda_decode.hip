@@ -22,7 +22,9 @@ __global__ __launch_bounds__(256) void decode_kernel(const IO *__restrict__ q, c
                                                      const float *__restrict__ beta,
                                                      const float *__restrict__ A, float *__restrict__ S,
                                                      int H, float *__restrict__ o, Layer ly) {
-    const int nh = blockIdx.x;  // n * H + h
+    // n * H + h; in reverse order the sweep starts with the states that a
+    // forward step before it wrote last (still in the last-level cache)
+    const int nh = ly.reverse_order ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x;
     const int h = nh % H;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
     const int cg = l & 31, rp = l >> 5;

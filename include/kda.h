@@ -198,6 +198,14 @@ int kda_chunk_fwd_ckpt(const void *q, const void *k, const void *v, kda_dtype qk
  *                applied to all 128 key channels (the scalar per-head gate of
  *                Gated DeltaNet that KDA refines channel-wise, Kimi Linear
  *                summary, section 3).  Zero: g_raw is [tokens, H, 128].
+ *   reverse_order  decode only (the prefill rejects nonzero with
+ *                KDA_ERR_SHAPE): nonzero visits the (sequence, head) states
+ *                last to first.  The results are the same bits either way.
+ *                A caller running consecutive steps over the same states
+ *                alternates it, so that each step starts with the states the
+ *                step before wrote last, which are still in the GPU's
+ *                last-level cache (the states of 256 x 32 heads are 512 MiB
+ *                against a 256 MB cache).
  */
 enum { KDA_GATE_K3 = 0, KDA_GATE_SOFTPLUS = 1 };
 typedef struct kda_layer_opts {
@@ -208,6 +216,7 @@ typedef struct kda_layer_opts {
     float norm_eps;
     int32_t gate_kind;
     int32_t gate_per_head;
+    int32_t reverse_order;
 } kda_layer_opts;
 /*
  * kda_chunk_fwd with the layer's steps fused in (opts, NULL gives KDA_ERR_NULL)

@@ -158,6 +158,8 @@ def test_prefill_gate_options_are_checked():
     assert call_prefill_layer(prefill_args(o=fake(4, 2048)), Opts(0, 0.0, None, None, 0.0, 1, 0)) == ALIAS
     assert call_prefill_layer(prefill_args(o=fake(4, 512)), Opts(0, 0.0, None, None, 0.0, 1, 1)) == ALIAS
     assert call_prefill_layer(prefill_args(B=0, N=0, T=0), Opts(0, 0.0, gate, w, 0.0, 1, 1)) == OK
+    # reverse_order is a decode option
+    assert call_prefill_layer(prefill_args(B=0, N=0, T=0), Opts(0, 0.0, None, None, 0.0, 0, 0, 1)) == SHAPE
 
 
 def test_ckpt_count():

@@ -211,6 +211,20 @@ def test_decode_variants(io, gate, per_head, steep, layer):
     assert eo <= TOL[io] and es <= TOL[io], (eo, es)
 
 
+def test_decode_reverse_order_gives_the_same_bits():
+    """Visiting the (sequence, head) states last to first changes only the order of work."""
+    d = decode_inputs(5460, "bf16", N=9, H=5)
+    q, k, v = (to_dev(d[n], torch.bfloat16) for n in ("q", "k", "v"))
+    z, beta, A = (to_dev(d[n], torch.float32) for n in ("z", "beta", "A"))
+    S1, S2 = to_dev(d["S"], torch.float32), to_dev(d["S"], torch.float32)
+    say("case decode reverse order")
+    for step in range(3):
+        o1 = kda.kda_decode_step(q, k, v, z, beta, A, S1)
+        o2 = kda.kda_decode_step(q, k, v, z, beta, A, S2, reverse_order=bool(step % 2 == 0))
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(S1, S2), step
+
+
 def test_decode_plain_options_are_the_plain_step():
     """kda_decode_step_layer with every option off gives the bits of kda_decode_step."""
     d = decode_inputs(5450, "bf16")
