@@ -293,7 +293,7 @@ static_assert(PTT <= PEH, "T lives in the E1 region");
 #define WY_WPE 3
 #endif
 #ifndef WY_WPE_SP
-#define WY_WPE_SP 4
+#define WY_WPE_SP 3
 #endif
 // QKN: q and k arrive raw and are normalised to unit length here (the layer's
 // step fused in); a separate instantiation, so the plain path carries none of it.
@@ -345,9 +345,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GK == GATE_
     f32x4 a1[4], a2[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) a1[j] = a2[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Phase-1 inputs of one half, as loaded: z and k of channel 64 hf + 16 w + lr
+    // at the eight tokens of each token block ks.
+    uint32_t zin[2][8];
+    uint16_t kin[2][8];
+    auto load_half = [&](int hf) __attribute__((always_inline)) {
+        const int ch = 64 * hf + 16 * w + lr;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int tl = 4 * g + (e & 3), tu = 32 * ks + 16 * (e >> 2);  // row = tu (scalar) + tl
+                zin[ks][e] = __builtin_amdgcn_raw_buffer_load_b32(rz, tl * pz + zcs * ch, tu * pz, 0);
+                kin[ks][e] = __builtin_amdgcn_raw_buffer_load_b16(rk, tl * ph + 2 * ch, tu * ph, 0);
+            }
+    };
+    // (Issuing the second half's loads during the first half's Gram phase was
+    // slower: 0.62 against 0.57 ms at 64K x 16.)
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
         if (hf) __syncthreads();  // the Gram half before is done with E1 and CB
+        load_half(hf);
         __builtin_amdgcn_sched_barrier(0);
         const int ch = 64 * hf + 16 * w + lr, chl = 16 * w + lr;
         float Rs[5], eRs[4];
@@ -358,13 +376,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GK == GATE_
             for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const int tl = 4 * g + (e & 3), tu = 32 * ks + 16 * (e >> 2);  // row = tu (scalar) + tl
+                    const int tl = 4 * g + (e & 3), tu = 32 * ks + 16 * (e >> 2);
                     const bool ok = tu + tl < len;
-                    const float zv = __builtin_bit_cast(
-                        float, __builtin_amdgcn_raw_buffer_load_b32(rz, tl * pz + zcs * ch, tu * pz, 0));
-                    const uint16_t kv = __builtin_amdgcn_raw_buffer_load_b16(rk, tl * ph + 2 * ch, tu * ph, 0);
-                    gv[ks][e] = gate_of<GK>(eA, ok ? zv : -__builtin_inff());  // z = -inf gives g = 0
-                    kb[ks][e] = __builtin_bit_cast(__bf16, kv);
+                    const uint32_t zu = zin[ks][e];
+                    const uint16_t ku = kin[ks][e];
+                    gv[ks][e] = gate_of<GK>(eA, ok ? __builtin_bit_cast(float, zu) : -__builtin_inff());  // -inf: g = 0
+                    kb[ks][e] = __builtin_bit_cast(__bf16, ku);
                 }
             // ---- phase 0 (QKN, first half only): the inverse L2 norms of the
             // chunk's key and query rows (wave w: rows 16 w .. 16 w + 15, four
@@ -550,33 +567,85 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GK == GATE_
                     a1[j] = mma_ss(a1[j], cs, rks);
                     a2[j] = mma_ss(a2[j], cs, rqs);
                 }
-            }
-            if constexpr (GK != GATE_K3) {
-                // Diagonal tile, position pair by position pair: lane (lr, g) forms
-                // its four pairs (r, c = 16 i + 4 g + m) over this half's 64
-                // channels, sum_ch k_r k_c e^{L_r - L_c} (and q_r), L = G - R_i
-                // from LDS; the exponent is clamped at 0 (c > r is masked later).
-                const float *rowl = &sm.a.E1[r * PEH], *rowk = &sm.CB[r * PEH];
-                const float *coll = &sm.a.E1[(16 * i + 4 * g) * PEH], *colk = &sm.CB[(16 * i + 4 * g) * PEH];
-                f32x4 ak = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-                for (int cg = 0; cg < 64; cg += 4) {
-                    const f32x4 l4 = *(const f32x4 *)(rowl + cg), k4 = *(const f32x4 *)(rowk + cg);
-                    const bf16x4 qv = ld_bf16x4(rq, r * (int)ph + 2 * (64 * hf + cg));
+                if constexpr (GK != GATE_K3) {
+                    // Diagonal tile, pairs in different 4-token micro-blocks: for
+                    // rows of micro-block m (chain m = 1..3) both factors are
+                    // referenced to P_m = L at the token before that block,
+                    // x_r e^{L_r - P_m} <= 1 and k_c e^{P_m - L_c} <= 1 for the
+                    // columns of earlier micro-blocks.  Rows outside block m and
+                    // columns from block m on enter chain m as zeros, so the three
+                    // chains add up in one accumulator.
+                    const int mr = lr >> 2;  // micro-block of this lane's row (B side) and column (A side)
+                    const float *rowP = &sm.a.E1[(16 * i + 4 * max(mr, 1) - 1) * PEH + cl];
+                    const f32x4 pr0 = *(const f32x4 *)rowP, pr1 = *(const f32x4 *)(rowP + 16);
+                    F8 yk, yq;
 #pragma unroll
                     for (int m = 0; m < 4; ++m) {
-                        const f32x4 lc = *(const f32x4 *)(coll + m * PEH + cg);
-                        const f32x4 kc = *(const f32x4 *)(colk + m * PEH + cg);
+                        const float fa = mr ? __expf(la[m] - pr0[m]) : 0.f, fb = mr ? __expf(lb[m] - pr1[m]) : 0.f;
+                        yk.v[m] = (QKN ? (float)k0[m] * nkr : (float)k0[m]) * fa;
+                        yk.v[4 + m] = (QKN ? (float)k1[m] * nkr : (float)k1[m]) * fb;
+                        yq.v[m] = (QKN ? (float)q0[m] * nqr : (float)q0[m]) * fa;
+                        yq.v[4 + m] = (QKN ? (float)q1[m] * nqr : (float)q1[m]) * fb;
+                    }
+                    const S8 yks = split8(yk), yqs = split8(yq);
+                    const S8 zero = {};
+                    const int cc = 16 * i + lr;
+                    const f32x4 kc0 = *(const f32x4 *)&sm.CB[cc * PEH + cl], kc1 = *(const f32x4 *)&sm.CB[cc * PEH + cl + 16];
+                    const f32x4 lc0 = *(const f32x4 *)&sm.a.E1[cc * PEH + cl];
+                    const f32x4 lc1 = *(const f32x4 *)&sm.a.E1[cc * PEH + cl + 16];
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const float f = kc[e] * __expf(fminf(l4[e] - lc[e], 0.f));
-                            ak[m] += k4[e] * f;
-                            aq[m] += (QKN ? (float)qv[e] * nqr : (float)qv[e]) * f;
+                    for (int mb = 1; mb < 4; ++mb) {
+                        const float *pm = &sm.a.E1[(16 * i + 4 * mb - 1) * PEH + cl];
+                        const f32x4 p0 = *(const f32x4 *)pm, p1 = *(const f32x4 *)(pm + 16);
+                        const bool colin = mr < mb;
+                        F8 xc;
+#pragma unroll
+                        for (int m = 0; m < 4; ++m) {
+                            xc.v[m] = colin ? kc0[m] * __expf(p0[m] - lc0[m]) : 0.f;
+                            xc.v[4 + m] = colin ? kc1[m] * __expf(p1[m] - lc1[m]) : 0.f;
                         }
+                        const S8 cs = split8(xc);
+                        const bool rowin = mr == mb;
+                        a1[i] = mma_ss(a1[i], cs, rowin ? yks : zero);
+                        a2[i] = mma_ss(a2[i], cs, rowin ? yqs : zero);
                     }
                 }
-                a1[i] += ak;
-                a2[i] += aq;
+            }
+            if constexpr (GK != GATE_K3) {
+                // Diagonal tile, pairs inside a micro-block, position pair by
+                // position pair over this half's 64 channels: lane p forms pair
+                // (row 16 i + p / 4, column of the same micro-block 4 (p / 16) + p % 4),
+                // sum_ch x_r k_c e^{min(L_r - L_c, 0)} (c > r is masked later), then
+                // hands it to the lane that holds that (row, column) of the tile.
+                const int prow = 16 * i + (l >> 2), pcol = 16 * i + 4 * (l >> 4) + (l & 3);
+                const float *rowl = &sm.a.E1[prow * PEH], *rowk = &sm.CB[prow * PEH];
+                const float *coll = &sm.a.E1[pcol * PEH], *colk = &sm.CB[pcol * PEH];
+                const float nqp = QKN ? sm.nq[prow] : 1.f;
+                float sk = 0.f, sq = 0.f;
+#pragma unroll 4
+                for (int cg = 0; cg < 64; cg += 4) {
+                    const f32x4 l4 = *(const f32x4 *)(rowl + cg), k4 = *(const f32x4 *)(rowk + cg);
+                    const f32x4 lc = *(const f32x4 *)(coll + cg), kc = *(const f32x4 *)(colk + cg);
+                    const bf16x4 qv = ld_bf16x4(rq, prow * (int)ph + 2 * (64 * hf + cg));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float f = kc[e] * __expf(fminf(l4[e] - lc[e], 0.f));
+                        sk += k4[e] * f;
+                        sq += (float)qv[e] * f;
+                    }
+                }
+                sq *= nqp;
+                // lane (lr, g) holds columns 16 i + 4 g + m of row 16 i + lr: pair 4 lr + m
+                // when g is the row's micro-block
+                const bool own = g == (lr >> 2);
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int src = 4 * (4 * lr + m);
+                    const float vk = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, sk)));
+                    const float vq = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, sq)));
+                    a1[i][m] += own ? vk : 0.f;
+                    a2[i][m] += own ? vq : 0.f;
+                }
             }
         }
     }
