@@ -25,6 +25,8 @@ Functions and what pins them (tests/test_oracle_pins.py):
 * ``recurrent_g``     the recurrence with given log-decays: equals ``recurrent``
                       with the K3 gate, the beta = 0 closed form;
 * ``softplus_gate``   the unbounded decay: softplus closed values and limits;
+* ``lowrank_z``       the forget gate's pre-activation from its low-rank
+                      projection: one-hot and separable inputs;
 * ``l2_normalize``, ``gated_rmsnorm``  the KDA layer's steps around the operator:
                       Pythagorean triples, constant vectors, the logistic
                       function's closed values and limits;
@@ -298,3 +300,15 @@ def gated_rmsnorm(o, gate, weight, eps: float = 1e-6):
     g = np.asarray(gate, dtype=np.float64)
     r = 1.0 / np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps)
     return o * r * np.asarray(weight, dtype=np.float64) * (1.0 / (1.0 + np.exp(-g)))
+
+
+def lowrank_z(u, W):
+    """The forget gate's pre-activation from its low-rank projection (Kimi Linear summary,
+    section 4: the forget and output gates use low-rank projections).  Reading: the second
+    factor of the projection maps a rank-r vector per token, shared by all heads, to every
+    head's 128 key channels: z[t, h, c] = sum_j u[t, j] * W[h, c, j], in float64.
+    u: [T, r]; W: [H, 128, r].  Returns z: [T, H, 128]."""
+    u = np.asarray(u, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    H, dk, r = W.shape
+    return (u @ W.reshape(H * dk, r).T).reshape(u.shape[0], H, dk)
