@@ -40,7 +40,22 @@ class LayerOpts(ctypes.Structure):
     the decay parameterisation."""
     _fields_ = [("qk_l2norm", ctypes.c_int32), ("qk_eps", ctypes.c_float), ("out_gate", ctypes.c_void_p),
                 ("norm_weight", ctypes.c_void_p), ("norm_eps", ctypes.c_float), ("gate_kind", ctypes.c_int32),
-                ("gate_per_head", ctypes.c_int32), ("reverse_order", ctypes.c_int32)]
+                ("gate_per_head", ctypes.c_int32), ("reverse_order", ctypes.c_int32), ("gate_u", ctypes.c_void_p),
+                ("gate_w", ctypes.c_void_p), ("gate_rank", ctypes.c_int32)]
+
+
+def _lowrank(gate_u, gate_w, rows, H, dev):
+    """Check the low-rank forget gate factors: gate_u [rows, r] and gate_w [H, 128, r], bf16."""
+    if gate_u is None and gate_w is None:
+        return None, None, 0
+    if gate_u is None or gate_w is None:
+        raise ValueError("gate_u and gate_w go together")
+    _need(gate_u, "gate_u", (torch.bfloat16,), dev)
+    _need(gate_w, "gate_w", (torch.bfloat16,), dev)
+    r = gate_u.shape[-1]
+    if gate_u.numel() != rows * r or gate_w.shape != (H, HEAD_DIM, r):
+        raise ValueError(f"gate_u must be [{rows}, r] and gate_w [{H}, {HEAD_DIM}, r]")
+    return gate_u.data_ptr(), gate_w.data_ptr(), int(r)
 
 
 GATES = {"k3": 0, "softplus": 1}  # kda_layer_opts::gate_kind
@@ -127,7 +142,7 @@ def ckpt_count(lengths, stride: int) -> int:
 def kda_chunk_fwd(q, k, v, g_raw, beta, A, S0=None, cu_seqlens=None, *, o=None, S_final=None,
                   workspace=None, stream=None, return_final_state=True, stage_events=None,
                   S_ckpt=None, ckpt_stride=0, qk_l2norm=False, qk_eps=1e-6, out_gate=None, norm_weight=None,
-                  norm_eps=1e-6, gate="k3"):
+                  norm_eps=1e-6, gate="k3", gate_u=None, gate_w=None):
     """Chunkwise KDA prefill.
 
     q, k, v: [B, T, H, 128] (or [T, H, 128]) bf16 or fp32; g_raw: same shape fp32 (the gate's z);
@@ -143,11 +158,17 @@ def kda_chunk_fwd(q, k, v, g_raw, beta, A, S0=None, cu_seqlens=None, *, o=None, 
     sigmoid(out_gate) (out_gate: fp32, shaped like o; norm_weight: fp32 [128]).
     gate: "k3" (g = -5 Sigmoid(e^A z)) or "softplus" (g = -e^A softplus(z), unbounded); g_raw shaped
     [B, T, H] (or [T, H]) gives one gate value per (token, head) for all 128 channels.
+    gate_u, gate_w: the forget gate's low-rank projection fused in, z[t, h, c] = sum_j gate_u[t, j]
+    gate_w[h, c, j] (bf16, [tokens, r] and [H, 128, r], r a multiple of 32 up to 256); g_raw is then
+    ignored and may be None.
     """
     lib = load()
     squeeze = q.dim() == 3
+    if g_raw is None and gate_u is None:
+        raise ValueError("g_raw is required without gate_u / gate_w")
     if squeeze:
-        q, k, v, g_raw, beta = (x.unsqueeze(0) for x in (q, k, v, g_raw, beta))
+        q, k, v, beta = (x.unsqueeze(0) for x in (q, k, v, beta))
+        g_raw = None if g_raw is None else g_raw.unsqueeze(0)
     if q.dim() != 4:
         raise ValueError("q must be [B, T, H, 128] or [T, H, 128]")
     B, T, H, dk = q.shape
@@ -157,12 +178,16 @@ def kda_chunk_fwd(q, k, v, g_raw, beta, A, S0=None, cu_seqlens=None, *, o=None, 
     _need(q, "q", io, dev)
     _need(k, "k", (q.dtype,), dev)
     _need(v, "v", (q.dtype,), dev)
-    _need(g_raw, "g_raw", (torch.float32,), dev)
+    lr_u, lr_w, lr_r = _lowrank(gate_u, gate_w, B * T, H, dev)
+    if lr_u is not None:
+        g_raw, per_head = None, False
+    else:
+        _need(g_raw, "g_raw", (torch.float32,), dev)
+        per_head = g_raw.shape == q.shape[:3]
     _need(beta, "beta", (torch.float32,), dev)
     _need(A, "A", (torch.float32,), dev)
-    per_head = g_raw.shape == q.shape[:3]
-    if k.shape != q.shape or (g_raw.shape != q.shape and not per_head) or v.shape[:3] != q.shape[:3] \
-            or beta.shape != (B, T, H):
+    if k.shape != q.shape or (g_raw is not None and g_raw.shape != q.shape and not per_head) \
+            or v.shape[:3] != q.shape[:3] or beta.shape != (B, T, H):
         raise ValueError("inconsistent shapes")
     if gate not in GATES:
         raise ValueError(f"gate must be one of {sorted(GATES)}")
@@ -190,7 +215,7 @@ def kda_chunk_fwd(q, k, v, g_raw, beta, A, S0=None, cu_seqlens=None, *, o=None, 
     args = (_ptr(q), _ptr(k), _ptr(v), dtype, _ptr(g_raw), _ptr(beta), _ptr(A), _ptr(S0),
             _ptr(cu_seqlens), B, T, H, N, dk, dv, _ptr(o), _ptr(S_final), _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream(stream))
-    layer = qk_l2norm or out_gate is not None or gate != "k3" or per_head
+    layer = qk_l2norm or out_gate is not None or gate != "k3" or per_head or lr_u is not None
     if S_ckpt is not None:
         _need(S_ckpt, "S_ckpt", (torch.float32,), dev)
         if S_ckpt.dim() != 4 or S_ckpt.shape[1:] != (H, dk, dv):
@@ -207,7 +232,7 @@ def kda_chunk_fwd(q, k, v, g_raw, beta, A, S0=None, cu_seqlens=None, *, o=None, 
                 raise ValueError("out_gate must be shaped like o and norm_weight must be [128]")
         opts = LayerOpts(int(bool(qk_l2norm)), float(qk_eps), None if out_gate is None else out_gate.data_ptr(),
                          None if norm_weight is None else norm_weight.data_ptr(), float(norm_eps), GATES[gate],
-                         int(per_head))
+                         int(per_head), 0, lr_u, lr_w, lr_r)
         ck = (_ptr(S_ckpt), int(ckpt_stride), S_ckpt.shape[0]) if S_ckpt is not None else (None, 0, 0)
         rc = lib.kda_chunk_fwd_layer(*args[:15], ctypes.byref(opts), args[15], args[16], *ck, *args[17:])
         _check(rc, "kda_chunk_fwd_layer")
@@ -228,12 +253,14 @@ def kda_chunk_fwd(q, k, v, g_raw, beta, A, S0=None, cu_seqlens=None, *, o=None, 
 
 
 def kda_decode_step(q, k, v, g_raw, beta, A, S, *, o=None, stream=None, qk_l2norm=False, qk_eps=1e-6,
-                    out_gate=None, norm_weight=None, norm_eps=1e-6, gate="k3", reverse_order=False):
+                    out_gate=None, norm_weight=None, norm_eps=1e-6, gate="k3", reverse_order=False, gate_u=None,
+                    gate_w=None):
     """One recurrent step for N sequences: q, k, v [N, H, 128]; g_raw [N, H, 128] (or [N, H]: one
     value per head); beta [N, H]; A [H]; S [N, H, 128, 128] fp32 updated in place.  Returns o
     [N, H, 128] fp32.  qk_l2norm, out_gate, norm_weight, norm_eps, gate: as kda_chunk_fwd
     (kda_decode_step_layer).  reverse_order: visit the (sequence, head) states last to first (same
-    results); alternate it over consecutive steps so each starts with the states still in cache."""
+    results); alternate it over consecutive steps so each starts with the states still in cache.
+    gate_u [N, r], gate_w [H, 128, r]: the low-rank forget gate, as kda_chunk_fwd (g_raw may be None)."""
     lib = load()
     N, H, dk = q.shape
     dv = v.shape[-1]
@@ -241,13 +268,19 @@ def kda_decode_step(q, k, v, g_raw, beta, A, S, *, o=None, stream=None, qk_l2nor
     _need(q, "q", (torch.bfloat16, torch.float32), dev)
     _need(k, "k", (q.dtype,), dev)
     _need(v, "v", (q.dtype,), dev)
-    _need(g_raw, "g_raw", (torch.float32,), dev)
+    lr_u, lr_w, lr_r = _lowrank(gate_u, gate_w, N, H, dev)
+    if lr_u is not None:
+        g_raw, per_head = None, False
+    else:
+        if g_raw is None:
+            raise ValueError("g_raw is required without gate_u / gate_w")
+        _need(g_raw, "g_raw", (torch.float32,), dev)
+        per_head = g_raw.shape == (N, H)
     _need(beta, "beta", (torch.float32,), dev)
     _need(A, "A", (torch.float32,), dev)
     _need(S, "S", (torch.float32,), dev)
-    per_head = g_raw.shape == (N, H)
-    if k.shape != q.shape or (g_raw.shape != q.shape and not per_head) or beta.shape != (N, H) \
-            or S.shape != (N, H, dk, dv):
+    if k.shape != q.shape or (g_raw is not None and g_raw.shape != q.shape and not per_head) \
+            or beta.shape != (N, H) or S.shape != (N, H, dk, dv):
         raise ValueError("inconsistent shapes")
     if gate not in GATES:
         raise ValueError(f"gate must be one of {sorted(GATES)}")
@@ -255,7 +288,7 @@ def kda_decode_step(q, k, v, g_raw, beta, A, S, *, o=None, stream=None, qk_l2nor
         o = torch.empty((N, H, dv), dtype=torch.float32, device=dev)
     dtype = KDA_BF16 if q.dtype == torch.bfloat16 else KDA_F32
     args = (_ptr(q), _ptr(k), _ptr(v), dtype, _ptr(g_raw), _ptr(beta), _ptr(A), _ptr(S), N, H, dk, dv)
-    if qk_l2norm or out_gate is not None or gate != "k3" or per_head or reverse_order:
+    if qk_l2norm or out_gate is not None or gate != "k3" or per_head or reverse_order or lr_u is not None:
         if out_gate is not None:
             _need(out_gate, "out_gate", (torch.float32,), dev)
             if norm_weight is None:
@@ -265,7 +298,7 @@ def kda_decode_step(q, k, v, g_raw, beta, A, S, *, o=None, stream=None, qk_l2nor
                 raise ValueError("out_gate must be shaped like o and norm_weight must be [128]")
         opts = LayerOpts(int(bool(qk_l2norm)), float(qk_eps), None if out_gate is None else out_gate.data_ptr(),
                          None if norm_weight is None else norm_weight.data_ptr(), float(norm_eps), GATES[gate],
-                         int(per_head), int(bool(reverse_order)))
+                         int(per_head), int(bool(reverse_order)), lr_u, lr_w, lr_r)
         rc = lib.kda_decode_step_layer(*args, ctypes.byref(opts), _ptr(o), _stream(stream))
         _check(rc, "kda_decode_step_layer")
     else:

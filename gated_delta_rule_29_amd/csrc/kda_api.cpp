@@ -87,16 +87,21 @@ int chunk_fwd(const void *q, const void *k, const void *v, kda_dtype qkv_dtype, 
     if (lo && (!(lo->qk_eps >= 0.f) || !(lo->norm_eps >= 0.f))) return KDA_ERR_SHAPE;  // NaN fails too
     if (lo && lo->gate_kind != KDA_GATE_K3 && lo->gate_kind != KDA_GATE_SOFTPLUS) return KDA_ERR_SHAPE;
     if (lo && lo->reverse_order != 0) return KDA_ERR_SHAPE;  // a decode option
-    const size_t z_row = lo && lo->gate_per_head ? 1 : kD;  // g_raw values per (token, head)
+    const bool lrz = lo && lo->gate_u;
+    if (lrz && (lo->gate_rank < 32 || lo->gate_rank > 256 || lo->gate_rank % 32 != 0 || lo->gate_per_head))
+        return KDA_ERR_SHAPE;
+    const size_t z_row = lrz ? 0 : (lo && lo->gate_per_head ? 1 : kD);  // g_raw values per (token, head)
     const int64_t T_total = (int64_t)B * T;
     if (T_total > INT32_MAX - 64 || (int64_t)n_seqs * H > INT32_MAX / 64) return KDA_ERR_SHAPE;
     if (S_ckpt && ckpt_capacity > (int64_t)(SIZE_MAX / 2) / ((int64_t)(H > 0 ? H : 1) * kD * kD * 4))
         return KDA_ERR_SHAPE;
     if (n_seqs == 0 || H == 0) return KDA_OK;  // nothing to compute
     if (!A) return KDA_ERR_NULL;
-    if (T_total > 0 && (!q || !k || !v || !g_raw || !beta || !o)) return KDA_ERR_NULL;
+    if (T_total > 0 && (!q || !k || !v || (!g_raw && !lrz) || !beta || !o)) return KDA_ERR_NULL;
     if (out_gate && !norm_weight) return KDA_ERR_NULL;
-    const void *ptrs[] = {q, k, v, g_raw, beta, A, S0, o, S_final, workspace, S_ckpt, out_gate, norm_weight};
+    if (lrz && !lo->gate_w) return KDA_ERR_NULL;
+    const void *gu = lrz ? lo->gate_u : nullptr, *gw = lrz ? lo->gate_w : nullptr;
+    const void *ptrs[] = {q, k, v, g_raw, beta, A, S0, o, S_final, workspace, S_ckpt, out_gate, norm_weight, gu, gw};
     for (const void *p : ptrs)
         if (misaligned(p)) return KDA_ERR_ALIGN;
     const size_t need = kda_chunk_fwd_workspace_bytes(T_total, n_seqs, H, qkv_dtype);
@@ -110,7 +115,9 @@ int chunk_fwd(const void *q, const void *k, const void *v, kda_dtype qkv_dtype, 
         overlap(o, o_bytes, beta, tok * 4) || overlap(o, o_bytes, A, (size_t)H * 4) ||
         overlap(o, o_bytes, S0, st_bytes) || overlap(o, o_bytes, S_final, st_bytes) ||
         overlap(o, o_bytes, workspace, need) || overlap(o, o_bytes, out_gate, o_bytes) ||
-        overlap(o, o_bytes, norm_weight, (size_t)kD * 4))
+        overlap(o, o_bytes, norm_weight, (size_t)kD * 4) ||
+        (lrz && (overlap(o, o_bytes, gu, (size_t)T_total * lo->gate_rank * 2) ||
+                 overlap(o, o_bytes, gw, (size_t)H * kD * lo->gate_rank * 2))))
         return KDA_ERR_ALIAS;
     if (S_ckpt) {
         const size_t ck_bytes = (size_t)ckpt_capacity * H * kD * kD * 4;
@@ -127,7 +134,7 @@ int chunk_fwd(const void *q, const void *k, const void *v, kda_dtype qkv_dtype, 
                        ckpt_capacity};
     const kda::Layer ly{lo && lo->qk_l2norm != 0, lo ? lo->qk_eps : 0.f, out_gate, norm_weight,
                         lo ? lo->norm_eps : 0.f, lo ? lo->gate_kind : KDA_GATE_K3, lo && lo->gate_per_head != 0,
-                        false};
+                        false, (const __bf16 *)gu, (const __bf16 *)gw, lrz ? lo->gate_rank : 0};
     const int rc = kda::launch_prefill(q, k, v, qkv_dtype == KDA_F32, g_raw, beta, A, S0, cu_seqlens, B, T, H,
                                        n_seqs, o, S_final, ck, ly, workspace, (hipStream_t)stream,
                                        (hipEvent_t *)stage_events);
@@ -188,18 +195,25 @@ int decode_step(const void *q, const void *k, const void *v, kda_dtype qkv_dtype
     if ((int64_t)N * H > INT32_MAX) return KDA_ERR_SHAPE;
     if (lo && (!(lo->qk_eps >= 0.f) || !(lo->norm_eps >= 0.f))) return KDA_ERR_SHAPE;  // NaN fails too
     if (lo && lo->gate_kind != KDA_GATE_K3 && lo->gate_kind != KDA_GATE_SOFTPLUS) return KDA_ERR_SHAPE;
+    const bool lrz = lo && lo->gate_u;
+    if (lrz && (lo->gate_rank < 32 || lo->gate_rank > 256 || lo->gate_rank % 32 != 0 || lo->gate_per_head))
+        return KDA_ERR_SHAPE;
     if (N == 0 || H == 0) return KDA_OK;
-    if (!q || !k || !v || !g_raw || !beta || !A || !S || !o) return KDA_ERR_NULL;
+    if (!q || !k || !v || (!g_raw && !lrz) || !beta || !A || !S || !o) return KDA_ERR_NULL;
     const float *out_gate = lo ? lo->out_gate : nullptr, *norm_weight = lo ? lo->norm_weight : nullptr;
     if (out_gate && !norm_weight) return KDA_ERR_NULL;
-    const void *ptrs[] = {q, k, v, g_raw, beta, A, S, o, out_gate, norm_weight};
+    if (lrz && !lo->gate_w) return KDA_ERR_NULL;
+    const void *gu = lrz ? lo->gate_u : nullptr, *gw = lrz ? lo->gate_w : nullptr;
+    const void *ptrs[] = {q, k, v, g_raw, beta, A, S, o, out_gate, norm_weight, gu, gw};
     for (const void *p : ptrs)
         if (misaligned(p)) return KDA_ERR_ALIGN;
     const size_t esz = qkv_dtype == KDA_F32 ? 4 : 2;
     const size_t nh = (size_t)N * H;
     const size_t o_bytes = nh * kD * 4;
-    const size_t z_row = lo && lo->gate_per_head ? 1 : kD;
-    if (overlap(o, o_bytes, S, nh * kD * kD * 4) || overlap(o, o_bytes, q, nh * kD * esz) ||
+    const size_t z_row = lrz ? 0 : (lo && lo->gate_per_head ? 1 : kD);
+    if ((lrz && (overlap(o, o_bytes, gu, (size_t)N * lo->gate_rank * 2) ||
+                 overlap(o, o_bytes, gw, (size_t)H * kD * lo->gate_rank * 2))) ||
+        overlap(o, o_bytes, S, nh * kD * kD * 4) || overlap(o, o_bytes, q, nh * kD * esz) ||
         overlap(o, o_bytes, k, nh * kD * esz) || overlap(o, o_bytes, v, nh * kD * esz) ||
         overlap(o, o_bytes, g_raw, nh * z_row * 4) || overlap(o, o_bytes, beta, nh * 4) ||
         overlap(o, o_bytes, A, (size_t)H * 4) || overlap(o, o_bytes, out_gate, o_bytes) ||
@@ -207,7 +221,7 @@ int decode_step(const void *q, const void *k, const void *v, kda_dtype qkv_dtype
         return KDA_ERR_ALIAS;
     const kda::Layer ly{lo && lo->qk_l2norm != 0, lo ? lo->qk_eps : 0.f, out_gate, norm_weight,
                         lo ? lo->norm_eps : 0.f, lo ? lo->gate_kind : KDA_GATE_K3, lo && lo->gate_per_head != 0,
-                        lo && lo->reverse_order != 0};
+                        lo && lo->reverse_order != 0, (const __bf16 *)gu, (const __bf16 *)gw, lrz ? lo->gate_rank : 0};
     const int rc = kda::launch_decode(q, k, v, qkv_dtype == KDA_F32, g_raw, beta, A, S, N, H, o, ly,
                                       (hipStream_t)stream);
     return rc == 0 ? KDA_OK : KDA_ERR_HIP;

@@ -54,6 +54,10 @@ struct Layer {
     int gate_kind;        // GATE_K3 or GATE_SOFTPLUS
     bool gate_per_head;   // z is [tokens, H]: one gate value per (token, head)
     bool reverse_order;   // decode: visit (sequence, head) pairs last to first
+    // Low-rank forget gate: z[t, h, c] = sum_j zu[t, j] zw[h, c, j] (zu == nullptr: z is given).
+    const __bf16 *zu;     // [tokens, zrank]
+    const __bf16 *zw;     // [H, 128, zrank]
+    int zrank;            // a multiple of 32, at most 256
 };
 
 __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {

@@ -46,7 +46,16 @@ __global__ __launch_bounds__(256) void decode_kernel(const IO *__restrict__ q, c
     const size_t vec = (size_t)nh * D;
     if (tid < D) {
         const float eA = __expf(A[h]);
-        const float zv = ly.gate_per_head ? z[nh] : z[vec + tid];
+        float zv;
+        if (ly.zu) {  // low-rank forget gate: z = sum_j u[n, j] W[h, c, j]
+            const int r = ly.zrank;
+            const __bf16 *ur = ly.zu + (size_t)(nh / H) * r, *wr = ly.zw + ((size_t)h * D + tid) * r;
+            float acc = 0.f;
+            for (int j = 0; j < r; ++j) acc += (float)ur[j] * (float)wr[j];
+            zv = acc;
+        } else {
+            zv = ly.gate_per_head ? z[nh] : z[vec + tid];
+        }
         s_alpha[tid] = __expf(ly.gate_kind == GATE_SOFTPLUS ? softplus_gate(eA, zv) : kda_gate(eA, zv));
         s_k[tid] = to_f(k[vec + tid]);
         s_q[tid] = to_f(q[vec + tid]);

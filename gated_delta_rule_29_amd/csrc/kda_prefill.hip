@@ -309,7 +309,16 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
             const int t = s * SUB + u;
             float gt = 0.f;
             if (t < len) {
-                const float zv = zh ? z[(size_t)(t0 + t) * H + h] : z[tok(t) + ch];
+                float zv;
+                if (tab.ly.zu) {  // low-rank forget gate: z = sum_j u[t, j] W[h, ch, j]
+                    const int r = tab.ly.zrank;
+                    const __bf16 *ur = tab.ly.zu + (size_t)(t0 + t) * r, *wr = tab.ly.zw + ((size_t)h * D + ch) * r;
+                    float acc = 0.f;
+                    for (int j = 0; j < r; ++j) acc += (float)ur[j] * (float)wr[j];
+                    zv = acc;
+                } else {
+                    zv = zh ? z[(size_t)(t0 + t) * H + h] : z[tok(t) + ch];
+                }
                 gt = sp ? softplus_gate(eA, zv) : kda_gate(eA, zv);
             }
             acc += (double)gt;

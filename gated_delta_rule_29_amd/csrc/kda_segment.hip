@@ -303,7 +303,7 @@ static_assert(PTT <= PEH, "T lives in the E1 region");
 // e^{G_r - G_c} of a diagonal tile cannot be split into a row and a column part
 // without overflow, so those tiles are formed position pair by position pair
 // on the VALU, in the log domain (the cost the K3 bound removes).
-template <bool QKN, int GK>
+template <bool QKN, int GK, bool LRZ>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GK == GATE_K3 ? WY_WPE : WY_WPE_SP))) void wy_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     const float *__restrict__ z, const float *__restrict__ beta, const float *__restrict__ A, int N, int H,
@@ -356,16 +356,67 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GK == GATE_
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int tl = 4 * g + (e & 3), tu = 32 * ks + 16 * (e >> 2);  // row = tu (scalar) + tl
-                zin[ks][e] = __builtin_amdgcn_raw_buffer_load_b32(rz, tl * pz + zcs * ch, tu * pz, 0);
+                if constexpr (!LRZ) zin[ks][e] = __builtin_amdgcn_raw_buffer_load_b32(rz, tl * pz + zcs * ch, tu * pz, 0);
                 kin[ks][e] = __builtin_amdgcn_raw_buffer_load_b16(rk, tl * ph + 2 * ch, tu * ph, 0);
             }
     };
+    // Low-rank forget gate: the z tiles of both channel halves on MFMA before
+    // phase 1, Z (64 tokens x the wave's 16 channels of a half) = U (tokens x r)
+    // W_h^T (r x channels).  A operand: token rows of U (shared by the halves);
+    // B operand: the wave's channel rows of W_h.  The C tile zc[hf][rt] holds
+    // tokens 16 rt + 4 g + m of channel 64 hf + 16 w + lr: the phase-1 layout.
+    // The rank goes in blocks of 128 whose loads are all issued before the first
+    // product (one load latency per block); k-steps past the rank re-read the
+    // last one and enter the products as zeros.
+    const int zr = LRZ ? tab.ly.zrank : 0, zr2 = 2 * zr;  // rank, bytes per row
+    const __amdgpu_buffer_rsrc_t ru = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(tab.ly.zu + (LRZ ? (size_t)t0 * zr : 0)), 0, LRZ ? len * zr2 : 0, BUF_RSRC3);
+    const __amdgpu_buffer_rsrc_t rwz = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(tab.ly.zw + (LRZ ? (size_t)h * D * zr : 0)), 0, LRZ ? D * zr2 : 0, BUF_RSRC3);
+    f32x4 zc[2][4];
+    load_half(0);  // the first half's k loads are in flight during the projection
+    if constexpr (LRZ) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) zc[hf][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int nit = zr / 32;  // k-steps of 32: 1 .. 8
+        const bf16x8 zero8 = {};
+        for (int kb = 0; kb < nit; kb += 4) {
+            bf16x8 wb[2][4], ua[4][4];
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) {
+                const int ko = 2 * (32 * min(kb + s4, nit - 1) + 8 * g);
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf)
+                    wb[hf][s4] = __builtin_bit_cast(
+                        bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rwz, (64 * hf + 16 * w + lr) * zr2 + ko, 0, 0));
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt)
+                    ua[s4][rt] = __builtin_bit_cast(
+                        bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ru, lr * zr2 + ko, 16 * rt * zr2, 0));
+            }
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) {
+                const bool live = kb + s4 < nit;
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) {
+                    const bf16x8 a = live ? ua[s4][rt] : zero8;
+#pragma unroll
+                    for (int hf = 0; hf < 2; ++hf) zc[hf][rt] = mfma_bf16(a, wb[hf][s4], zc[hf][rt]);
+                }
+            }
+        }
+    }
+
     // (Issuing the second half's loads during the first half's Gram phase was
     // slower: 0.62 against 0.57 ms at 64K x 16.)
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-        if (hf) __syncthreads();  // the Gram half before is done with E1 and CB
-        load_half(hf);
+        if (hf) {
+            __syncthreads();  // the Gram half before is done with E1 and CB
+            load_half(1);
+        }
         __builtin_amdgcn_sched_barrier(0);
         const int ch = 64 * hf + 16 * w + lr, chl = 16 * w + lr;
         float Rs[5], eRs[4];
@@ -378,9 +429,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GK == GATE_
                 for (int e = 0; e < 8; ++e) {
                     const int tl = 4 * g + (e & 3), tu = 32 * ks + 16 * (e >> 2);
                     const bool ok = tu + tl < len;
-                    const uint32_t zu = zin[ks][e];
+                    float zv;
+                    if constexpr (LRZ) {
+                        const f32x4 zt = zc[hf][2 * ks + (e >> 2)];
+                        zv = zt[e & 3];
+                    } else {
+                        const uint32_t zu = zin[ks][e];
+                        zv = __builtin_bit_cast(float, zu);
+                    }
                     const uint16_t ku = kin[ks][e];
-                    gv[ks][e] = gate_of<GK>(eA, ok ? __builtin_bit_cast(float, zu) : -__builtin_inff());  // -inf: g = 0
+                    gv[ks][e] = gate_of<GK>(eA, ok ? zv : -__builtin_inff());  // -inf: g = 0
                     kb[ks][e] = __builtin_bit_cast(__bf16, ku);
                 }
             // ---- phase 0 (QKN, first half only): the inverse L2 norms of the
@@ -1396,16 +1454,21 @@ int launch_segment_prefill(const __bf16 *q, const __bf16 *k, const __bf16 *v, co
     if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return -1;
     if (T_total > 0) {
         const dim3 grid((unsigned)(ncm * H)), blk(256);
-        if (ly.gate_kind == GATE_SOFTPLUS) {
-            if (ly.qk_norm)
-                hipLaunchKernelGGL((wy_kernel<true, GATE_SOFTPLUS>), grid, blk, 0, stream, q, k, v, z, beta, A, N, H, tab);
-            else
-                hipLaunchKernelGGL((wy_kernel<false, GATE_SOFTPLUS>), grid, blk, 0, stream, q, k, v, z, beta, A, N, H,
-                                   tab);
-        } else if (ly.qk_norm) {
-            hipLaunchKernelGGL((wy_kernel<true, GATE_K3>), grid, blk, 0, stream, q, k, v, z, beta, A, N, H, tab);
+        auto wy = [&](auto qkn, auto gk, auto lrz) {
+            hipLaunchKernelGGL((wy_kernel<decltype(qkn)::value, decltype(gk)::value, decltype(lrz)::value>), grid,
+                               blk, 0, stream, q, k, v, z, beta, A, N, H, tab);
+        };
+        using T_ = std::true_type;
+        using F_ = std::false_type;
+        using K3 = std::integral_constant<int, GATE_K3>;
+        using SP = std::integral_constant<int, GATE_SOFTPLUS>;
+        const bool sp = ly.gate_kind == GATE_SOFTPLUS, lr = ly.zu != nullptr;
+        if (sp) {
+            if (ly.qk_norm) lr ? wy(T_{}, SP{}, T_{}) : wy(T_{}, SP{}, F_{});
+            else lr ? wy(F_{}, SP{}, T_{}) : wy(F_{}, SP{}, F_{});
         } else {
-            hipLaunchKernelGGL((wy_kernel<false, GATE_K3>), grid, blk, 0, stream, q, k, v, z, beta, A, N, H, tab);
+            if (ly.qk_norm) lr ? wy(T_{}, K3{}, T_{}) : wy(T_{}, K3{}, F_{});
+            else lr ? wy(F_{}, K3{}, T_{}) : wy(F_{}, K3{}, F_{});
         }
     }
     if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return -1;

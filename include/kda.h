@@ -206,6 +206,15 @@ int kda_chunk_fwd_ckpt(const void *q, const void *k, const void *v, kda_dtype qk
  *                step before wrote last, which are still in the GPU's
  *                last-level cache (the states of 256 x 32 heads are 512 MiB
  *                against a 256 MB cache).
+ *   gate_u, gate_w, gate_rank  the forget gate's low-rank projection (Kimi
+ *                Linear summary, section 4), fused in: with gate_u set, z is
+ *                not read from g_raw (which may be NULL) but formed as
+ *                z[t, h, c] = sum_j gate_u[t, j] * gate_w[h, c, j], with
+ *                gate_u [tokens, gate_rank] and gate_w [H, 128, gate_rank],
+ *                both bf16 (KDA_ERR_NULL if gate_w is NULL).  gate_rank is a
+ *                multiple of 32 in [32, 256] (KDA_ERR_SHAPE otherwise, and
+ *                with gate_per_head).  The decay is then gate_kind's, as with
+ *                a given z.  Both must be 16-byte aligned and must not overlap o.
  */
 enum { KDA_GATE_K3 = 0, KDA_GATE_SOFTPLUS = 1 };
 typedef struct kda_layer_opts {
@@ -217,6 +226,9 @@ typedef struct kda_layer_opts {
     int32_t gate_kind;
     int32_t gate_per_head;
     int32_t reverse_order;
+    const void *gate_u;
+    const void *gate_w;
+    int32_t gate_rank;
 } kda_layer_opts;
 /*
  * kda_chunk_fwd with the layer's steps fused in (opts, NULL gives KDA_ERR_NULL)

@@ -32,7 +32,7 @@ from __future__ import annotations
 import numpy as np
 
 SLICE = 4096
-TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "z": 3, "beta": 4, "A": 5, "S0": 6}
+TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "z": 3, "beta": 4, "A": 5, "S0": 6, "gate_u": 7, "gate_w": 8}
 
 
 def rng(seed: int, tensor: str, slice_id: int = 0) -> np.random.Generator:
@@ -102,6 +102,15 @@ def prefill_inputs(seed: int, T_total: int, H: int, dtype: str = "bf16", z_scale
     d["A"] = head_params(seed, H)
     d["S0"] = initial_state(seed, n_seqs, H, s0_std, D)
     return d
+
+
+def lowrank_gate(seed: int, rows: int, H: int, rank: int, D: int = 128):
+    """Factors of a low-rank forget-gate projection, bf16-representable float32:
+    u [rows, rank] ~ N(0, 1) and W [H, D, rank] ~ N(0, 1 / rank), so that each
+    z = sum_j u[t, j] W[h, c, j] is about N(0, 1) like the z of the other workloads."""
+    u = bf16_round(rng(seed, "gate_u").standard_normal((rows, rank), dtype=np.float32))
+    w = rng(seed, "gate_w").standard_normal((H, D, rank), dtype=np.float32) / np.float32(np.sqrt(rank))
+    return u, bf16_round(w)
 
 
 def decode_tokens(seed: int, step: int, N: int, H: int, dtype: str = "bf16", D: int = 128) -> dict:

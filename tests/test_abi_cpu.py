@@ -162,6 +162,22 @@ def test_prefill_gate_options_are_checked():
     assert call_prefill_layer(prefill_args(B=0, N=0, T=0), Opts(0, 0.0, None, None, 0.0, 0, 0, 1)) == SHAPE
 
 
+def test_prefill_lowrank_gate_options_are_checked():
+    u, w = fake(15).value, fake(16).value
+    # rank: a multiple of 32 in [32, 256]; not with the per-head gate
+    for r in (0, 16, 48, 288):
+        assert call_prefill_layer(prefill_args(z=None), Opts(0, 0.0, None, None, 0.0, 0, 0, 0, u, w, r)) == SHAPE
+    assert call_prefill_layer(prefill_args(z=None), Opts(0, 0.0, None, None, 0.0, 0, 1, 0, u, w, 64)) == SHAPE
+    assert call_prefill_layer(prefill_args(z=None), Opts(0, 0.0, None, None, 0.0, 0, 0, 0, u, None, 64)) == NULL
+    assert call_prefill_layer(prefill_args(z=None), Opts(0, 0.0, None, None, 0.0, 0, 0, 0, u + 2, w, 64)) == ALIGN
+    assert call_prefill_layer(prefill_args(o=fake(15, 256)), Opts(0, 0.0, None, None, 0.0, 0, 0, 0, u, w, 64)) == ALIAS
+    assert call_prefill_layer(prefill_args(o=fake(16, 256)), Opts(0, 0.0, None, None, 0.0, 0, 0, 0, u, w, 64)) == ALIAS
+    # without the factors g_raw is required
+    assert call_prefill_layer(prefill_args(z=None), Opts(0, 0.0, None, None, 0.0)) == NULL
+    assert call_prefill_layer(prefill_args(z=None, B=0, N=0, T=0),
+                              Opts(0, 0.0, None, None, 0.0, 0, 0, 0, u, w, 128)) == OK
+
+
 def test_ckpt_count():
     assert kda.ckpt_count([0, 63, 64, 6143, 6144, 20000], 6144) == 0 + 0 + 0 + 0 + 1 + 3
     assert kda.ckpt_count([128, 129, 255, 256], 128) == 1 + 1 + 1 + 2
@@ -219,3 +235,8 @@ def test_decode_layer_rejects():
     assert call_decode_layer(decode_args(o=fake(4, 1024)), Opts(0, 0.0, None, None, 0.0, 0, 0)) == ALIAS
     assert call_decode_layer(decode_args(o=fake(4, 16)), Opts(0, 0.0, None, None, 0.0, 0, 1)) == ALIAS
     assert call_decode_layer(decode_args(N=0), Opts(1, 1e-6, gate, w, 1e-6, 1, 1)) == OK
+    u, wl = fake(15).value, fake(16).value
+    assert call_decode_layer(decode_args(z=None), Opts(0, 0.0, None, None, 0.0, 0, 0, 0, u, wl, 40)) == SHAPE
+    assert call_decode_layer(decode_args(z=None), Opts(0, 0.0, None, None, 0.0, 0, 0, 0, None, wl, 64)) == NULL
+    assert call_decode_layer(decode_args(z=None), Opts(0, 0.0, None, None, 0.0, 0, 0, 0, u, None, 64)) == NULL
+    assert call_decode_layer(decode_args(o=fake(15, 64)), Opts(0, 0.0, None, None, 0.0, 0, 0, 0, u, wl, 64)) == ALIAS
