@@ -61,6 +61,7 @@ typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -292,6 +293,9 @@ static_assert(PTT <= PEH, "T lives in the E1 region");
 #ifndef WY_WPE
 #define WY_WPE 3
 #endif
+#ifndef WY_ROT
+#define WY_ROT 1
+#endif
 #ifndef WY_WPE_SP
 #define WY_WPE_SP 3
 #endif
@@ -315,6 +319,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GK == GATE_
     const int64_t t0 = tab.seq_start[n] + (int64_t)(c - tab.chunk_off[n]) * CH;
     const int len = (int)min((int64_t)CH, tab.seq_end[n] - t0);
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, g = l >> 4, lr = l & 15;
+    // Row-block role of this wave in the Gram and inverse phases, whose work
+    // grows with the row block: rotated from workgroup to workgroup.
+    const int wr = WY_ROT ? (w + (int)(blockIdx.x & 3u)) & 3 : w;
     const size_t HD = (size_t)H * D;
     const size_t base = (size_t)t0 * HD + (size_t)h * D;  // element (t, ch) at base + t * HD + ch
     char *blk = tab.blocks + ((size_t)c * H + h) * BLK;
@@ -339,7 +346,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GK == GATE_
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)(v + base), 0, len * ph, BUF_RSRC3);
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void *)(q + base), 0, len * ph, BUF_RSRC3);
     bf16x8 kga[2][2];  // [hf][ks]: channel tile 4 hf + w
-    // Gram accumulators of sub-chunk i = w against sub-chunks j <= i; tiles come
+    // Gram accumulators of sub-chunk i = wr against sub-chunks j <= i; tiles come
     // out transposed: lane (lr, g) holds row r = 16i + lr against columns
     // 16j + 4g + m.
     f32x4 a1[4], a2[4];
@@ -362,12 +369,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GK == GATE_
     };
     // Low-rank forget gate: the z tiles of both channel halves on MFMA before
     // phase 1, Z (64 tokens x the wave's 16 channels of a half) = U (tokens x r)
-    // W_h^T (r x channels).  A operand: token rows of U (shared by the halves);
-    // B operand: the wave's channel rows of W_h.  The C tile zc[hf][rt] holds
-    // tokens 16 rt + 4 g + m of channel 64 hf + 16 w + lr: the phase-1 layout.
-    // The rank goes in blocks of 128 whose loads are all issued before the first
-    // product (one load latency per block); k-steps past the rank re-read the
-    // last one and enter the products as zeros.
+    // W_h^T (r x channels).  A operand: token rows of U, from a copy in LDS
+    // shared by the waves; B operand: the wave's channel rows of W_h.  The C tile
+    // zc[hf][rt] holds tokens 16 rt + 4 g + m of channel 64 hf + 16 w + lr: the
+    // phase-1 layout.  The rank goes in blocks of 128 whose W loads are all
+    // issued before the first product; k-steps past the rank re-read the last
+    // one and enter the products as zeros.
     const int zr = LRZ ? tab.ly.zrank : 0, zr2 = 2 * zr;  // rank, bytes per row
     const __amdgpu_buffer_rsrc_t ru = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(tab.ly.zu + (LRZ ? (size_t)t0 * zr : 0)), 0, LRZ ? len * zr2 : 0, BUF_RSRC3);
@@ -382,19 +389,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GK == GATE_
             for (int rt = 0; rt < 4; ++rt) zc[hf][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
         const int nit = zr / 32;  // k-steps of 32: 1 .. 8
         const bf16x8 zero8 = {};
+        // The chunk's u tile is copied once into LDS (the E1 and CB arrays, free
+        // until phase 1 writes them): 16-byte slot s holds row t = s / nch at
+        // chunk (s - t) mod nch, so the 16 rows one A-operand read touches fall
+        // in different banks.
+        const int nch = zr / 8;  // 16-byte chunks per row
+        char *ulds = (char *)&sm;
+        static_assert(sizeof(sm.a) + sizeof(sm.CB) >= 64 * 512, "u tile fits E1 and CB");
+        for (int s0 = 64 * w; s0 < 64 * nch; s0 += 256) {
+            const int sl = s0 + l, t = sl / nch, c = (sl % nch - t % nch + nch) % nch;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ru, (lds_void *)(ulds + 16 * s0), 16, t * zr2 + 16 * c, 0, 0, 0);
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
+        __syncthreads();
         for (int kb = 0; kb < nit; kb += 4) {
             bf16x8 wb[2][4], ua[4][4];
 #pragma unroll
             for (int s4 = 0; s4 < 4; ++s4) {
-                const int ko = 2 * (32 * min(kb + s4, nit - 1) + 8 * g);
+                const int kc = min(kb + s4, nit - 1), ko = 2 * (32 * kc + 8 * g);
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf)
                     wb[hf][s4] = __builtin_bit_cast(
                         bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rwz, (64 * hf + 16 * w + lr) * zr2 + ko, 0, 0));
 #pragma unroll
-                for (int rt = 0; rt < 4; ++rt)
-                    ua[s4][rt] = __builtin_bit_cast(
-                        bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ru, lr * zr2 + ko, 16 * rt * zr2, 0));
+                for (int rt = 0; rt < 4; ++rt) {
+                    const int t = 16 * rt + lr;
+                    ua[s4][rt] = *(const bf16x8 *)(ulds + t * zr2 + 16 * ((4 * kc + g + t) % nch));
+                }
             }
 #pragma unroll
             for (int s4 = 0; s4 < 4; ++s4) {
@@ -407,6 +428,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GK == GATE_
                 }
             }
         }
+        __syncthreads();  // every wave has read the u tile before phase 1 writes E1 and CB
     }
 
     // (Issuing the second half's loads during the first half's Gram phase was
@@ -555,14 +577,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GK == GATE_
         }
         __syncthreads();
 
-        // ---- phase 2 (this half): Gram tiles of sub-chunk i = w against j <= i, and Q~.
+        // ---- phase 2 (this half): Gram tiles of sub-chunk i = wr against j <= i, and Q~.
         // Row operands x_r e^{G_r - R_i} (x = k, q) are formed once per 32-channel
         // block; the column operand k_c e^{R_i - G_c} is CB_c e^{R_i - R_{j+1}}: CB
         // lies in [e^-80, 1] |k|, the factor is <= 1 for j < i (an underflow drops
         // only terms below e^-87) and in [1, e^80] for j = i.  The channel order
         // inside each 32-block is perm32, shared by both operands and by Q~.
         {
-            const int i = w, r = 16 * i + lr;
+            const int i = wr, r = 16 * i + lr;
             const float nkr = QKN ? sm.nk[r] : 1.f, nqr = QKN ? sm.nq[r] : 1.f;
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh) {
@@ -709,7 +731,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GK == GATE_
     }
     f32x4 akk[4];
     {
-        const int i = w, r = 16 * i + lr;
+        const int i = wr, r = 16 * i + lr;
         const float br = sm.beta[r];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -736,7 +758,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GK == GATE_
     }
     __syncthreads();  // E1 is dead: T takes its place
     {
-        const int i = w, r = 16 * i + lr;
+        const int i = wr, r = 16 * i + lr;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             if (j <= i) *(f32x4 *)&sm.a.T[r * PTT + 16 * j + 4 * g] = akk[j];
@@ -751,7 +773,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GK == GATE_
     // ---- phase 3: T = (I + Akk)^{-1}, blocked forward substitution in place.
     // Diagonal 16 x 16 blocks: lane m of wave b solves column m of block b.
     if (l < 16) {
-        const int b = w, m = l;
+        const int b = wr, m = l;
         const float *blk0 = &sm.a.T[(16 * b) * PTT + 16 * b];
         float tcol[SUB];
 #pragma unroll
@@ -772,7 +794,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GK == GATE_
     // Off-diagonal blocks, row block i: T_ij = -T_ii sum_{j <= kb < i} A_i,kb T_kb,j (exact fp32 MFMA)
     for (int i = 1; i < 4; ++i) {
         f32x4 Xb = {0.f, 0.f, 0.f, 0.f};
-        const int jb = w;
+        const int jb = wr;
         if (jb < i) {
             for (int kb = jb; kb < i; ++kb) {
 #pragma unroll
@@ -926,7 +948,6 @@ constexpr int CHAIN_UNROLL_A = CHAIN_NBUF_A == 3 ? 6 : 2;
 constexpr int CH_NW = 8;  // waves per chain workgroup
 constexpr int CH_NT = 64 * CH_NW;
 
-typedef __attribute__((address_space(3))) void lds_void;
 
 // Copy one chunk's LDS image straight from its block into LDS
 // (buffer_load_dwordx4 ... lds: lane l of a wave lands at dst + 16 l, so each
