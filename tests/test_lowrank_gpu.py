@@ -103,3 +103,49 @@ def test_decode_lowrank_gate(io, gate):
     eo, es = err(o.cpu().numpy(), o_ref), err(S_t.cpu().numpy(), S_ref)
     say(f"  err_o={eo:.3e} err_S={es:.3e}")
     assert eo <= TOL[io] and es <= TOL[io], (eo, es)
+
+
+def test_lowrank_gate_with_layer_steps_snapshots_and_softplus():
+    """Every layer option at once on a ragged pack: q/k normalisation, the low-rank
+    forget gate under softplus decay, snapshots, and the output step.  The operator part
+    is held to the bar against the oracle; the output step to fp32 rounding against the
+    step applied to the GPU's own operator output (as for the plain layer test)."""
+    lens = [300, 64, 0, 257]
+    cu = synth.cu_seqlens(lens)
+    T, H, rank, eps, stride = int(cu[-1]), 2, 96, 1e-6, 128
+    d = synth.prefill_inputs(5750, T, H, s0_std=0.02, n_seqs=len(lens))
+    rng = np.random.Generator(np.random.PCG64(5751))
+    for n in ("q", "k"):
+        d[n] = synth.bf16_round(d[n] * rng.uniform(0.3, 3.0, size=(T, H, 1)).astype(np.float32))
+    gate = (2.0 * rng.standard_normal((T, H, 128))).astype(np.float32)
+    weight = rng.uniform(0.5, 1.5, size=128).astype(np.float32)
+    u, W = synth.lowrank_gate(5750, T, H, rank)
+    q, k, v = (to_dev(d[n], torch.bfloat16) for n in ("q", "k", "v"))
+    beta, A, S0 = (to_dev(d[n], torch.float32) for n in ("beta", "A", "S0"))
+    cu_t = to_dev(np.asarray(cu, np.int32), torch.int32)
+    gu, gw = to_dev(u, torch.bfloat16), to_dev(W, torch.bfloat16)
+    ck = torch.empty((kda.ckpt_count(lens, stride), H, 128, 128), dtype=torch.float32, device=q.device)
+    say("case lowrank + softplus + layer steps + snapshots")
+    kw = dict(gate="softplus", gate_u=gu, gate_w=gw, qk_l2norm=True, qk_eps=eps)
+    y, S1 = kda.kda_chunk_fwd(q, k, v, None, beta, A, S0, cu_t, S_ckpt=ck, ckpt_stride=stride,
+                              out_gate=to_dev(gate, torch.float32), norm_weight=to_dev(weight, torch.float32),
+                              norm_eps=eps, **kw)
+    o, S2 = kda.kda_chunk_fwd(q, k, v, None, beta, A, S0, cu_t, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(S1, S2)
+    qn, kn = oracle.l2_normalize(d["q"], eps), oracle.l2_normalize(d["k"], eps)
+    g = oracle.softplus_gate(oracle.lowrank_z(u, W), d["A"])
+    o_ref, S_ref = oracle.recurrent_g(qn, kn, d["v"], g, d["beta"], d["S0"], cu)
+    o_np = o.cpu().numpy()
+    eo, es = err(o_np, o_ref), err(S1.cpu().numpy(), S_ref)
+    ey = err(y.cpu().numpy(), oracle.gated_rmsnorm(o_np, gate, weight, eps))
+    say(f"  err_o={eo:.3e} err_S={es:.3e} err_output_step={ey:.3e}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"] and ey <= 1e-5
+    slot = 0
+    for n, L in enumerate(lens):
+        for m in range(L // stride):
+            sl = slice(int(cu[n]), int(cu[n]) + (m + 1) * stride)
+            _, S_m = oracle.recurrent_g(qn[sl], kn[sl], d["v"][sl], g[sl], d["beta"][sl], d["S0"][n:n + 1])
+            assert err(ck[slot].cpu().numpy(), S_m[0]) <= TOL["bf16"], (n, m)
+            slot += 1
+    assert slot == ck.shape[0]
