@@ -1384,13 +1384,29 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(const float *__restrict__
                 for (int m = 0; m < 4; ++m) S_final[s0b + (size_t)(32 * w + 16 * u + 4 * g + m) * D + col] = Sr[u][m];
         return;
     }
-    for (int p = 0; p < pn; ++p) {
+    // M_p and B_p of the step after next are loaded while this step computes:
+    // two register sets, loads always issued (past the last map they re-read it).
+    F8 Mr[2][2][4];
+    f32x4 Br[2][2];
+    auto load_map = [&](int p, int set) __attribute__((always_inline)) {
+        const size_t b = ((size_t)(first + min(p, max(pn - 2, 0))) * H + h) * D * D;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int r0 = 32 * w + 16 * u;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) Br[set][u][m] = tab.Bseg[b + (size_t)(r0 + 4 * g + m) * D + col];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) Mr[set][u][ks] = ld_f8(&tab.Mseg[b + (size_t)(r0 + lr) * D + 32 * ks + 8 * g]);
+        }
+    };
+    auto step = [&](int p, int set) __attribute__((always_inline)) {
         const size_t b = ((size_t)(first + p) * H + h) * D * D;
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int m = 0; m < 4; ++m) tab.Sin[b + (size_t)(32 * w + 16 * u + 4 * g + m) * D + col] = Sr[u][m];
-        if (p == pn - 1) break;
+        if (p == pn - 1) return;
+        load_map(p + 1, set ^ 1);
 #pragma unroll
         for (int u = 0; u < 2; ++u)
             *(f32x4 *)&Ss[lr * 132 + 32 * w + 16 * u + 4 * g] = Sr[u];
@@ -1401,15 +1417,16 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(const float *__restrict__
         __syncthreads();
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const int r0 = 32 * w + 16 * u;
-            f32x4 acc;
+            f32x4 acc = Br[set][u];
 #pragma unroll
-            for (int m = 0; m < 4; ++m) acc[m] = tab.Bseg[b + (size_t)(r0 + 4 * g + m) * D + col];
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                acc = mma_ff(acc, ld_f8(&tab.Mseg[b + (size_t)(r0 + lr) * D + 32 * ks + 8 * g]), sb[ks]);
+            for (int ks = 0; ks < 4; ++ks) acc = mma_ff(acc, Mr[set][u][ks], sb[ks]);
             Sr[u] = acc;
         }
+    };
+    load_map(0, 0);
+    for (int p = 0; p < pn; p += 2) {
+        step(p, 0);
+        if (p + 1 < pn) step(p + 1, 1);
     }
 }
 
