@@ -219,6 +219,22 @@ def test_head_counts(H, T):
     check(d, o, Sf, label=f"H={H}")
 
 
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_many_short_sequences(io):
+    """1,500 sequences of lengths 0..40 (a third of them empty): the sequence tables are
+    built by scans over several 256-wide blocks, and most sequences hold one partial chunk."""
+    rng = np.random.Generator(np.random.PCG64(3950))
+    lens = [int(x) for x in rng.integers(0, 41, size=1500)]
+    for i in range(0, 1500, 3):
+        lens[i] = 0
+    cu = synth.cu_seqlens(lens)
+    d = synth.prefill_inputs(3951, int(cu[-1]), 2, dtype=io, s0_std=0.02, n_seqs=len(lens))
+    say(f"case {len(lens)} short sequences, {int(cu[-1])} tokens io={io}")
+    o, Sf = run_prefill(d, cu=cu, S0=d["S0"], io=io)
+    check(d, o, Sf, cu=cu, io=io, label="many short")
+    assert np.array_equal(Sf[0::3], d["S0"][0::3])  # empty sequences keep their state exactly
+
+
 def test_serving_batch_mixed_lengths():
     """Sixty sequences of seeded lengths 0..2500 packed with cu_seqlens (a serving-style batch)."""
     rng = np.random.Generator(np.random.PCG64(3900))
