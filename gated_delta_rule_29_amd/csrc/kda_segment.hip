@@ -106,7 +106,6 @@ __device__ __forceinline__ void split_f16_pair(float a, float b, uint32_t &hi, u
 
 constexpr int PTT = 68;  // pitch (floats) of T [64][64]
 
-// f(std::integral_constant<int, i>) for i = 0 .. N-1, expanded at compile time.
 // Unsigned maximum over one DPP row (16 lanes with equal lane / 16), in every lane.
 __device__ __forceinline__ uint32_t row_umax16(uint32_t x) {
     x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false));
@@ -159,6 +158,7 @@ __device__ __forceinline__ f32x4 u_decode(UBlk b) {
     return u;
 }
 
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, expanded at compile time.
 template <typename F, int... I>
 __device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
     (f(std::integral_constant<int, I>{}), ...);
@@ -170,6 +170,7 @@ __device__ __forceinline__ void static_for(F &&f) {
 
 struct SegTable {
     int32_t *seg_off;    // [N+1] first segment of each sequence
+    int32_t *segA_off;   // [N+1] first pass-A segment (pass A skips a sequence's last)
     int32_t *chunk_off;  // [N+1] first chunk of each sequence
     int64_t *seq_start;  // [N]
     int64_t *seq_end;    // [N]
@@ -184,17 +185,20 @@ struct SegTable {
 
 // ------------------------------------------------------------------ prep --
 
-// Sequences: s_m = running max of the clamped offsets.  chunk_off and seg_off
-// are exclusive prefix sums of ceil(len / 64) and ceil(ceil(len / 64) / L).
+// Sequences: s_m = running max of the clamped offsets.  chunk_off, seg_off and
+// segA_off are exclusive prefix sums of ceil(len / 64), of the segment counts
+// ceil(ceil(len / 64) / L), and of those less one (pass A skips a sequence's
+// last segment).
 __global__ __launch_bounds__(256) void seg_prep_kernel(const int32_t *__restrict__ cu, int N, int64_t T_total,
                                                        int64_t Tper, SegTable tab) {
-    __shared__ int64_t s_a[256], s_b[256];
-    __shared__ int64_t s_prev_max, s_prev_seg, s_prev_chunk;
+    __shared__ int64_t s_a[256], s_b[256], s_c[256];
+    __shared__ int64_t s_prev_max, s_prev_a, s_prev_b, s_prev_c;
     const int tid = threadIdx.x;
     if (tid == 0) {
         s_prev_max = 0;
-        s_prev_seg = 0;
-        s_prev_chunk = 0;
+        s_prev_a = 0;
+        s_prev_b = 0;
+        s_prev_c = 0;
     }
     __syncthreads();
     for (int base = 0; base <= N; base += 256) {
@@ -219,28 +223,34 @@ __global__ __launch_bounds__(256) void seg_prep_kernel(const int32_t *__restrict
         if (m >= 1 && m <= N) tab.seq_end[m - 1] = sm;
         int64_t nch = 0;
         if (m >= 1 && m <= N) nch = (sm - sp + CH - 1) / CH;
+        const int64_t ns = (nch + tab.L - 1) / tab.L;
         __syncthreads();
-        s_a[tid] = (nch + tab.L - 1) / tab.L;
+        s_a[tid] = ns;
         s_b[tid] = nch;
+        s_c[tid] = ns > 0 ? ns - 1 : 0;
         __syncthreads();
         for (int off = 1; off < 256; off <<= 1) {
             const int64_t x = tid >= off ? s_a[tid - off] : 0;
             const int64_t y = tid >= off ? s_b[tid - off] : 0;
+            const int64_t z = tid >= off ? s_c[tid - off] : 0;
             __syncthreads();
             s_a[tid] += x;
             s_b[tid] += y;
+            s_c[tid] += z;
             __syncthreads();
         }
-        const int64_t seg = s_a[tid] + s_prev_seg, chk = s_b[tid] + s_prev_chunk;
+        const int64_t seg = s_a[tid] + s_prev_a, chk = s_b[tid] + s_prev_b, sa = s_c[tid] + s_prev_c;
         if (m <= N) {
             tab.seg_off[m] = (int32_t)seg;
             tab.chunk_off[m] = (int32_t)chk;
+            tab.segA_off[m] = (int32_t)sa;
         }
         __syncthreads();
         if (tid == 255) {
             s_prev_max = sm;
-            s_prev_seg = seg;
-            s_prev_chunk = chk;
+            s_prev_a = seg;
+            s_prev_b = chk;
+            s_prev_c = sa;
         }
         __syncthreads();
     }
@@ -997,16 +1007,21 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     __shared__ __align__(16) char ogate[PASS_A ? 16 : CH_NW * CH * 64];
     constexpr int NCT = PASS_A ? 2 : 1;
 
-    const int x = blockIdx.x, h = blockIdx.y;
-    const int nseg = tab.seg_off[N];
-    if (x >= nseg) return;
-    const int n = seg_find(tab.seg_off, N, x);
-    const int j = x - tab.seg_off[n];
+    // Workgroup i takes head i mod H of the pass's (i / H)-th segment: the
+    // workgroups with work come first and in one block, so they spread evenly
+    // over the XCDs and none waits behind an empty one.  Pass A has no work for
+    // a sequence's last segment (its map is not needed).
+    const int a = blockIdx.x / H, h = blockIdx.x % H;
+    const int32_t *soff = PASS_A ? tab.segA_off : tab.seg_off;
+    if (a >= soff[N]) return;
+    const int n = seg_find(soff, N, a);
+    const int j = a - soff[n];
+    const int x = tab.seg_off[n] + j;  // segment index of the maps and states
     const int pn = tab.seg_off[n + 1] - tab.seg_off[n];
-    if (PASS_A && j == pn - 1) return;  // the last segment's map is not needed
+    const int L = tab.L;
     const int64_t s0 = tab.seq_start[n], s1 = tab.seq_end[n];
     const int nch = (int)((s1 - s0 + CH - 1) / CH);
-    const int cbeg = j * tab.L, cend = min(nch, cbeg + tab.L);
+    const int cbeg = j * L, cend = min(nch, cbeg + L);
     const size_t bstride = (size_t)H * BLK;
     const char *blk0 = tab.blocks + ((size_t)tab.chunk_off[n] * H + h) * BLK;
 
@@ -1448,7 +1463,7 @@ static inline int64_t seg_max(int64_t T_total, int N, int H) {
 }
 
 size_t seg_workspace_bytes(int64_t T_total, int N, int H) {
-    const size_t tab = 2 * align_up(4 * (size_t)(N + 1)) + 2 * align_up(8 * (size_t)N) + align_up(8 * (size_t)(N + 1));
+    const size_t tab = 3 * align_up(4 * (size_t)(N + 1)) + 2 * align_up(8 * (size_t)N) + align_up(8 * (size_t)(N + 1));
     return tab + (size_t)seg_chunks_max(T_total, N) * H * BLK +
            3 * (size_t)seg_max(T_total, N, H) * H * D * D * sizeof(float);
 }
@@ -1468,6 +1483,8 @@ int launch_segment_prefill(const __bf16 *q, const __bf16 *k, const __bf16 *v, co
     SegTable tab;
     tab.seg_off = (int32_t *)p;
     p += align_up(4 * (size_t)(N + 1));
+    tab.segA_off = (int32_t *)p;
+    p += align_up(4 * (size_t)(N + 1));
     tab.chunk_off = (int32_t *)p;
     p += align_up(4 * (size_t)(N + 1));
     tab.seq_start = (int64_t *)p;
@@ -1485,6 +1502,8 @@ int launch_segment_prefill(const __bf16 *q, const __bf16 *k, const __bf16 *v, co
     tab.Bseg = tab.Mseg + st;
     tab.Sin = tab.Bseg + st;
     tab.L = L;
+    // a launch covers at most 2^32 - 1 work-items (unreachable within a GPU's memory)
+    if (ncm * H > (int64_t)(UINT32_MAX / 256) || nsm * H > (int64_t)(UINT32_MAX / CH_NT)) return -1;
     if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return -1;
     hipLaunchKernelGGL(seg_prep_kernel, dim3(1), dim3(256), 0, stream, cu, N, T_total, cu ? (int64_t)0 : T, tab);
     if (ck.S && launch_ckpt_prep(tab.seq_start, tab.seq_end, N, (int64_t)ck.stride_chunks * CH, ckpt_off, stream) != 0)
@@ -1510,12 +1529,13 @@ int launch_segment_prefill(const __bf16 *q, const __bf16 *k, const __bf16 *v, co
         }
     }
     if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return -1;
-    hipLaunchKernelGGL(seg_chain_kernel<true>, dim3((unsigned)nsm, (unsigned)H), dim3(CH_NT), 0, stream, N, H, tab,
+    const dim3 cgrid((unsigned)(nsm * H));
+    hipLaunchKernelGGL(seg_chain_kernel<true>, cgrid, dim3(CH_NT), 0, stream, N, H, tab,
                        o, S_final);
     if (ev && hipEventRecord(ev[3], stream) != hipSuccess) return -1;
     hipLaunchKernelGGL(seg_scan_kernel, dim3((unsigned)(N * H), 8), dim3(256), 0, stream, S0, N, H, tab, S_final);
     if (ev && hipEventRecord(ev[4], stream) != hipSuccess) return -1;
-    hipLaunchKernelGGL(seg_chain_kernel<false>, dim3((unsigned)nsm, (unsigned)H), dim3(CH_NT), 0, stream, N, H, tab,
+    hipLaunchKernelGGL(seg_chain_kernel<false>, cgrid, dim3(CH_NT), 0, stream, N, H, tab,
                        o, S_final);
     if (hipGetLastError() != hipSuccess) return -1;
     if (ev && hipEventRecord(ev[5], stream) != hipSuccess) return -1;
