@@ -259,7 +259,7 @@ def kda_decode_step(q, k, v, g_raw, beta, A, S, *, o=None, stream=None, qk_l2nor
     value per head); beta [N, H]; A [H]; S [N, H, 128, 128] fp32 updated in place.  Returns o
     [N, H, 128] fp32.  qk_l2norm, out_gate, norm_weight, norm_eps, gate: as kda_chunk_fwd
     (kda_decode_step_layer).  reverse_order: visit the (sequence, head) states last to first (same
-    results); alternate it over consecutive steps so each starts with the states still in cache.
+    results, same speed).
     gate_u [N, r], gate_w [H, 128, r]: the low-rank forget gate, as kda_chunk_fwd (g_raw may be None)."""
     lib = load()
     N, H, dk = q.shape

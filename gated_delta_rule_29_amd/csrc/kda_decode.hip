@@ -5,7 +5,7 @@
 // KDA layer's q/k normalisation and gated output RMSNorm.
 //
 // One workgroup of 256 threads per (sequence, head).  The 64 KiB fp32 state is
-// streamed from HBM once and written back once:
+// streamed from HBM once and written back once, with non-temporal stores:
 //   wave w owns key rows [32w, 32w+32); lane l owns columns 4*(l&31)..+3 of the
 //   rows 32w + 2m + (l>>5), m = 0..15 (16 float4 per lane, held in registers).
 // Per head: alpha = exp(g(z)); S' = Diag(alpha) S; p = S'^T k and r = S'^T q
@@ -134,7 +134,9 @@ __global__ __launch_bounds__(256) void decode_kernel(const IO *__restrict__ q, c
         const float ki = s_k[i] * nk;
         float4 x = st[m];
         x.x += ki * dl.x; x.y += ki * dl.y; x.z += ki * dl.z; x.w += ki * dl.w;
-        *(float4 *)(Sh + (size_t)i * D + 4 * cg) = x;
+        // non-temporal: the state is next read a whole step later, after the
+        // other heads' states have passed through the caches
+        __builtin_nontemporal_store(f32x4{x.x, x.y, x.z, x.w}, (f32x4 *)(Sh + (size_t)i * D + 4 * cg));
     }
 }
 

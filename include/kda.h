@@ -201,11 +201,8 @@ int kda_chunk_fwd_ckpt(const void *q, const void *k, const void *v, kda_dtype qk
  *   reverse_order  decode only (the prefill rejects nonzero with
  *                KDA_ERR_SHAPE): nonzero visits the (sequence, head) states
  *                last to first.  The results are the same bits either way.
- *                A caller running consecutive steps over the same states
- *                alternates it, so that each step starts with the states the
- *                step before wrote last, which are still in the GPU's
- *                last-level cache (the states of 256 x 32 heads are 512 MiB
- *                against a 256 MB cache).
+ *                (The state stores are non-temporal, so the order has no
+ *                effect on the speed of consecutive steps.)
  *   gate_u, gate_w, gate_rank  the forget gate's low-rank projection (Kimi
  *                Linear summary, section 4), fused in: with gate_u set, z is
  *                not read from g_raw (which may be NULL) but formed as
