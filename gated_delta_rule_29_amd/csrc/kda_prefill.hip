@@ -19,15 +19,19 @@
 // fp32 / bf16 range, so the diagonal tiles are dense MFMA products too.
 //
 // Kernels (one launch each, in stream order):
-//   prep_kernel   sequence boundaries (clamped, non-decreasing) and the first
-//                 chunk index of every sequence;
+//   prep_kernel   sequence boundaries (clamped, non-decreasing), the first
+//                 chunk of every sequence and its first segment (L chunks);
 //   intra_kernel  one workgroup per (chunk, head), all chunks in parallel:
 //                 gate + sub-chunk cumsums, the two Gram tiles on MFMA, the
 //                 blocked forward substitution, W and U on MFMA; writes the
 //                 per-chunk operands of the chain to the workspace;
-//   chain_kernel  one workgroup per (sequence, head, 16 value columns): keeps
-//                 its 128 x 16 fp32 state slice in registers across the
-//                 sequence's chunks and forms Delta, the output and the next
+//   chain_kernel<true>   the affine map S -> M S + B of every segment but a
+//                 sequence's last, one workgroup per (segment, head, 16 of
+//                 the 256 columns of [M | B]);
+//   seg_scan_kernel (kda_segment.hip)  the state entering each segment;
+//   chain_kernel<false>  one workgroup per (segment, head, 16 value columns):
+//                 keeps its 128 x 16 fp32 state slice in registers across the
+//                 segment's chunks and forms Delta, the output and the next
 //                 state with MFMA.
 //
 // Precision: q, k, v arrive in bf16 (exact MFMA operands).  Intermediates that
@@ -55,21 +59,31 @@ __host__ __device__ constexpr size_t align256(size_t x) { return (x + 255) & ~(s
 
 struct Table {  // workspace header
     int32_t *chunk_off;  // [N+1] first chunk of each sequence; chunk_off[N] = total
+    int32_t *seg_off;    // [N+1] first segment of each sequence
+    int32_t *segA_off;   // [N+1] first map segment (every segment but a sequence's last)
     int64_t *seq_start;  // [N]
     int64_t *seq_end;    // [N]
     int64_t *ckpt_off;   // [N+1] first snapshot slot of each sequence
     char *blocks;        // chain operands, block (c, h) at (c * H + h) * BLK_BYTES
+    float *Mseg;         // [nseg][H][128][128] segment transitions
+    float *Bseg;         // [nseg][H][128][128] segment offsets
+    float *Sin;          // [nseg][H][128][128] state entering each segment
+    int L;               // chunks per segment
     Ckpt ck;
     Layer ly;
 };
 
 __host__ __device__ inline size_t table_bytes(int N) {
-    return align256(4 * (size_t)(N + 1)) + 2 * align256(8 * (size_t)N) + align256(8 * (size_t)(N + 1));
+    return 3 * align256(4 * (size_t)(N + 1)) + 2 * align256(8 * (size_t)N) + align256(8 * (size_t)(N + 1));
 }
 __host__ __device__ inline Table carve(void *ws, int N) {
     char *p = (char *)ws;
     Table t;
     t.chunk_off = (int32_t *)p;
+    p += align256(4 * (size_t)(N + 1));
+    t.seg_off = (int32_t *)p;
+    p += align256(4 * (size_t)(N + 1));
+    t.segA_off = (int32_t *)p;
     p += align256(4 * (size_t)(N + 1));
     t.seq_start = (int64_t *)p;
     p += align256(8 * (size_t)N);
@@ -78,11 +92,26 @@ __host__ __device__ inline Table carve(void *ws, int N) {
     t.ckpt_off = (int64_t *)p;
     p += align256(8 * (size_t)(N + 1));
     t.blocks = p;
+    t.Mseg = t.Bseg = t.Sin = nullptr;
+    t.L = 1;
     t.ck = Ckpt{nullptr, t.ckpt_off, 1, 0};
     t.ly = Layer{false, 0.f, nullptr, nullptr, 0.f};
     return t;
 }
 __host__ inline int64_t max_chunks(int64_t T_total, int N) { return (T_total + CH - 1) / CH + N; }
+// Segments of the chain: about SEG32_TARGET (segment, head) pairs in all, so
+// that the chain passes have over a thousand workgroups (8 and 16 per pair).
+// Their time at 64K x 16 is the same from 128 to 1,024 pairs (they are bound
+// by throughput, not by the length of the chain); fewer pairs shorten the scan.
+constexpr int SEG32_TARGET = 128;
+__host__ inline int seg32_len(int64_t T_total, int N, int H) {
+    const int64_t per_head = SEG32_TARGET / (H > 0 ? H : 1) > 0 ? SEG32_TARGET / H : 1;
+    return (int)((max_chunks(T_total, N) + per_head - 1) / per_head);
+}
+__host__ inline int64_t seg32_max(int64_t T_total, int N, int H) {
+    const int L = seg32_len(T_total, N, H);
+    return (max_chunks(T_total, N) + L - 1) / L + N;
+}
 
 // ------------------------------------------------------------------- prep --
 
@@ -90,14 +119,18 @@ __host__ inline int64_t max_chunks(int64_t T_total, int N) { return (T_total + C
 // so sequences never overlap and the chunk count is at most ceil(T/64) + N.
 // cu == nullptr means B equal sequences of Tper tokens.  One workgroup walks
 // the N + 1 offsets in tiles of 256 with a running max and a running sum.
+// It also writes seg_off and segA_off: the exclusive prefix sums of each
+// sequence's segment count ceil(chunks / L) and of that count less one.
 __global__ __launch_bounds__(256) void prep_kernel(const int32_t *__restrict__ cu, int N, int64_t T_total,
                                                    int64_t Tper, Table tab) {
-    __shared__ int64_t s_scan[256];
-    __shared__ int64_t s_prev_max, s_prev_sum;
+    __shared__ int64_t s_scan[256], s_seg[256], s_sa[256];
+    __shared__ int64_t s_prev_max, s_prev_sum, s_prev_seg, s_prev_sa;
     const int tid = threadIdx.x;
     if (tid == 0) {
         s_prev_max = 0;
         s_prev_sum = 0;
+        s_prev_seg = 0;
+        s_prev_sa = 0;
     }
     __syncthreads();
     for (int base = 0; base <= N; base += 256) {
@@ -123,21 +156,34 @@ __global__ __launch_bounds__(256) void prep_kernel(const int32_t *__restrict__ c
         if (m >= 1 && m <= N) tab.seq_end[m - 1] = sm;
         // chunks of sequence m - 1, inclusive running sum = chunk_off[m]
         const int64_t cnt = (m >= 1 && m <= N) ? (sm - sp + CH - 1) / CH : 0;
+        const int64_t ns = (cnt + tab.L - 1) / tab.L;
         __syncthreads();
         s_scan[tid] = cnt;
+        s_seg[tid] = ns;
+        s_sa[tid] = ns > 0 ? ns - 1 : 0;
         __syncthreads();
         for (int off = 1; off < 256; off <<= 1) {
             const int64_t x = tid >= off ? s_scan[tid - off] : 0;
+            const int64_t y = tid >= off ? s_seg[tid - off] : 0;
+            const int64_t z = tid >= off ? s_sa[tid - off] : 0;
             __syncthreads();
             s_scan[tid] += x;
+            s_seg[tid] += y;
+            s_sa[tid] += z;
             __syncthreads();
         }
-        const int64_t incl = s_scan[tid] + s_prev_sum;
-        if (m <= N) tab.chunk_off[m] = (int32_t)incl;
+        const int64_t incl = s_scan[tid] + s_prev_sum, sg = s_seg[tid] + s_prev_seg, sa = s_sa[tid] + s_prev_sa;
+        if (m <= N) {
+            tab.chunk_off[m] = (int32_t)incl;
+            tab.seg_off[m] = (int32_t)sg;
+            tab.segA_off[m] = (int32_t)sa;
+        }
         __syncthreads();
         if (tid == 255) {
             s_prev_max = sm;
             s_prev_sum = incl;
+            s_prev_seg = sg;
+            s_prev_sa = sa;
         }
         __syncthreads();
     }
@@ -554,71 +600,79 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
 
 // ----------------------------------------------------------------- chain --
 
-constexpr int NB = 16;  // value columns per workgroup
+constexpr int NB = 16;  // state columns per workgroup
 
-template <bool F32>
-struct ChainSmem;
-template <>
-struct ChainSmem<false> {          // bf16 hi / lo, transposed [column][k]
-    __bf16 Sh[NB * 136], Sl[NB * 136];
-    __bf16 Dh[NB * 72], Dl[NB * 72];
-};
-template <>
-struct ChainSmem<true> {
-    float S[NB * 132];
-    float Dl[NB * 68];
+struct ChainSmem {
+    float S[NB * 132];  // the state slice, transposed [column][key row]
+    float Dl[NB * 68];  // Delta, transposed [column][token]
 };
 
-template <typename IO>
-__global__ __launch_bounds__(256) void chain_kernel(const float *__restrict__ S0, int N, int H, Table tab,
-                                                    float *__restrict__ o, float *__restrict__ S_final) {
-    constexpr bool F32 = sizeof(IO) == 4;
-    __shared__ ChainSmem<F32> sm;
-    // XCD-aware mapping: workgroups L with equal L % 8 share an XCD (and its L2);
-    // the 8 column blocks of one (sequence, head) get equal L % 8.
-    const int L = blockIdx.x;
-    const int p = (L & 7) + 8 * (L >> 6), cb = (L >> 3) & 7;
-    if (p >= N * H) return;
-    const int n = p / H, h = p % H;
-    const int col0 = NB * cb;
+// largest n in [0, N) with off[n] <= x (for x < off[N] that is the owner of x)
+__device__ inline int seq_of(const int32_t *off, int N, int x) {
+    int lo = 0, hi = N - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (off[mid] <= x)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
+// The chain over one segment of a sequence, 16 state columns per workgroup,
+// exact fp32 MFMA throughout.  The segment map carries a state S entering the
+// segment to M S + B; MAP = true computes the columns of X = [M | B] (128 x
+// 256) by running the chain step from X = [I | 0], with U entering only the B
+// columns; MAP = false runs it from the state the scan gave the segment and
+// writes o (and snapshots, and S_final after a sequence's last segment).
+// Workgroups are numbered so that the column blocks of one (segment, head)
+// share an XCD (and its L2, which serves their common operand block), and the
+// (segment, head) pairs with work come first.
+template <bool MAP>
+__global__ __launch_bounds__(256) void chain_kernel(int N, int H, Table tab, float *__restrict__ o,
+                                                    float *__restrict__ S_final) {
+    __shared__ ChainSmem sm;
+    constexpr int NCB = MAP ? 16 : 8;  // column blocks per (segment, head)
+    const int Lw = blockIdx.x;
+    const int p = (Lw & 7) + 8 * (Lw / (8 * NCB)), cb = (Lw >> 3) % NCB;
+    const int a = p / H, h = p % H;
+    const int32_t *soff = MAP ? tab.segA_off : tab.seg_off;
+    if (a >= soff[N]) return;
+    const int n = seq_of(soff, N, a);
+    const int j = a - soff[n];
+    const int x = tab.seg_off[n] + j;  // segment index of the maps and states
+    const int pn = tab.seg_off[n + 1] - tab.seg_off[n];
+    const bool bcol = MAP && cb >= 8;               // a column of B (U enters)
+    const int col0 = NB * (MAP ? cb & 7 : cb);      // column within M, B or the state
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, lr = l & 15;
 
     // state slice: wave w owns key rows [32w, 32w+32) as two 16-row tiles (C layout)
     f32x4 Sr[2];
-    const size_t sbase = ((size_t)n * H + h) * D * D;
+    const size_t sblk = ((size_t)x * H + h) * D * D;
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
-            Sr[u][m] = S0 ? S0[sbase + (size_t)(32 * w + 16 * u + 4 * g + m) * D + col0 + lr] : 0.f;
+        for (int m = 0; m < 4; ++m) {
+            const int r = 32 * w + 16 * u + 4 * g + m;
+            Sr[u][m] = MAP ? (!bcol && r == col0 + lr ? 1.f : 0.f) : tab.Sin[sblk + (size_t)r * D + col0 + lr];
+        }
 
-    const int cbeg = tab.chunk_off[n], cend = tab.chunk_off[n + 1];
+    const int cseq = tab.chunk_off[n];  // the sequence's first chunk
+    const int cbeg = cseq + j * tab.L, cend = min(tab.chunk_off[n + 1], cbeg + tab.L);
     const int64_t sstart = tab.seq_start[n], send = tab.seq_end[n];
     const int nks_aq = w < 2 ? 1 : 2;  // 32-token k-steps of Aqk row tile w
     const int64_t ck_base = tab.ck.S ? tab.ck.off[n] : 0;
 
     for (int c = cbeg; c < cend; ++c) {
         const char *blk = tab.blocks + ((size_t)c * H + h) * BLK_BYTES;
-        const int64_t t0 = sstart + (int64_t)(c - cbeg) * CH;
+        const int64_t t0 = sstart + (int64_t)(c - cseq) * CH;
         const int len = (int)min((int64_t)CH, send - t0);
 
         // (1) publish the state slice as the B operand of W S and Q~ S
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int r0 = 32 * w + 16 * u + 4 * g;
-            if constexpr (F32) {
-                *(float4 *)&sm.S[lr * 132 + r0] = make_float4(Sr[u][0], Sr[u][1], Sr[u][2], Sr[u][3]);
-            } else {
-                bf16x4 hv, lv;
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    hv[m] = (__bf16)Sr[u][m];
-                    lv[m] = (__bf16)(Sr[u][m] - (float)hv[m]);
-                }
-                *(bf16x4 *)&sm.Sh[lr * 136 + r0] = hv;
-                *(bf16x4 *)&sm.Sl[lr * 136 + r0] = lv;
-            }
-        }
+        for (int u = 0; u < 2; ++u)
+            *(float4 *)&sm.S[lr * 132 + 32 * w + 16 * u + 4 * g] = make_float4(Sr[u][0], Sr[u][1], Sr[u][2], Sr[u][3]);
         __syncthreads();
 
         // (2) Delta rows [16w, 16w+16) = U - W S ;  O = Q~ S
@@ -627,69 +681,27 @@ __global__ __launch_bounds__(256) void chain_kernel(const float *__restrict__ S0
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const int k0 = 32 * ks + 8 * g;
-            if constexpr (F32) {
-                const F8 sb = ld_f8(&sm.S[lr * 132 + k0]);
-                ws = mma_ff(ws, ld_f8((const float *)(blk + OFF_W) + row * D + k0), sb);
-                oacc = mma_ff(oacc, ld_f8((const float *)(blk + OFF_QT) + row * D + k0), sb);
-            } else {
-                S8 sb;
-                sb.hi = ld_b8(&sm.Sh[lr * 136 + k0]);
-                sb.lo = ld_b8(&sm.Sl[lr * 136 + k0]);
-                ws = mma_11(ws, ld_b8((const __bf16 *)(blk + OFF_W) + row * D + k0), sb.hi);
-                S8 qa;
-                qa.hi = ld_b8((const __bf16 *)(blk + OFF_QT) + row * D + k0);
-                qa.lo = ld_b8((const __bf16 *)(blk + OFF_QT) + CH * D + row * D + k0);
-                oacc = mma_ss(oacc, qa, sb);
-            }
+            const F8 sb = ld_f8(&sm.S[lr * 132 + k0]);
+            ws = mma_ff(ws, ld_f8((const float *)(blk + OFF_W) + row * D + k0), sb);
+            if constexpr (!MAP) oacc = mma_ff(oacc, ld_f8((const float *)(blk + OFF_QT) + row * D + k0), sb);
         }
         f32x4 dl;
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
-            dl[m] = ((const float *)(blk + OFF_U))[(16 * w + 4 * g + m) * D + col0 + lr] - ws[m];
+        for (int m = 0; m < 4; ++m) {
+            const float uv = (!MAP || bcol) ? ((const float *)(blk + OFF_U))[(16 * w + 4 * g + m) * D + col0 + lr] : 0.f;
+            dl[m] = uv - ws[m];
+        }
 
         // (3) publish Delta as the B operand of Aqk Delta and K~^T Delta
-        {
-            const int r0 = 16 * w + 4 * g;
-            if constexpr (F32) {
-                *(float4 *)&sm.Dl[lr * 68 + r0] = make_float4(dl[0], dl[1], dl[2], dl[3]);
-            } else {
-                bf16x4 hv, lv;
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    hv[m] = (__bf16)dl[m];
-                    lv[m] = (__bf16)(dl[m] - (float)hv[m]);
-                }
-                *(bf16x4 *)&sm.Dh[lr * 72 + r0] = hv;
-                *(bf16x4 *)&sm.Dl[lr * 72 + r0] = lv;
-            }
-        }
+        *(float4 *)&sm.Dl[lr * 68 + 16 * w + 4 * g] = make_float4(dl[0], dl[1], dl[2], dl[3]);
         __syncthreads();
-
-        // Delta fragments for the two 32-token k-steps
         F8 dF[2];
-        S8 dS[2];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int k0 = 32 * ks + 8 * g;
-            if constexpr (F32) {
-                dF[ks] = ld_f8(&sm.Dl[lr * 68 + k0]);
-            } else {
-                dS[ks].hi = ld_b8(&sm.Dh[lr * 72 + k0]);
-                dS[ks].lo = ld_b8(&sm.Dl[lr * 72 + k0]);
-            }
-        }
+        for (int ks = 0; ks < 2; ++ks) dF[ks] = ld_f8(&sm.Dl[lr * 68 + 32 * ks + 8 * g]);
         // (4) O += Aqk Delta  (row tile w; Aqk is zero above the diagonal)
-        for (int ks = 0; ks < nks_aq; ++ks) {
-            const int k0 = 32 * ks + 8 * g;
-            if constexpr (F32) {
-                oacc = mma_ff(oacc, ld_f8((const float *)(blk + OFF_AQ) + row * CH + k0), dF[ks]);
-            } else {
-                S8 aa;
-                aa.hi = ld_b8((const __bf16 *)(blk + OFF_AQ) + row * CH + k0);
-                aa.lo = ld_b8((const __bf16 *)(blk + OFF_AQ) + CH * CH + row * CH + k0);
-                oacc = mma_ss(oacc, aa, dS[ks]);
-            }
-        }
+        if constexpr (!MAP)
+            for (int ks = 0; ks < nks_aq; ++ks)
+                oacc = mma_ff(oacc, ld_f8((const float *)(blk + OFF_AQ) + row * CH + 32 * ks + 8 * g), dF[ks]);
         // (5) S <- Diag(gamma) S + K~^T Delta  (key rows [32w, 32w+32))
         const float *gam = (const float *)(blk + OFF_GM);
 #pragma unroll
@@ -699,43 +711,41 @@ __global__ __launch_bounds__(256) void chain_kernel(const float *__restrict__ S0
 #pragma unroll
             for (int m = 0; m < 4; ++m) acc[m] = gam[kr + 4 * g + m] * Sr[u][m];
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const int k0 = 32 * ks + 8 * g;
-                if constexpr (F32) {
-                    acc = mma_ff(acc, ld_f8((const float *)(blk + OFF_KT) + (kr + lr) * CH + k0), dF[ks]);
-                } else {
-                    S8 ka;
-                    ka.hi = ld_b8((const __bf16 *)(blk + OFF_KT) + (kr + lr) * CH + k0);
-                    ka.lo = ld_b8((const __bf16 *)(blk + OFF_KT) + D * CH + (kr + lr) * CH + k0);
-                    acc = mma_ss(acc, ka, dS[ks]);
-                }
-            }
+            for (int ks = 0; ks < 2; ++ks)
+                acc = mma_ff(acc, ld_f8((const float *)(blk + OFF_KT) + (kr + lr) * CH + 32 * ks + 8 * g), dF[ks]);
             Sr[u] = acc;
         }
-        // (5b) snapshot after a full chunk that ends a stride
-        if (tab.ck.S && len == CH && (c - cbeg + 1) % tab.ck.stride_chunks == 0) {
-            const int64_t slot = ck_base + (c - cbeg + 1) / tab.ck.stride_chunks - 1;
-            if (slot < tab.ck.cap) {
-                float *dst = tab.ck.S + ((size_t)slot * H + h) * D * D;
+        if constexpr (!MAP) {
+            // (5b) snapshot after a full chunk that ends a stride
+            if (tab.ck.S && len == CH && (c - cseq + 1) % tab.ck.stride_chunks == 0) {
+                const int64_t slot = ck_base + (c - cseq + 1) / tab.ck.stride_chunks - 1;
+                if (slot < tab.ck.cap) {
+                    float *dst = tab.ck.S + ((size_t)slot * H + h) * D * D;
 #pragma unroll
-                for (int u = 0; u < 2; ++u)
+                    for (int u = 0; u < 2; ++u)
 #pragma unroll
-                    for (int m = 0; m < 4; ++m) dst[(size_t)(32 * w + 16 * u + 4 * g + m) * D + col0 + lr] = Sr[u][m];
+                        for (int m = 0; m < 4; ++m)
+                            dst[(size_t)(32 * w + 16 * u + 4 * g + m) * D + col0 + lr] = Sr[u][m];
+                }
+            }
+            // (6) output rows of this chunk
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int t = 16 * w + 4 * g + m;
+                if (t < len) o[((size_t)(t0 + t) * H + h) * D + col0 + lr] = oacc[m];
             }
         }
-        // (6) output rows of this chunk
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int t = 16 * w + 4 * g + m;
-            if (t < len) o[((size_t)(t0 + t) * H + h) * D + col0 + lr] = oacc[m];
-        }
     }
-    if (S_final) {
+    float *dst = nullptr;
+    if (MAP)
+        dst = (bcol ? tab.Bseg : tab.Mseg) + sblk;
+    else if (S_final && j == pn - 1)
+        dst = S_final + ((size_t)n * H + h) * D * D;
+    if (dst) {
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
-            for (int m = 0; m < 4; ++m)
-                S_final[sbase + (size_t)(32 * w + 16 * u + 4 * g + m) * D + col0 + lr] = Sr[u][m];
+            for (int m = 0; m < 4; ++m) dst[(size_t)(32 * w + 16 * u + 4 * g + m) * D + col0 + lr] = Sr[u][m];
     }
 }
 
@@ -770,12 +780,17 @@ int launch_segment_prefill(const __bf16 *q, const __bf16 *k, const __bf16 *v, co
                            float *o, float *S_final, const Ckpt &ck, const Layer &ly, void *ws,
                            hipStream_t stream, hipEvent_t *ev);
 int set_segment_attributes();
+int launch_seg_scan(const float *S0, int N, int H, const int32_t *seg_off, float *Mseg, float *Bseg, float *Sin,
+                    float *S_final, hipStream_t stream);
 
 // bf16 q/k/v run the segment-parallel fused path (kda_segment.hip); fp32 q/k/v
-// run the three-kernel path below with exact fp32 MFMA products.
+// run the path below with exact fp32 MFMA products: the per-chunk operands,
+// the segment maps, the scan over segments (shared with the bf16 path) and the
+// chain over each segment.
 size_t prefill_workspace_bytes(int64_t T_total, int N, int H, bool f32io) {
     if (!f32io) return seg_workspace_bytes(T_total, N, H);
-    return table_bytes(N) + (size_t)max_chunks(T_total, N) * (size_t)H * BLK_BYTES;
+    return table_bytes(N) + (size_t)max_chunks(T_total, N) * (size_t)H * BLK_BYTES +
+           3 * (size_t)seg32_max(T_total, N, H) * H * D * D * sizeof(float);
 }
 
 // ck.S == nullptr: no snapshots (ck.off is ignored; the launchers point it at
@@ -791,6 +806,16 @@ int launch_prefill(const void *q, const void *k, const void *v, bool f32io, cons
     Table tab = carve(ws, N);
     tab.ck = Ckpt{ck.S, tab.ckpt_off, ck.stride_chunks, ck.cap};
     tab.ly = ly;
+    tab.L = seg32_len(T_total, N, H);
+    const int64_t nsm = seg32_max(T_total, N, H);
+    const size_t st = (size_t)nsm * H * D * D;
+    tab.Mseg = (float *)(tab.blocks + (size_t)max_chunks(T_total, N) * (size_t)H * BLK_BYTES);
+    tab.Bseg = tab.Mseg + st;
+    tab.Sin = tab.Bseg + st;
+    // chain grids: 8 (state) or 16 (map) workgroups of 256 per (segment, head)
+    // slot; a launch covers at most 2^32 - 1 work-items
+    const int64_t slots8 = (nsm * H + 7) / 8;
+    if (slots8 * 128 > (int64_t)(UINT32_MAX / 256) || max_chunks(T_total, N) * H > (int64_t)UINT32_MAX) return -1;
     if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return -1;
     hipLaunchKernelGGL(prep_kernel, dim3(1), dim3(256), 0, stream, cu, N, T_total, cu ? (int64_t)0 : T, tab);
     if (ck.S && launch_ckpt_prep(tab.seq_start, tab.seq_end, N, (int64_t)ck.stride_chunks * CH, tab.ckpt_off,
@@ -809,18 +834,18 @@ int launch_prefill(const void *q, const void *k, const void *v, bool f32io, cons
         }
     }
     if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return -1;
-    const int64_t pairs = (int64_t)N * H;
-    const unsigned nwg = (unsigned)(64 * ((pairs + 7) / 8));
-    if (f32io)
-        hipLaunchKernelGGL(chain_kernel<float>, dim3(nwg), dim3(256), 0, stream, S0, N, H, tab, o, S_final);
-    else
-        hipLaunchKernelGGL(chain_kernel<__bf16>, dim3(nwg), dim3(256), 0, stream, S0, N, H, tab, o, S_final);
+    hipLaunchKernelGGL(chain_kernel<true>, dim3((unsigned)(128 * slots8)), dim3(256), 0, stream, N, H, tab, o,
+                       S_final);
+    if (ev && hipEventRecord(ev[3], stream) != hipSuccess) return -1;
+    if (launch_seg_scan(S0, N, H, tab.seg_off, tab.Mseg, tab.Bseg, tab.Sin, S_final, stream) != 0) return -1;
+    if (ev && hipEventRecord(ev[4], stream) != hipSuccess) return -1;
+    hipLaunchKernelGGL(chain_kernel<false>, dim3((unsigned)(64 * slots8)), dim3(256), 0, stream, N, H, tab, o,
+                       S_final);
     if (ly.gate && T_total > 0)
         hipLaunchKernelGGL(gated_rmsnorm_kernel, dim3((unsigned)((T_total * H + 3) / 4)), dim3(256), 0, stream, o,
                            ly.gate, ly.weight, ly.norm_eps, T_total * H);
     if (hipGetLastError() != hipSuccess) return -1;
-    for (int e = 3; e < 6; ++e)
-        if (ev && hipEventRecord(ev[e], stream) != hipSuccess) return -1;
+    if (ev && hipEventRecord(ev[5], stream) != hipSuccess) return -1;
     return 0;
 }
 

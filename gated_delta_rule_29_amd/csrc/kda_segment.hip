@@ -1542,6 +1542,20 @@ int launch_segment_prefill(const __bf16 *q, const __bf16 *k, const __bf16 *v, co
     return 0;
 }
 
+// The scan over segments on its own, for the fp32 path (which has its own
+// per-chunk operands and chain passes but the same segment maps).
+int launch_seg_scan(const float *S0, int N, int H, const int32_t *seg_off, float *Mseg, float *Bseg, float *Sin,
+                    float *S_final, hipStream_t stream) {
+    if ((int64_t)N * H > (int64_t)(UINT32_MAX / 256)) return -1;
+    SegTable tab{};
+    tab.seg_off = const_cast<int32_t *>(seg_off);
+    tab.Mseg = Mseg;
+    tab.Bseg = Bseg;
+    tab.Sin = Sin;
+    hipLaunchKernelGGL(seg_scan_kernel, dim3((unsigned)(N * H), 8), dim3(256), 0, stream, S0, N, H, tab, S_final);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 int set_segment_attributes() { return 0; }  // every kernel here uses static LDS only
 
 }  // namespace kda

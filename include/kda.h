@@ -73,11 +73,12 @@ int kda_version(void);
 /*
  * Bytes of device workspace kda_chunk_fwd needs for T_total packed tokens in
  * n_seqs sequences, H heads and the given q/k/v dtype (0 for an empty problem
- * or invalid sizes).  With bf16 q/k/v the workspace holds a sequence /
- * segment table and, per (segment, head), the segment's state transition, its
- * state offset and its incoming state (3 x 64 KiB); about 55 MB for 64K tokens
- * x 16 heads.  With fp32 q/k/v it holds the per-chunk operands of the chain
- * (145 KiB per chunk and head).  Contents are scratch between calls.
+ * or invalid sizes).  It holds a sequence / segment table, the per-chunk
+ * operands of the chain (78,848 B per chunk and head with bf16 q/k/v, 147,968 B
+ * with fp32) and, per (segment, head), the segment's state transition, its
+ * state offset and its incoming state (3 x 64 KiB): about 1.35 GB for 64K
+ * tokens x 16 heads with bf16 q/k/v, 2.45 GB with fp32.  Contents are scratch
+ * between calls.
  */
 size_t kda_chunk_fwd_workspace_bytes(int64_t T_total, int32_t n_seqs, int32_t H, kda_dtype qkv_dtype);
 
