@@ -242,12 +242,14 @@ __device__ inline int find_seq(const int32_t *chunk_off, int N, int c) {
 constexpr int PG = 132;  // LDS pitch (floats) of [64][128] token-major arrays
 constexpr int PT = 68;   // LDS pitch (floats) of [*][64] arrays
 
+// 77.6 KB, so that two workgroups share a CU.
 template <typename IO>
 struct IntraSmem {
-    float E1[CH * PG];     // e^{G_t - R_{s(t)}}: row factor, in [e^-80, 1]
+    union {
+        float E1[CH * PG];   // e^{G_t - R_{s(t)}}: row factor, in [e^-80, 1] (phases 1-2)
+        float Akk[CH * PT];  // Akk, then T = (I + Akk)^{-1} in place (phases 2-4)
+    } u;
     float KG[D * PT];      // (K * Gam)^T  [channel][token]
-    float Vt[D * PT];      // V^T          [channel][token]
-    float Akk[CH * PT];    // Akk, then T = (I + Akk)^{-1} in place
     double R[5 * D];       // R_s: cumulative log-decay before sub-chunk s (R_4 = G_n)
     float nk[CH], nq[CH];  // 1 / |k_t|, 1 / |q_t| (or 1: inputs already unit length)
     float PF[6 * D];       // e^{R_i - R_j} for the six sub-chunk pairs j < i
@@ -369,7 +371,7 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
             }
             acc += (double)gt;
             Gl[si][u] = acc;
-            sm.E1[t * PG + ch] = sp ? (float)acc : __expf((float)acc);
+            sm.u.E1[t * PG + ch] = sp ? (float)acc : __expf((float)acc);
         }
         sm.R[(s + 1) * D + ch] = acc;  // sub-chunk total, turned into R below
     }
@@ -407,9 +409,7 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
                 const bool ok = t < len;
                 const float kv = ok ? to_f(k[tok(t) + ch]) * sm.nk[t] : 0.f;
                 const float qv = ok ? to_f(q[tok(t) + ch]) * sm.nq[t] : 0.f;
-                const float vv = ok ? to_f(v[tok(t) + ch]) : 0.f;
                 sm.KG[ch * PT + t] = kv * gam;
-                sm.Vt[ch * PT + t] = vv;
                 st_split1<F32>(qt, CH * D, (size_t)t * D + ch, qv * gam);
                 kt_vals[u] = kv * __expf((float)(Gn - Gt));
             }
@@ -434,7 +434,13 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
     // tile list: for mat in {kk, qk}, i in 0..3, j in 0..i (20 tiles), wave wv
     // takes tiles wv, wv+4, ..  The product is formed transposed (column side as
     // the A operand) so that each lane ends up with 4 consecutive columns of a row.
-    for (int tix = wv; tix < 20; tix += 4) {
+    // Akk shares its LDS with E1: the tiles of Akk wait in registers until every
+    // wave is done with E1.
+    f32x4 kkv[3];
+#pragma unroll
+    for (int it = 0; it < 5; ++it) {
+        const int tix = wv + 4 * it;
+        if (tix >= 20) break;
         const int mat = tix / 10, rem = tix % 10;
         int i = 0;
         while ((i + 1) * (i + 2) / 2 <= rem) ++i;
@@ -449,12 +455,12 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
             const float nr = mat == 0 ? sm.nk[rr] : sm.nq[rr];
             const int c0 = 16 * i + 4 * g;
             for (int e = 0; e < D; ++e) {
-                const float xr = rr < len ? to_f(X[tok(rr) + e]) * nr : 0.f, lrr = sm.E1[rr * PG + e];
+                const float xr = rr < len ? to_f(X[tok(rr) + e]) * nr : 0.f, lrr = sm.u.E1[rr * PG + e];
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const int cc = c0 + m;
                     const float kc = cc < len ? to_f(k[tok(cc) + e]) * sm.nk[cc] : 0.f;
-                    acc[m] += xr * kc * __expf(fminf(lrr - sm.E1[cc * PG + e], 0.f));
+                    acc[m] += xr * kc * __expf(fminf(lrr - sm.u.E1[cc * PG + e], 0.f));
                 }
             }
         } else
@@ -469,12 +475,12 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
             for (int e = 0; e < 8; ++e) {
                 float inv, er;
                 if (sp) {  // e^{(R_i - R_j) - (G_c - R_j)} <= 1 for j < i
-                    inv = __expf((float)(sm.R[i * D + c0 + e] - sm.R[j * D + c0 + e]) - sm.E1[cr * PG + c0 + e]);
-                    er = __expf(sm.E1[rr * PG + c0 + e]);
+                    inv = __expf((float)(sm.R[i * D + c0 + e] - sm.R[j * D + c0 + e]) - sm.u.E1[cr * PG + c0 + e]);
+                    er = __expf(sm.u.E1[rr * PG + c0 + e]);
                 } else {
-                    inv = __frcp_rn(sm.E1[cr * PG + c0 + e]);  // e^{R_j - G_c}
+                    inv = __frcp_rn(sm.u.E1[cr * PG + c0 + e]);  // e^{R_j - G_c}
                     if (j < i) inv *= sm.PF[pair_index(i, j) * D + c0 + e];
-                    er = sm.E1[rr * PG + c0 + e];
+                    er = sm.u.E1[rr * PG + c0 + e];
                 }
                 a.v[e] = kc.v[e] * nc * inv;
                 b.v[e] = xr.v[e] * nr * er;
@@ -495,10 +501,21 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
             else
                 val[m] = cc <= rr ? acc[m] : 0.f;
         }
-        if (mat == 0)
-            *(float4 *)&sm.Akk[rr * PT + cb] = make_float4(val[0], val[1], val[2], val[3]);
-        else
+        if (mat == 0) {
+            if (it < 3) kkv[it] = f32x4{val[0], val[1], val[2], val[3]};
+        } else {
             st_split4<F32>(blk + OFF_AQ, CH * CH, (size_t)rr * CH + cb, val[0], val[1], val[2], val[3]);
+        }
+    }
+    __syncthreads();  // E1 is dead: Akk takes its place
+#pragma unroll
+    for (int it = 0; it < 3; ++it) {
+        const int tix = wv + 4 * it;
+        if (tix >= 10) break;
+        int i = 0;
+        while ((i + 1) * (i + 2) / 2 <= tix) ++i;
+        const int j = tix - i * (i + 1) / 2;
+        *(f32x4 *)&sm.u.Akk[(16 * i + lr) * PT + 16 * j + 4 * g] = kkv[it];
     }
     __syncthreads();
 
@@ -511,11 +528,11 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
         for (int r = 0; r < SUB; ++r) {
             float acc = r == m ? 1.f : 0.f;
 #pragma unroll
-            for (int cc = 0; cc < r; ++cc) acc -= sm.Akk[(16 * b + r) * PT + 16 * b + cc] * tcol[cc];
+            for (int cc = 0; cc < r; ++cc) acc -= sm.u.Akk[(16 * b + r) * PT + 16 * b + cc] * tcol[cc];
             tcol[r] = acc;
         }
 #pragma unroll
-        for (int r = 0; r < SUB; ++r) sm.Akk[(16 * b + r) * PT + 16 * b + m] = tcol[r];
+        for (int r = 0; r < SUB; ++r) sm.u.Akk[(16 * b + r) * PT + 16 * b + m] = tcol[r];
     }
     __syncthreads();
     // off-diagonal blocks: T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj (fp32 MFMA, exact products)
@@ -526,8 +543,8 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
             for (int kb = j; kb < i; ++kb) {
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
-                    const float a = sm.Akk[(16 * i + lr) * PT + 16 * kb + 4 * s + g];
-                    const float b = sm.Akk[(16 * kb + 4 * s + g) * PT + 16 * j + lr];
+                    const float a = sm.u.Akk[(16 * i + lr) * PT + 16 * kb + 4 * s + g];
+                    const float b = sm.u.Akk[(16 * kb + 4 * s + g) * PT + 16 * j + lr];
                     X = mfma_f32(a, b, X);
                 }
             }
@@ -538,11 +555,11 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
             f32x4 Y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const float a = sm.Akk[(16 * i + lr) * PT + 16 * i + 4 * g + s];
+                const float a = sm.u.Akk[(16 * i + lr) * PT + 16 * i + 4 * g + s];
                 Y = mfma_f32(a, X[s], Y);
             }
 #pragma unroll
-            for (int m = 0; m < 4; ++m) sm.Akk[(16 * i + 4 * g + m) * PT + 16 * j + lr] = -Y[m];
+            for (int m = 0; m < 4; ++m) sm.u.Akk[(16 * i + 4 * g + m) * PT + 16 * j + lr] = -Y[m];
         }
         __syncthreads();
     }
@@ -551,7 +568,8 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
     // wave wv: row tile rt = wv for W and 3 - wv for U; 8 column tiles each
     for (int pass = 0; pass < 2; ++pass) {
         const int rt = pass == 0 ? wv : 3 - wv;
-        const float *src = pass == 0 ? sm.KG : sm.Vt;
+        // pass 0: (K * Gam)^T from LDS; pass 1: V^T read from global memory
+        // (rows past the end of the sequence as 0)
         const int nks = rt < 2 ? 1 : 2;
         const int r = 16 * rt + lr;
         F8 tb[2];
@@ -560,7 +578,7 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int cc = 32 * ks + 8 * g + e;
-                tb[ks].v[e] = (ks < nks && cc <= r) ? sm.Akk[r * PT + cc] * sm.beta[cc] : 0.f;
+                tb[ks].v[e] = (ks < nks && cc <= r) ? sm.u.Akk[r * PT + cc] * sm.beta[cc] : 0.f;
             }
         }
         S8 tbs[2];
@@ -574,7 +592,16 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 if (ks >= nks) break;
-                const F8 xa = ld_f8(&src[(16 * ct + lr) * PT + 32 * ks + 8 * g]);
+                F8 xa;
+                if (pass == 0) {
+                    xa = ld_f8(&sm.KG[(16 * ct + lr) * PT + 32 * ks + 8 * g]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int t = 32 * ks + 8 * g + e;
+                        xa.v[e] = t < len ? to_f(v[tok(t) + 16 * ct + lr]) : 0.f;
+                    }
+                }
                 if constexpr (F32)
                     acc = mma_ff(acc, xa, tb[ks]);
                 else
