@@ -627,7 +627,8 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
 
 // ----------------------------------------------------------------- chain --
 
-constexpr int NB = 16;  // state columns per workgroup
+constexpr int NCT = 2;         // 16-column tiles per workgroup
+constexpr int NB = 16 * NCT;  // state columns per workgroup
 
 struct ChainSmem {
     float S[NB * 132];  // the state slice, transposed [column][key row]
@@ -647,20 +648,21 @@ __device__ inline int seq_of(const int32_t *off, int N, int x) {
     return lo;
 }
 
-// The chain over one segment of a sequence, 16 state columns per workgroup,
-// exact fp32 MFMA throughout.  The segment map carries a state S entering the
-// segment to M S + B; MAP = true computes the columns of X = [M | B] (128 x
-// 256) by running the chain step from X = [I | 0], with U entering only the B
-// columns; MAP = false runs it from the state the scan gave the segment and
-// writes o (and snapshots, and S_final after a sequence's last segment).
-// Workgroups are numbered so that the column blocks of one (segment, head)
-// share an XCD (and its L2, which serves their common operand block), and the
-// (segment, head) pairs with work come first.
+// The chain over one segment of a sequence, 32 state columns per workgroup
+// (each operand fragment loaded serves both 16-column tiles), exact fp32 MFMA
+// throughout.  The segment map carries a state S entering the segment to
+// M S + B; MAP = true computes the columns of X = [M | B] (128 x 256) by
+// running the chain step from X = [I | 0], with U entering only the B columns;
+// MAP = false runs it from the state the scan gave the segment and writes o
+// (and snapshots, and S_final after a sequence's last segment).  Workgroups
+// are numbered so that the column blocks of one (segment, head) share an XCD
+// (and its L2, which serves their common operand block), and the (segment,
+// head) pairs with work come first.
 template <bool MAP>
 __global__ __launch_bounds__(256) void chain_kernel(int N, int H, Table tab, float *__restrict__ o,
                                                     float *__restrict__ S_final) {
     __shared__ ChainSmem sm;
-    constexpr int NCB = MAP ? 16 : 8;  // column blocks per (segment, head)
+    constexpr int NCB = (MAP ? 2 * D : D) / NB;  // column blocks per (segment, head)
     const int Lw = blockIdx.x;
     const int p = (Lw & 7) + 8 * (Lw / (8 * NCB)), cb = (Lw >> 3) % NCB;
     const int a = p / H, h = p % H;
@@ -670,20 +672,23 @@ __global__ __launch_bounds__(256) void chain_kernel(int N, int H, Table tab, flo
     const int j = a - soff[n];
     const int x = tab.seg_off[n] + j;  // segment index of the maps and states
     const int pn = tab.seg_off[n + 1] - tab.seg_off[n];
-    const bool bcol = MAP && cb >= 8;               // a column of B (U enters)
-    const int col0 = NB * (MAP ? cb & 7 : cb);      // column within M, B or the state
+    const bool bcol = MAP && cb >= NCB / 2;              // columns of B (U enters)
+    const int col0 = NB * (MAP ? cb % (NCB / 2) : cb);  // first column within M, B or the state
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, lr = l & 15;
 
-    // state slice: wave w owns key rows [32w, 32w+32) as two 16-row tiles (C layout)
-    f32x4 Sr[2];
+    // state slice: wave w owns key rows [32w, 32w+32) as two 16-row tiles (C
+    // layout) of each column tile ct (columns col0 + 16 ct + lr)
+    f32x4 Sr[NCT][2];
     const size_t sblk = ((size_t)x * H + h) * D * D;
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int r = 32 * w + 16 * u + 4 * g + m;
-            Sr[u][m] = MAP ? (!bcol && r == col0 + lr ? 1.f : 0.f) : tab.Sin[sblk + (size_t)r * D + col0 + lr];
-        }
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int r = 32 * w + 16 * u + 4 * g + m, cc = col0 + 16 * ct + lr;
+                Sr[ct][u][m] = MAP ? (!bcol && r == cc ? 1.f : 0.f) : tab.Sin[sblk + (size_t)r * D + cc];
+            }
 
     const int cseq = tab.chunk_off[n];  // the sequence's first chunk
     const int cbeg = cseq + j * tab.L, cend = min(tab.chunk_off[n + 1], cbeg + tab.L);
@@ -698,49 +703,77 @@ __global__ __launch_bounds__(256) void chain_kernel(int N, int H, Table tab, flo
 
         // (1) publish the state slice as the B operand of W S and Q~ S
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-            *(float4 *)&sm.S[lr * 132 + 32 * w + 16 * u + 4 * g] = make_float4(Sr[u][0], Sr[u][1], Sr[u][2], Sr[u][3]);
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+                *(float4 *)&sm.S[(16 * ct + lr) * 132 + 32 * w + 16 * u + 4 * g] =
+                    make_float4(Sr[ct][u][0], Sr[ct][u][1], Sr[ct][u][2], Sr[ct][u][3]);
         __syncthreads();
 
         // (2) Delta rows [16w, 16w+16) = U - W S ;  O = Q~ S
-        f32x4 ws = {0.f, 0.f, 0.f, 0.f}, oacc = {0.f, 0.f, 0.f, 0.f};
+        f32x4 ws[NCT], oacc[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) ws[ct] = oacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
         const int row = 16 * w + lr;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const int k0 = 32 * ks + 8 * g;
-            const F8 sb = ld_f8(&sm.S[lr * 132 + k0]);
-            ws = mma_ff(ws, ld_f8((const float *)(blk + OFF_W) + row * D + k0), sb);
-            if constexpr (!MAP) oacc = mma_ff(oacc, ld_f8((const float *)(blk + OFF_QT) + row * D + k0), sb);
-        }
-        f32x4 dl;
+            const F8 wa = ld_f8((const float *)(blk + OFF_W) + row * D + k0);
+            F8 qa;
+            if constexpr (!MAP) qa = ld_f8((const float *)(blk + OFF_QT) + row * D + k0);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const float uv = (!MAP || bcol) ? ((const float *)(blk + OFF_U))[(16 * w + 4 * g + m) * D + col0 + lr] : 0.f;
-            dl[m] = uv - ws[m];
+            for (int ct = 0; ct < NCT; ++ct) {
+                const F8 sb = ld_f8(&sm.S[(16 * ct + lr) * 132 + k0]);
+                ws[ct] = mma_ff(ws[ct], wa, sb);
+                if constexpr (!MAP) oacc[ct] = mma_ff(oacc[ct], qa, sb);
+            }
         }
-
         // (3) publish Delta as the B operand of Aqk Delta and K~^T Delta
-        *(float4 *)&sm.Dl[lr * 68 + 16 * w + 4 * g] = make_float4(dl[0], dl[1], dl[2], dl[3]);
-        __syncthreads();
-        F8 dF[2];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) dF[ks] = ld_f8(&sm.Dl[lr * 68 + 32 * ks + 8 * g]);
+        for (int ct = 0; ct < NCT; ++ct) {
+            f32x4 dl;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const float uv = (!MAP || bcol)
+                                     ? ((const float *)(blk + OFF_U))[(16 * w + 4 * g + m) * D + col0 + 16 * ct + lr]
+                                     : 0.f;
+                dl[m] = uv - ws[ct][m];
+            }
+            *(float4 *)&sm.Dl[(16 * ct + lr) * 68 + 16 * w + 4 * g] = make_float4(dl[0], dl[1], dl[2], dl[3]);
+        }
+        __syncthreads();
+        F8 dF[NCT][2];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) dF[ct][ks] = ld_f8(&sm.Dl[(16 * ct + lr) * 68 + 32 * ks + 8 * g]);
         // (4) O += Aqk Delta  (row tile w; Aqk is zero above the diagonal)
         if constexpr (!MAP)
-            for (int ks = 0; ks < nks_aq; ++ks)
-                oacc = mma_ff(oacc, ld_f8((const float *)(blk + OFF_AQ) + row * CH + 32 * ks + 8 * g), dF[ks]);
+            for (int ks = 0; ks < nks_aq; ++ks) {
+                const F8 aa = ld_f8((const float *)(blk + OFF_AQ) + row * CH + 32 * ks + 8 * g);
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) oacc[ct] = mma_ff(oacc[ct], aa, dF[ct][ks]);
+            }
         // (5) S <- Diag(gamma) S + K~^T Delta  (key rows [32w, 32w+32))
         const float *gam = (const float *)(blk + OFF_GM);
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int kr = 32 * w + 16 * u;
-            f32x4 acc;
+            f32x4 acc[NCT];
 #pragma unroll
-            for (int m = 0; m < 4; ++m) acc[m] = gam[kr + 4 * g + m] * Sr[u][m];
+            for (int m = 0; m < 4; ++m) {
+                const float gm = gam[kr + 4 * g + m];
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-                acc = mma_ff(acc, ld_f8((const float *)(blk + OFF_KT) + (kr + lr) * CH + 32 * ks + 8 * g), dF[ks]);
-            Sr[u] = acc;
+                for (int ct = 0; ct < NCT; ++ct) acc[ct][m] = gm * Sr[ct][u][m];
+            }
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const F8 ka = ld_f8((const float *)(blk + OFF_KT) + (kr + lr) * CH + 32 * ks + 8 * g);
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) acc[ct] = mma_ff(acc[ct], ka, dF[ct][ks]);
+            }
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) Sr[ct][u] = acc[ct];
         }
         if constexpr (!MAP) {
             // (5b) snapshot after a full chunk that ends a stride
@@ -749,17 +782,21 @@ __global__ __launch_bounds__(256) void chain_kernel(int N, int H, Table tab, flo
                 if (slot < tab.ck.cap) {
                     float *dst = tab.ck.S + ((size_t)slot * H + h) * D * D;
 #pragma unroll
-                    for (int u = 0; u < 2; ++u)
+                    for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-                        for (int m = 0; m < 4; ++m)
-                            dst[(size_t)(32 * w + 16 * u + 4 * g + m) * D + col0 + lr] = Sr[u][m];
+                        for (int u = 0; u < 2; ++u)
+#pragma unroll
+                            for (int m = 0; m < 4; ++m)
+                                dst[(size_t)(32 * w + 16 * u + 4 * g + m) * D + col0 + 16 * ct + lr] = Sr[ct][u][m];
                 }
             }
             // (6) output rows of this chunk
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const int t = 16 * w + 4 * g + m;
-                if (t < len) o[((size_t)(t0 + t) * H + h) * D + col0 + lr] = oacc[m];
+                if (t < len)
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct) o[((size_t)(t0 + t) * H + h) * D + col0 + 16 * ct + lr] = oacc[ct][m];
             }
         }
     }
@@ -770,9 +807,12 @@ __global__ __launch_bounds__(256) void chain_kernel(int N, int H, Table tab, flo
         dst = S_final + ((size_t)n * H + h) * D * D;
     if (dst) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+        for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-            for (int m = 0; m < 4; ++m) dst[(size_t)(32 * w + 16 * u + 4 * g + m) * D + col0 + lr] = Sr[u][m];
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    dst[(size_t)(32 * w + 16 * u + 4 * g + m) * D + col0 + 16 * ct + lr] = Sr[ct][u][m];
     }
 }
 
@@ -839,7 +879,7 @@ int launch_prefill(const void *q, const void *k, const void *v, bool f32io, cons
     tab.Mseg = (float *)(tab.blocks + (size_t)max_chunks(T_total, N) * (size_t)H * BLK_BYTES);
     tab.Bseg = tab.Mseg + st;
     tab.Sin = tab.Bseg + st;
-    // chain grids: 8 (state) or 16 (map) workgroups of 256 per (segment, head)
+    // chain grids: 4 (state) or 8 (map) workgroups of 256 per (segment, head)
     // slot; a launch covers at most 2^32 - 1 work-items
     const int64_t slots8 = (nsm * H + 7) / 8;
     if (slots8 * 128 > (int64_t)(UINT32_MAX / 256) || max_chunks(T_total, N) * H > (int64_t)UINT32_MAX) return -1;
@@ -861,13 +901,13 @@ int launch_prefill(const void *q, const void *k, const void *v, bool f32io, cons
         }
     }
     if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return -1;
-    hipLaunchKernelGGL(chain_kernel<true>, dim3((unsigned)(128 * slots8)), dim3(256), 0, stream, N, H, tab, o,
-                       S_final);
+    hipLaunchKernelGGL(chain_kernel<true>, dim3((unsigned)(8 * (2 * D / NB) * slots8)), dim3(256), 0, stream, N, H,
+                       tab, o, S_final);
     if (ev && hipEventRecord(ev[3], stream) != hipSuccess) return -1;
     if (launch_seg_scan(S0, N, H, tab.seg_off, tab.Mseg, tab.Bseg, tab.Sin, S_final, stream) != 0) return -1;
     if (ev && hipEventRecord(ev[4], stream) != hipSuccess) return -1;
-    hipLaunchKernelGGL(chain_kernel<false>, dim3((unsigned)(64 * slots8)), dim3(256), 0, stream, N, H, tab, o,
-                       S_final);
+    hipLaunchKernelGGL(chain_kernel<false>, dim3((unsigned)(8 * (D / NB) * slots8)), dim3(256), 0, stream, N, H,
+                       tab, o, S_final);
     if (ly.gate && T_total > 0)
         hipLaunchKernelGGL(gated_rmsnorm_kernel, dim3((unsigned)((T_total * H + 3) / 4)), dim3(256), 0, stream, o,
                            ly.gate, ly.weight, ly.norm_eps, T_total * H);
