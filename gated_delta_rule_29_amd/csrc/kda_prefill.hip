@@ -348,6 +348,16 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
     // the exponential turns into relative error of every decay factor.  Only
     // the final argument of each exponential is rounded to fp32.
     double Gl[2][SUB];
+    // All of this thread's z values are loaded before the first is used (rows
+    // past the end read row 0 and are masked), so their latencies overlap.
+    float zr[2][SUB];
+#pragma unroll
+    for (int si = 0; si < 2; ++si)
+#pragma unroll
+        for (int u = 0; u < SUB; ++u) {
+            const int t = (half + 2 * si) * SUB + u, tc = t < len ? t : 0;
+            zr[si][u] = tab.ly.zu ? 0.f : (zh ? z[(size_t)(t0 + tc) * H + h] : z[tok(tc) + ch]);
+        }
 #pragma unroll
     for (int si = 0; si < 2; ++si) {
         const int s = half + 2 * si;
@@ -365,7 +375,7 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
                     for (int j = 0; j < r; ++j) acc += (float)ur[j] * (float)wr[j];
                     zv = acc;
                 } else {
-                    zv = zh ? z[(size_t)(t0 + t) * H + h] : z[tok(t) + ch];
+                    zv = zr[si][u];
                 }
                 gt = sp ? softplus_gate(eA, zv) : kda_gate(eA, zv);
             }
@@ -400,15 +410,21 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
         for (int si = 0; si < 2; ++si) {
             const int s = half + 2 * si;
             const double Rs = sm.R[s * D + ch];
-            float kt_vals[SUB];
+            float kt_vals[SUB], kr[SUB], qr[SUB];
+#pragma unroll
+            for (int u = 0; u < SUB; ++u) {  // loads first (rows past the end read row 0)
+                const int t = s * SUB + u, tc = t < len ? t : 0;
+                kr[u] = to_f(k[tok(tc) + ch]);
+                qr[u] = to_f(q[tok(tc) + ch]);
+            }
 #pragma unroll
             for (int u = 0; u < SUB; ++u) {
                 const int t = s * SUB + u;
                 const double Gt = Rs + Gl[si][u];
                 const float gam = __expf((float)Gt);
                 const bool ok = t < len;
-                const float kv = ok ? to_f(k[tok(t) + ch]) * sm.nk[t] : 0.f;
-                const float qv = ok ? to_f(q[tok(t) + ch]) * sm.nq[t] : 0.f;
+                const float kv = ok ? kr[u] * sm.nk[t] : 0.f;
+                const float qv = ok ? qr[u] * sm.nq[t] : 0.f;
                 sm.KG[ch * PT + t] = kv * gam;
                 st_split1<F32>(qt, CH * D, (size_t)t * D + ch, qv * gam);
                 kt_vals[u] = kv * __expf((float)(Gn - Gt));
@@ -463,13 +479,21 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
                     acc[m] += xr * kc * __expf(fminf(lrr - sm.u.E1[cc * PG + e], 0.f));
                 }
             }
-        } else
+        } else {
+        // the tile's row fragments for all four k-steps, loaded before the first
+        // product (rows past the end read row 0 and are zeroed)
+        F8 kcs[4], xrs[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            kcs[ks] = ld_io8(k + tok(cr < len ? cr : 0) + 32 * ks + 8 * g);
+            xrs[ks] = ld_io8(X + tok(rr < len ? rr : 0) + 32 * ks + 8 * g);
+        }
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const int c0 = 32 * ks + 8 * g;
             F8 a, b;
-            const F8 kc = cr < len ? ld_io8(k + tok(cr) + c0) : F8{};
-            const F8 xr = rr < len ? ld_io8(X + tok(rr) + c0) : F8{};
+            const F8 kc = cr < len ? kcs[ks] : F8{};
+            const F8 xr = rr < len ? xrs[ks] : F8{};
             const float nc = sm.nk[cr], nr = mat == 0 ? sm.nk[rr] : sm.nq[rr];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -489,6 +513,7 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
                 acc = mma_ff(acc, a, b);
             else
                 acc = mma_ss(acc, split8(a), split8(b));
+        }
         }
         // acc[m] = M[r = rr][c = 16 j + 4 g + m]
         const int cb = 16 * j + 4 * g;
@@ -588,6 +613,19 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
         }
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct) {
+            // pass 1: this column tile's V values, all loaded before its products
+            // (rows past the end read row 0 and are zeroed)
+            F8 vcol[2];
+            if (pass == 1) {
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int t = 32 * ks + 8 * g + e;
+                        const float x = to_f(v[tok(t < len ? t : 0) + 16 * ct + lr]);
+                        vcol[ks].v[e] = t < len ? x : 0.f;
+                    }
+            }
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
@@ -596,11 +634,7 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
                 if (pass == 0) {
                     xa = ld_f8(&sm.KG[(16 * ct + lr) * PT + 32 * ks + 8 * g]);
                 } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int t = 32 * ks + 8 * g + e;
-                        xa.v[e] = t < len ? to_f(v[tok(t) + 16 * ct + lr]) : 0.f;
-                    }
+                    xa = vcol[ks];
                 }
                 if constexpr (F32)
                     acc = mma_ff(acc, xa, tb[ks]);
