@@ -669,6 +669,16 @@ struct ChainSmem {
     float Dl[NB * 68];  // Delta, transposed [column][token]
 };
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS accesses
+// (lgkmcnt), not for its global loads in flight, which __syncthreads' fence
+// would also wait for.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // largest n in [0, N) with off[n] <= x (for x < off[N] that is the owner of x)
 __device__ inline int seq_of(const int32_t *off, int N, int x) {
     int lo = 0, hi = N - 1;
@@ -730,8 +740,55 @@ __global__ __launch_bounds__(256) void chain_kernel(int N, int H, Table tab, flo
     const int nks_aq = w < 2 ? 1 : 2;  // 32-token k-steps of Aqk row tile w
     const int64_t ck_base = tab.ck.S ? tab.ck.off[n] : 0;
 
+    // Operands of one chunk, in registers.  The barriers wait only for LDS
+    // traffic, so loads stay in flight across them.  The map pass loads each
+    // group for chunk c + 1 as soon as chunk c has used it (the last chunk
+    // re-reads itself); the state pass, which has no registers to spare for
+    // that, issues all of chunk c's loads at the top of its step.
+    constexpr bool PF = MAP;
+    const int row = 16 * w + lr;
+    F8 wf[4], qf[4], kf[2][2], af[2];
+    float uv[NCT][4], gmv[2][4];
+    auto load_wq = [&](const char *blk) __attribute__((always_inline)) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            wf[ks] = ld_f8((const float *)(blk + OFF_W) + row * D + 32 * ks + 8 * g);
+            if constexpr (!MAP) qf[ks] = ld_f8((const float *)(blk + OFF_QT) + row * D + 32 * ks + 8 * g);
+        }
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                uv[ct][m] = (!MAP || bcol)
+                                ? ((const float *)(blk + OFF_U))[(16 * w + 4 * g + m) * D + col0 + 16 * ct + lr]
+                                : 0.f;
+    };
+    auto load_ka = [&](const char *blk) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int kr = 32 * w + 16 * u;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+                kf[u][ks] = ld_f8((const float *)(blk + OFF_KT) + (kr + lr) * CH + 32 * ks + 8 * g);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) gmv[u][m] = ((const float *)(blk + OFF_GM))[kr + 4 * g + m];
+        }
+        if constexpr (!MAP)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) af[ks] = ld_f8((const float *)(blk + OFF_AQ) + row * CH + 32 * ks + 8 * g);
+    };
+    auto block = [&](int cc) { return tab.blocks + ((size_t)cc * H + h) * BLK_BYTES; };
+    if (PF && cbeg < cend) {
+        load_wq(block(cbeg));
+        load_ka(block(cbeg));
+    }
+
     for (int c = cbeg; c < cend; ++c) {
-        const char *blk = tab.blocks + ((size_t)c * H + h) * BLK_BYTES;
+        const char *nblk = block(min(c + 1, cend - 1));
+        if (!PF) {
+            load_wq(block(c));
+            load_ka(block(c));
+        }
         const int64_t t0 = sstart + (int64_t)(c - cseq) * CH;
         const int len = (int)min((int64_t)CH, send - t0);
 
@@ -742,40 +799,33 @@ __global__ __launch_bounds__(256) void chain_kernel(int N, int H, Table tab, flo
             for (int u = 0; u < 2; ++u)
                 *(float4 *)&sm.S[(16 * ct + lr) * 132 + 32 * w + 16 * u + 4 * g] =
                     make_float4(Sr[ct][u][0], Sr[ct][u][1], Sr[ct][u][2], Sr[ct][u][3]);
-        __syncthreads();
+        lds_barrier();
 
         // (2) Delta rows [16w, 16w+16) = U - W S ;  O = Q~ S
         f32x4 ws[NCT], oacc[NCT];
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) ws[ct] = oacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int row = 16 * w + lr;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            const int k0 = 32 * ks + 8 * g;
-            const F8 wa = ld_f8((const float *)(blk + OFF_W) + row * D + k0);
-            F8 qa;
-            if constexpr (!MAP) qa = ld_f8((const float *)(blk + OFF_QT) + row * D + k0);
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
-                const F8 sb = ld_f8(&sm.S[(16 * ct + lr) * 132 + k0]);
-                ws[ct] = mma_ff(ws[ct], wa, sb);
-                if constexpr (!MAP) oacc[ct] = mma_ff(oacc[ct], qa, sb);
+                const F8 sb = ld_f8(&sm.S[(16 * ct + lr) * 132 + 32 * ks + 8 * g]);
+                ws[ct] = mma_ff(ws[ct], wf[ks], sb);
+                if constexpr (!MAP) oacc[ct] = mma_ff(oacc[ct], qf[ks], sb);
             }
         }
+        f32x4 dl[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) dl[ct][m] = uv[ct][m] - ws[ct][m];
+        if (PF) load_wq(nblk);
         // (3) publish Delta as the B operand of Aqk Delta and K~^T Delta
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            f32x4 dl;
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const float uv = (!MAP || bcol)
-                                     ? ((const float *)(blk + OFF_U))[(16 * w + 4 * g + m) * D + col0 + 16 * ct + lr]
-                                     : 0.f;
-                dl[m] = uv - ws[ct][m];
-            }
-            *(float4 *)&sm.Dl[(16 * ct + lr) * 68 + 16 * w + 4 * g] = make_float4(dl[0], dl[1], dl[2], dl[3]);
-        }
-        __syncthreads();
+        for (int ct = 0; ct < NCT; ++ct)
+            *(float4 *)&sm.Dl[(16 * ct + lr) * 68 + 16 * w + 4 * g] =
+                make_float4(dl[ct][0], dl[ct][1], dl[ct][2], dl[ct][3]);
+        lds_barrier();
         F8 dF[NCT][2];
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
@@ -783,32 +833,27 @@ __global__ __launch_bounds__(256) void chain_kernel(int N, int H, Table tab, flo
             for (int ks = 0; ks < 2; ++ks) dF[ct][ks] = ld_f8(&sm.Dl[(16 * ct + lr) * 68 + 32 * ks + 8 * g]);
         // (4) O += Aqk Delta  (row tile w; Aqk is zero above the diagonal)
         if constexpr (!MAP)
-            for (int ks = 0; ks < nks_aq; ++ks) {
-                const F8 aa = ld_f8((const float *)(blk + OFF_AQ) + row * CH + 32 * ks + 8 * g);
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) oacc[ct] = mma_ff(oacc[ct], aa, dF[ct][ks]);
-            }
+            for (int ks = 0; ks < 2; ++ks)
+                if (ks < nks_aq)
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct) oacc[ct] = mma_ff(oacc[ct], af[ks], dF[ct][ks]);
         // (5) S <- Diag(gamma) S + K~^T Delta  (key rows [32w, 32w+32))
-        const float *gam = (const float *)(blk + OFF_GM);
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const int kr = 32 * w + 16 * u;
             f32x4 acc[NCT];
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const float gm = gam[kr + 4 * g + m];
+            for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) acc[ct][m] = gm * Sr[ct][u][m];
-            }
+                for (int m = 0; m < 4; ++m) acc[ct][m] = gmv[u][m] * Sr[ct][u][m];
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const F8 ka = ld_f8((const float *)(blk + OFF_KT) + (kr + lr) * CH + 32 * ks + 8 * g);
+            for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) acc[ct] = mma_ff(acc[ct], ka, dF[ct][ks]);
-            }
+                for (int ct = 0; ct < NCT; ++ct) acc[ct] = mma_ff(acc[ct], kf[u][ks], dF[ct][ks]);
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) Sr[ct][u] = acc[ct];
         }
+        if (PF) load_ka(nblk);
         if constexpr (!MAP) {
             // (5b) snapshot after a full chunk that ends a stride
             if (tab.ck.S && len == CH && (c - cseq + 1) % tab.ck.stride_chunks == 0) {
