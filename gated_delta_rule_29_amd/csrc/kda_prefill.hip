@@ -34,10 +34,10 @@
 //                 segment's chunks and forms Delta, the output and the next
 //                 state with MFMA.
 //
-// Precision: q, k, v arrive in bf16 (exact MFMA operands).  Intermediates that
-// carry fp32 information enter bf16 MFMAs as an unevaluated hi + lo pair
-// (hi*hi + hi*lo + lo*hi), except W in W S, which tolerates a single bf16
-// rounding.  The fp32 I/O build uses fp32 MFMA for every product.
+// This file serves fp32 q/k/v (bf16 q/k/v take kda_segment.hip's path): every
+// product is an exact fp32 MFMA.  intra_kernel is written over the I/O type
+// (with bf16, fp32 intermediates would enter MFMA as hi + lo bf16 pairs); the
+// library instantiates it for fp32 only.
 #include "kda_common.hpp"
 
 namespace kda {
@@ -971,13 +971,8 @@ int launch_prefill(const void *q, const void *k, const void *v, bool f32io, cons
     if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return -1;
     if (T_total > 0) {
         const size_t smem = sizeof(IntraSmem<float>);
-        if (f32io) {
-            hipLaunchKernelGGL(intra_kernel<float>, dim3((unsigned)nc, (unsigned)H), dim3(256), smem, stream,
-                               (const float *)q, (const float *)k, (const float *)v, z, beta, A, N, H, tab);
-        } else {
-            hipLaunchKernelGGL(intra_kernel<__bf16>, dim3((unsigned)nc, (unsigned)H), dim3(256), smem, stream,
-                               (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, z, beta, A, N, H, tab);
-        }
+        hipLaunchKernelGGL(intra_kernel<float>, dim3((unsigned)nc, (unsigned)H), dim3(256), smem, stream,
+                           (const float *)q, (const float *)k, (const float *)v, z, beta, A, N, H, tab);
     }
     if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return -1;
     hipLaunchKernelGGL(chain_kernel<true>, dim3((unsigned)(8 * (2 * D / NB) * slots8)), dim3(256), 0, stream, N, H,
@@ -1000,9 +995,6 @@ int set_prefill_attributes() {
     const int smem = (int)sizeof(IntraSmem<float>);
     if (hipFuncSetAttribute((const void *)intra_kernel<float>, hipFuncAttributeMaxDynamicSharedMemorySize, smem) !=
         hipSuccess)
-        return -1;
-    if (hipFuncSetAttribute((const void *)intra_kernel<__bf16>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            smem) != hipSuccess)
         return -1;
     return 0;
 }
