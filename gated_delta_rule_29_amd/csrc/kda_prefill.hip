@@ -26,11 +26,11 @@
 //                 blocked forward substitution, W and U on MFMA; writes the
 //                 per-chunk operands of the chain to the workspace;
 //   chain_kernel<true>   the affine map S -> M S + B of every segment but a
-//                 sequence's last, one workgroup per (segment, head, 16 of
+//                 sequence's last, one workgroup per (segment, head, 32 of
 //                 the 256 columns of [M | B]);
 //   seg_scan_kernel (kda_segment.hip)  the state entering each segment;
-//   chain_kernel<false>  one workgroup per (segment, head, 16 value columns):
-//                 keeps its 128 x 16 fp32 state slice in registers across the
+//   chain_kernel<false>  one workgroup per (segment, head, 32 value columns):
+//                 keeps its 128 x 32 fp32 state slice in registers across the
 //                 segment's chunks and forms Delta, the output and the next
 //                 state with MFMA.
 //
