@@ -212,10 +212,11 @@ def test_decode_steps_continue_prefill():
 
 
 @pytest.mark.parametrize("io", ["bf16", "f32"])
-@pytest.mark.parametrize("H,T", [(32, 4096), (64, 1000), (1, 5000)])
+@pytest.mark.parametrize("H,T", [(32, 4096), (64, 1000), (1, 5000), (200, 300)])
 def test_head_counts(H, T, io):
     """Other head counts change how many segments each head is cut into (about 256
-    (segment, head) pairs in all with bf16 q/k/v, 128 with fp32)."""
+    (segment, head) pairs in all with bf16 q/k/v, 128 with fp32; with 200 heads every
+    head is one segment on either path)."""
     d = synth.prefill_inputs(3800 + H, T, H, dtype=io, s0_std=0.02)
     say(f"case heads H={H} T={T} io={io}")
     o, Sf = run_prefill(d, S0=d["S0"], io=io)
