@@ -325,8 +325,10 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
             sk += __shfl_xor(sk, 2);
             sq += __shfl_xor(sq, 1);
             sq += __shfl_xor(sq, 2);
-            nk = 1.f / __fsqrt_rn(sk + tab.ly.qk_eps);
-            nq = 1.f / __fsqrt_rn(sq + tab.ly.qk_eps);
+            // rows past the end get 0, not 1 / sqrt(0 + eps): with eps = 0 that
+            // would be inf, and inf times a zero row is NaN
+            nk = tr < len ? 1.f / __fsqrt_rn(sk + tab.ly.qk_eps) : 0.f;
+            nq = tr < len ? 1.f / __fsqrt_rn(sq + tab.ly.qk_eps) : 0.f;
         }
         if ((l & 3) == 0) {
             sm.nk[tr] = nk;

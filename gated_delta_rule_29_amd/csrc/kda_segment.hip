@@ -114,6 +114,14 @@ __device__ __forceinline__ uint32_t row_umax16(uint32_t x) {
     x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x140, 0xF, 0xF, false));
     return x;
 }
+// Unsigned maximum over the whole wave, wave-uniform (so the compiler keeps it
+// in a scalar register and branches on it without divergence).
+__device__ __forceinline__ uint32_t wave_umax(uint32_t x) {
+    x = row_umax16(x);
+    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)x, 0), b = (uint32_t)__builtin_amdgcn_readlane((int)x, 16),
+                   c = (uint32_t)__builtin_amdgcn_readlane((int)x, 32), d = (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
+    return max(max(a, b), max(c, d));
+}
 // max |u| over a lane's four values as the bits of a non-negative float: as
 // unsigned integers these order like the values, and NaN orders above inf, so
 // a NaN is kept (fmaxf would drop it).
@@ -149,12 +157,14 @@ __device__ __forceinline__ UBlk u_encode(f32x4 u, uint32_t bmax_bits) {
     return {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pk_i16(qv[0], qv[1])),
             __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pk_i16(qv[2], qv[3])), sc};
 }
-__device__ __forceinline__ f32x4 u_decode(UBlk b) {
+// Decoded and multiplied by 2^e (exact unless the result leaves fp32's normal range).
+__device__ __forceinline__ f32x4 u_decode(UBlk b, int e) {
+    const float sc = __builtin_amdgcn_ldexpf(b.sc, e);
     f32x4 u;
-    u[0] = (float)(int)(int16_t)(b.q01 & 0xFFFF) * b.sc;
-    u[1] = (float)((int)b.q01 >> 16) * b.sc;
-    u[2] = (float)(int)(int16_t)(b.q23 & 0xFFFF) * b.sc;
-    u[3] = (float)((int)b.q23 >> 16) * b.sc;
+    u[0] = (float)(int)(int16_t)(b.q01 & 0xFFFF) * sc;
+    u[1] = (float)((int)b.q01 >> 16) * sc;
+    u[2] = (float)(int)(int16_t)(b.q23 & 0xFFFF) * sc;
+    u[3] = (float)((int)b.q23 >> 16) * sc;
     return u;
 }
 
@@ -500,9 +510,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GK == GATE_
                     sk += __shfl_xor(sk, 2);
                     sq += __shfl_xor(sq, 1);
                     sq += __shfl_xor(sq, 2);
-                    if ((l & 3) == 0) {
-                        sm.nk[tr] = 1.f / __fsqrt_rn(sk + tab.ly.qk_eps);
-                        sm.nq[tr] = 1.f / __fsqrt_rn(sq + tab.ly.qk_eps);
+                    if ((l & 3) == 0) {  // rows past the end: 0 (1 / sqrt(0) would make NaN with qk_eps = 0)
+                        sm.nk[tr] = tr < len ? 1.f / __fsqrt_rn(sk + tab.ly.qk_eps) : 0.f;
+                        sm.nq[tr] = tr < len ? 1.f / __fsqrt_rn(sq + tab.ly.qk_eps) : 0.f;
                     }
                     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
                     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -1049,6 +1059,17 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
                 else
                     X[rt][ct][m] = tab.Sin[sblk + (size_t)r * D + col];
             }
+    // X holds this wave's state columns times 2^E.  The state and Delta enter
+    // the products as fp16, whose range (2^-14 .. 65504) a state of any other
+    // magnitude would leave: the map is linear in (S, U) column by column, so
+    // the wave may carry its columns at any power-of-two scale, and it picks E
+    // at every step so that the state and the chunk's U stay below 2^11 (and
+    // above 2^7).  Then |Delta| = |U - W S| < 2^11 + sqrt(128) 2^11 < 2^15
+    // (with unit keys and beta in [0, 1] each row of W S is bounded by the
+    // norm of a state column), and values 2^-21 below the largest still get
+    // fp16's full precision.  U is decoded, and o and the states leave, at the
+    // matching scale; powers of two are exact.
+    int E = 0;
 
     // Past the segment's last chunk the copies read nothing (and U is 0).
     using UReg = UBlk;  // as stored: decoded at the start of the step that uses it
@@ -1082,7 +1103,8 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
             for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    const float val = X[rt][ct][m];  // a value: a bit-cast of the element expression reads element 0
+                    // a value: a bit-cast of the element expression reads element 0
+                    const float val = __builtin_amdgcn_ldexpf(X[rt][ct][m], -E);
                     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val), rs, lane_off,
                                                           ((16 * rt + m) * D + 16 * ct) * 4, 0);
                 }
@@ -1206,11 +1228,43 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __builtin_amdgcn_s_barrier();
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        // The step's scale: e bounds max(|X|, |U 2^E|) by 2^(e - 126) (fp32
+        // exponent fields; |U| < 2^14 sc in its block format).  Inf or NaN
+        // present: keep E, the result is not finite either way.
+        {
+            float mx = 0.f, ms = 0.f;
+#pragma unroll
+            for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const float xv = X[rt][ct][m];
+                        mx = fmaxf(mx, fabsf(xv));
+                    }
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) ms = fmaxf(ms, Dcur[rt][ct].sc);
+            const int es = (int)(__builtin_bit_cast(uint32_t, mx) >> 23), eu = (int)(__builtin_bit_cast(uint32_t, ms) >> 23);
+            const int el = (es == 255 || eu == 255) ? 0xFFFF : max(es, eu ? max(eu + 13 + E, 0) : 0);
+            const int e = (int)wave_umax((uint32_t)el);
+            if (e != 0xFFFF && e != 0 && (e < 134 || e > 137)) {
+                const int sh = 136 - e;
+                E += sh;
+#pragma unroll
+                for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                        for (int m = 0; m < 4; ++m) X[rt][ct][m] = __builtin_amdgcn_ldexpf(X[rt][ct][m], sh);
+            }
+        }
         f32x4 Dl[4][NCT];  // Delta = U - W S accumulates onto this chunk's U
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) Dl[rt][ct] = u_decode(Dcur[rt][ct]);
+            for (int ct = 0; ct < NCT; ++ct) Dl[rt][ct] = u_decode(Dcur[rt][ct], E);
         if constexpr (!PASS_A) {
             if (chunk > cbeg) store_o(O, t0_prev, len_prev, (chunk - 1) & 1);
             if (ep) dma_gate(chunk);
@@ -1295,6 +1349,10 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
         if constexpr (!PASS_A) {
             t0_prev = t0;
             len_prev = len;
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) O[rt][m] = __builtin_amdgcn_ldexpf(O[rt][m], -E);  // to o's own scale
             if (ep) {  // this wave's per-row sums of squares of O
                 float *pp = opart + (chunk & 1) * CH_NW * CH + wv * CH;
 #pragma unroll
@@ -1355,7 +1413,8 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
             for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
                 for (int m = 0; m < 4; ++m)
-                    dst[sblk + (size_t)(16 * rt + 4 * g + m) * D + cbase + 16 * ct + lr] = X[rt][ct][m];
+                    dst[sblk + (size_t)(16 * rt + 4 * g + m) * D + cbase + 16 * ct + lr] =
+                        __builtin_amdgcn_ldexpf(X[rt][ct][m], -E);
     } else {
         if (S_final && j == pn - 1) {
             const size_t fb = ((size_t)n * H + h) * D * D;
@@ -1365,7 +1424,8 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
                 for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
                     for (int m = 0; m < 4; ++m)
-                        S_final[fb + (size_t)(16 * rt + 4 * g + m) * D + colw + 16 * ct + lr] = X[rt][ct][m];
+                        S_final[fb + (size_t)(16 * rt + 4 * g + m) * D + colw + 16 * ct + lr] =
+                            __builtin_amdgcn_ldexpf(X[rt][ct][m], -E);
         }
     }
 }

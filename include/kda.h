@@ -29,7 +29,16 @@
  *   - q and k are expected to be L2-normalised by the caller (the KDA layer
  *     normalises them before the operator); the operator does not normalise and
  *     applies no query scale.
- *   - beta is the final delta strength (already squashed into (0, 1)).
+ *   - beta is the final delta strength (already squashed into (0, 1)); 0 and 1
+ *     are valid.
+ *   - Input scale.  With bf16 q/k/v the state and Delta enter the chunk
+ *     products as fp16 values; each workgroup carries its state columns at a
+ *     power-of-two scale it re-picks every chunk, so o and S_final keep their
+ *     accuracy for v and S0 of any magnitude whose states and outputs stay in
+ *     fp32's normal range (tested from 2^-60 to 2^60 times unit scale).  That
+ *     bound relies on the documented preconditions: unit-length keys and
+ *     beta in [0, 1].  The fp32 path and the decode step compute in fp32
+ *     throughout.
  *   - z = -inf gives alpha = 1 exactly and z = +inf gives alpha = e^-5; both are
  *     valid.  NaN inputs propagate to the outputs.
  *   - Pointers must be 16-byte aligned (KDA_ERR_ALIGN otherwise).
