@@ -21,7 +21,7 @@ import os
 
 import torch
 
-__all__ = ["kda_chunk_fwd", "kda_decode_step", "kda_chunk_fwd_workspace_bytes", "KDAError", "lib_path",
+__all__ = ["kda_chunk_fwd", "kda_chunk_fwd_noalloc", "kda_decode_step", "kda_chunk_fwd_workspace_bytes", "KDAError", "lib_path",
            "HEAD_DIM", "status_str", "load", "LayerOpts", "GATES"]
 
 HEAD_DIM = 128
@@ -84,6 +84,8 @@ def load():
                                   sz, P]
     lib.kda_chunk_fwd.restype = ctypes.c_int
     lib.kda_chunk_fwd_timed.argtypes = lib.kda_chunk_fwd.argtypes + [P]
+    lib.kda_chunk_fwd_noalloc.argtypes = lib.kda_chunk_fwd.argtypes[:17] + [P]
+    lib.kda_chunk_fwd_noalloc.restype = ctypes.c_int
     lib.kda_chunk_fwd_ckpt.argtypes = lib.kda_chunk_fwd.argtypes[:17] + [P, i64, i64] + lib.kda_chunk_fwd.argtypes[17:]
     lib.kda_chunk_fwd_ckpt.restype = ctypes.c_int
     lib.kda_chunk_fwd_layer.argtypes = (lib.kda_chunk_fwd.argtypes[:15] + [ctypes.POINTER(LayerOpts), P, P, P, i64, i64]
@@ -250,6 +252,43 @@ def kda_chunk_fwd(q, k, v, g_raw, beta, A, S0=None, cu_seqlens=None, *, o=None, 
     if squeeze:
         o = o.squeeze(0)
     return o, S_final
+
+
+def kda_chunk_fwd_noalloc(q, k, v, g_raw, beta, A, o, S0=None, cu_seqlens=None, S_final=None, stream=None):
+    """kda_chunk_fwd on the library's own device-resident workspace (kda_chunk_fwd_noalloc): nothing is
+    allocated, so the caller passes o ([.., H, 128] fp32, shaped like v) and, if wanted, S_final
+    ([N, H, 128, 128] fp32).  Problems larger than the workspace raise KDAError (KDA_ERR_WORKSPACE);
+    calls that overlap on one GPU race.  Arguments are otherwise as kda_chunk_fwd."""
+    lib = load()
+    if q.dim() == 3:
+        q, k, v, beta, g_raw = (x.unsqueeze(0) for x in (q, k, v, beta, g_raw))
+        o = o.unsqueeze(0)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, 128] or [T, H, 128]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    _need(q, "q", (torch.bfloat16, torch.float32), dev)
+    for t, name in ((k, "k"), (v, "v")):
+        _need(t, name, (q.dtype,), dev)
+    for t, name in ((g_raw, "g_raw"), (beta, "beta"), (A, "A"), (o, "o")):
+        _need(t, name, (torch.float32,), dev)
+    if k.shape != q.shape or g_raw.shape != q.shape or v.shape[:3] != q.shape[:3] or beta.shape != (B, T, H) \
+            or A.shape != (H,) or o.shape != (B, T, H, dv):
+        raise ValueError("inconsistent shapes")
+    N = B
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", (torch.int32,), dev)
+        N = cu_seqlens.numel() - 1
+    for t, name in ((S0, "S0"), (S_final, "S_final")):
+        if t is not None:
+            _need(t, name, (torch.float32,), dev)
+            if t.shape != (N, H, dk, dv):
+                raise ValueError(f"{name} must be [{N}, {H}, {dk}, {dv}]")
+    dtype = KDA_BF16 if q.dtype == torch.bfloat16 else KDA_F32
+    rc = lib.kda_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), dtype, _ptr(g_raw), _ptr(beta), _ptr(A), _ptr(S0),
+                                   _ptr(cu_seqlens), B, T, H, N, dk, dv, _ptr(o), _ptr(S_final), _stream(stream))
+    _check(rc, "kda_chunk_fwd_noalloc")
 
 
 def kda_decode_step(q, k, v, g_raw, beta, A, S, *, o=None, stream=None, qk_l2norm=False, qk_eps=1e-6,

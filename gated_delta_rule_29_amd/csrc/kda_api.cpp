@@ -39,6 +39,35 @@ bool overlap(const void *a, size_t na, const void *b, size_t nb) {
 std::once_flag g_attr_once;
 int g_attr_status = 0;
 
+// Device-resident workspace of kda_chunk_fwd_noalloc, one copy per GPU (the
+// code object holds it for as long as the process runs).  In host code the
+// array's name is only a stand-in: its device address on each GPU comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) char scratch[KDA_NOALLOC_WORKSPACE_BYTES];
+void *g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_status[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+
+// Passed as `workspace` by kda_chunk_fwd_noalloc: "use the array above".
+void *const kStaticWorkspace = (void *)&g_scratch_ptr;
+
+// The device address of `scratch` on `dev`, or nullptr if it cannot be had.
+void *scratch_on(int dev) {
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::call_once(g_scratch_once[dev], [dev] {
+        int cur = -1;
+        hipError_t rc = hipGetDevice(&cur);
+        if (rc == hipSuccess && cur != dev) rc = hipSetDevice(dev);
+        void *ptr = nullptr;
+        if (rc == hipSuccess) rc = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (cur >= 0 && cur != dev && hipSetDevice(cur) != hipSuccess && rc == hipSuccess) rc = hipErrorUnknown;
+        g_scratch_status[dev] = rc;
+        g_scratch_ptr[dev] = rc == hipSuccess ? ptr : nullptr;
+    });
+    return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 KDA_EXPORT const char *kda_status_str(int status) {
@@ -101,11 +130,17 @@ int chunk_fwd(const void *q, const void *k, const void *v, kda_dtype qkv_dtype, 
     if (out_gate && !norm_weight) return KDA_ERR_NULL;
     if (lrz && !lo->gate_w) return KDA_ERR_NULL;
     const void *gu = lrz ? lo->gate_u : nullptr, *gw = lrz ? lo->gate_w : nullptr;
-    const void *ptrs[] = {q, k, v, g_raw, beta, A, S0, o, S_final, workspace, S_ckpt, out_gate, norm_weight, gu, gw};
+    const void *ptrs[] = {q,      k,        v,           g_raw, beta, A, S0, o, S_final,
+                          workspace == kStaticWorkspace ? nullptr : workspace, S_ckpt, out_gate, norm_weight, gu, gw};
     for (const void *p : ptrs)
         if (misaligned(p)) return KDA_ERR_ALIGN;
     const size_t need = kda_chunk_fwd_workspace_bytes(T_total, n_seqs, H, qkv_dtype);
-    if (!workspace || workspace_bytes < need) return KDA_ERR_WORKSPACE;
+    // kda_chunk_fwd_noalloc passes kStaticWorkspace: the library's own array,
+    // whose address is looked up only once every other check has passed.
+    const bool own_ws = workspace == kStaticWorkspace;
+    if (own_ws ? need > (size_t)KDA_NOALLOC_WORKSPACE_BYTES : (!workspace || workspace_bytes < need))
+        return KDA_ERR_WORKSPACE;
+    if (own_ws) workspace = nullptr;
     const size_t esz = qkv_dtype == KDA_F32 ? 4 : 2;
     const size_t tok = (size_t)T_total * H;
     const size_t o_bytes = tok * kD * 4;
@@ -128,6 +163,14 @@ int chunk_fwd(const void *q, const void *k, const void *v, kda_dtype qkv_dtype, 
             if (overlap(S_ckpt, ck_bytes, others[i], sizes[i])) return KDA_ERR_ALIAS;
     }
 
+    if (own_ws) {
+        int dev = -1;
+        if (hipStreamGetDevice((hipStream_t)stream, &dev) != hipSuccess) return KDA_ERR_HIP;
+        workspace = scratch_on(dev);  // the array of the stream's GPU
+        if (!workspace) return KDA_ERR_HIP;
+        if (overlap(o, o_bytes, workspace, need) || overlap(S_ckpt, (size_t)ckpt_capacity * H * kD * kD * 4, workspace, need))
+            return KDA_ERR_ALIAS;
+    }
     std::call_once(g_attr_once, [] { g_attr_status = kda::set_prefill_attributes(); });
     if (g_attr_status != 0) return KDA_ERR_HIP;
     const kda::Ckpt ck{S_ckpt && ckpt_capacity > 0 ? S_ckpt : nullptr, nullptr, (int)(S_ckpt ? ckpt_stride / 64 : 1),
@@ -159,6 +202,14 @@ KDA_EXPORT int kda_chunk_fwd(const void *q, const void *k, const void *v, kda_dt
                              size_t workspace_bytes, void *stream) {
     return chunk_fwd(q, k, v, qkv_dtype, g_raw, beta, A, S0, cu_seqlens, B, T, H, n_seqs, dk, dv, o, S_final,
                      workspace, workspace_bytes, stream, nullptr, nullptr, 0, 0, nullptr);
+}
+
+KDA_EXPORT int kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v, kda_dtype qkv_dtype,
+                                     const float *g_raw, const float *beta, const float *A, const float *S0,
+                                     const int32_t *cu_seqlens, int32_t B, int64_t T, int32_t H, int32_t n_seqs,
+                                     int32_t dk, int32_t dv, float *o, float *S_final, void *stream) {
+    return chunk_fwd(q, k, v, qkv_dtype, g_raw, beta, A, S0, cu_seqlens, B, T, H, n_seqs, dk, dv, o, S_final,
+                     kStaticWorkspace, 0, stream, nullptr, nullptr, 0, 0, nullptr);
 }
 
 KDA_EXPORT int kda_chunk_fwd_ckpt(const void *q, const void *k, const void *v, kda_dtype qkv_dtype,

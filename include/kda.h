@@ -19,7 +19,9 @@
  *   - Head dims are fixed: d_k = d_v = 128 (Kimi Linear summary, sections 4 and
  *     6.3).  Any other value returns KDA_ERR_SHAPE.
  *   - Every tensor pointer is a device pointer owned by the caller; the library
- *     allocates no device memory and keeps no mutable global state.
+ *     allocates no device memory.  Its only global state is set once per
+ *     process (kernel attributes) or once per GPU (the address of the
+ *     workspace array of kda_chunk_fwd_noalloc), thread-safely.
  *   - Layouts are dense, row-major, innermost dimension last:
  *       q, k, z : [tokens, H, 128]   v, o : [tokens, H, 128]
  *       beta    : [tokens, H]        A    : [H]
@@ -144,6 +146,31 @@ int kda_chunk_fwd_timed(const void *q, const void *k, const void *v, kda_dtype q
                         const int32_t *cu_seqlens, int32_t B, int64_t T, int32_t H, int32_t n_seqs,
                         int32_t dk, int32_t dv, float *o, float *S_final, void *workspace,
                         size_t workspace_bytes, void *stream, void *const *stage_events);
+
+/*
+ * kda_chunk_fwd without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  The workspace is a device-resident array of
+ * KDA_NOALLOC_WORKSPACE_BYTES inside the library, one per GPU, held from the
+ * first call on that GPU until the process ends; the call allocates nothing
+ * (no hipMalloc, hipFree or allocating library routine).  A problem whose
+ * kda_chunk_fwd_workspace_bytes exceeds KDA_NOALLOC_WORKSPACE_BYTES returns
+ * KDA_ERR_WORKSPACE: with bf16 q/k/v and 16 heads up to 4,544 tokens fit
+ * (2,048 tokens x 16 heads need 62 MB).  The GPU is the stream's
+ * (hipStreamGetDevice); its first call takes the array's address with
+ * hipGetSymbolAddress (KDA_ERR_HIP if that fails).
+ *
+ * Every call on one GPU shares that GPU's array and leaves its contents
+ * behind (nothing in it needs to start at zero): calls that overlap in time
+ * on one GPU, on different streams or from different threads, race and give
+ * wrong results.  Serialise them (one stream, or events).  Everything else
+ * (arguments, validation, results: the same bits) is as kda_chunk_fwd.
+ */
+#define KDA_NOALLOC_WORKSPACE_BYTES (128u << 20)
+int kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v, kda_dtype qkv_dtype,
+                          const float *g_raw, const float *beta, const float *A, const float *S0,
+                          const int32_t *cu_seqlens, int32_t B, int64_t T, int32_t H, int32_t n_seqs,
+                          int32_t dk, int32_t dv, float *o, float *S_final, void *stream);
 
 /*
  * kda_chunk_fwd that also keeps state snapshots for a KDA-aware prefix cache

@@ -240,3 +240,28 @@ def test_decode_layer_rejects():
     assert call_decode_layer(decode_args(z=None), Opts(0, 0.0, None, None, 0.0, 0, 0, 0, None, wl, 64)) == NULL
     assert call_decode_layer(decode_args(z=None), Opts(0, 0.0, None, None, 0.0, 0, 0, 0, u, None, 64)) == NULL
     assert call_decode_layer(decode_args(o=fake(15, 64)), Opts(0, 0.0, None, None, 0.0, 0, 0, 0, u, wl, 64)) == ALIAS
+
+
+def call_prefill_noalloc(a):
+    lib = kda.load()
+    return lib.kda_chunk_fwd_noalloc(a["q"], a["k"], a["v"], a["dtype"], a["z"], a["beta"], a["A"], a["S0"],
+                                     a["cu"], a["B"], a["T"], a["H"], a["N"], a["dk"], a["dv"], a["o"], a["Sf"],
+                                     a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dk=64), SHAPE), (dict(dtype=7), DTYPE), (dict(q=None), NULL), (dict(N=2), SEQLENS),
+    (dict(q=fake(1, 8)), ALIGN), (dict(o=fake(1, 64)), ALIAS),
+    # more than the library's own workspace holds: rejected before any HIP call
+    (dict(T=8192, H=16), WORKSPACE), (dict(T=4096, H=16, dtype=1), WORKSPACE),
+])
+def test_prefill_noalloc_rejects(kw, code):
+    assert call_prefill_noalloc(prefill_args(**kw)) == code
+
+
+def test_prefill_noalloc_limit_matches_the_header():
+    text = open(HEADER).read()
+    limit = int(re.search(r"#define KDA_NOALLOC_WORKSPACE_BYTES \((\d+)u << (\d+)\)", text).group(1)) << 20
+    lib = kda.load()
+    assert lib.kda_chunk_fwd_workspace_bytes(4544, 1, 16, 0) <= limit < lib.kda_chunk_fwd_workspace_bytes(4608, 1, 16, 0)
+    assert call_prefill_noalloc(prefill_args(B=0, N=0, T=0)) == OK
