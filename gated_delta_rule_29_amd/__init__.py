@@ -120,6 +120,32 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _on_gpu(t, name="q"):
+    """The kernels take device pointers: a host tensor would hand them host addresses."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU, got {t.device}")
+
+
+def _keep_for(stream, *tensors):
+    """Tensors this binding allocated were allocated for the current stream; when the library runs on
+    another one, tell the caching allocator, so their memory is not reused before that work ends."""
+    if stream is None or stream == torch.cuda.current_stream():
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
+
+
+def _out(t, name, shape, device):
+    """A caller-supplied output: fp32, contiguous, on the inputs' device and exactly `shape` (the kernels
+    write that many values into it)."""
+    _need(t, name, (torch.float32,), device)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be {list(shape)}, got {list(t.shape)}")
+
+
 def _need(t, name, dtypes, device):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a tensor")
@@ -165,12 +191,16 @@ def kda_chunk_fwd(q, k, v, g_raw, beta, A, S0=None, cu_seqlens=None, *, o=None, 
     ignored and may be None.
     """
     lib = load()
+    _on_gpu(q)
     squeeze = q.dim() == 3
     if g_raw is None and gate_u is None:
         raise ValueError("g_raw is required without gate_u / gate_w")
     if squeeze:
         q, k, v, beta = (x.unsqueeze(0) for x in (q, k, v, beta))
         g_raw = None if g_raw is None else g_raw.unsqueeze(0)
+        if o is not None:
+            _out(o, "o", (q.shape[1], q.shape[2], v.shape[-1]), q.device)
+            o = o.unsqueeze(0)
     if q.dim() != 4:
         raise ValueError("q must be [B, T, H, 128] or [T, H, 128]")
     B, T, H, dk = q.shape
@@ -206,14 +236,24 @@ def kda_chunk_fwd(q, k, v, g_raw, beta, A, S0=None, cu_seqlens=None, *, o=None, 
         _need(S0, "S0", (torch.float32,), dev)
         if S0.shape != (N, H, dk, dv):
             raise ValueError(f"S0 must be [{N}, {H}, {dk}, {dv}]")
+    mine = []  # tensors allocated here
     if o is None:
         o = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
-    if return_final_state and S_final is None:
+        mine.append(o)
+    else:
+        _out(o, "o", (B, T, H, dv), dev)
+    if S_final is not None:
+        _out(S_final, "S_final", (N, H, dk, dv), dev)
+    elif return_final_state:
         S_final = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+        mine.append(S_final)
     dtype = KDA_BF16 if q.dtype == torch.bfloat16 else KDA_F32
     need = int(lib.kda_chunk_fwd_workspace_bytes(B * T, N, H, dtype))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        mine.append(workspace)
+    else:
+        _need(workspace, "workspace", (torch.uint8,), dev)
     args = (_ptr(q), _ptr(k), _ptr(v), dtype, _ptr(g_raw), _ptr(beta), _ptr(A), _ptr(S0),
             _ptr(cu_seqlens), B, T, H, N, dk, dv, _ptr(o), _ptr(S_final), _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream(stream))
@@ -249,6 +289,7 @@ def kda_chunk_fwd(q, k, v, g_raw, beta, A, S0=None, cu_seqlens=None, *, o=None, 
     else:
         rc = lib.kda_chunk_fwd_timed(*args, ctypes.cast(stage_events, ctypes.c_void_p))
         _check(rc, "kda_chunk_fwd")
+    _keep_for(stream, *mine)
     if squeeze:
         o = o.squeeze(0)
     return o, S_final
@@ -260,6 +301,7 @@ def kda_chunk_fwd_noalloc(q, k, v, g_raw, beta, A, o, S0=None, cu_seqlens=None, 
     ([N, H, 128, 128] fp32).  Problems larger than the workspace raise KDAError (KDA_ERR_WORKSPACE);
     calls that overlap on one GPU race.  Arguments are otherwise as kda_chunk_fwd."""
     lib = load()
+    _on_gpu(q)
     if q.dim() == 3:
         q, k, v, beta, g_raw = (x.unsqueeze(0) for x in (q, k, v, beta, g_raw))
         o = o.unsqueeze(0)
@@ -301,6 +343,7 @@ def kda_decode_step(q, k, v, g_raw, beta, A, S, *, o=None, stream=None, qk_l2nor
     results, same speed).
     gate_u [N, r], gate_w [H, 128, r]: the low-rank forget gate, as kda_chunk_fwd (g_raw may be None)."""
     lib = load()
+    _on_gpu(q)
     N, H, dk = q.shape
     dv = v.shape[-1]
     dev = q.device
@@ -323,8 +366,11 @@ def kda_decode_step(q, k, v, g_raw, beta, A, S, *, o=None, stream=None, qk_l2nor
         raise ValueError("inconsistent shapes")
     if gate not in GATES:
         raise ValueError(f"gate must be one of {sorted(GATES)}")
+    mine = None
     if o is None:
-        o = torch.empty((N, H, dv), dtype=torch.float32, device=dev)
+        o = mine = torch.empty((N, H, dv), dtype=torch.float32, device=dev)
+    else:
+        _out(o, "o", (N, H, dv), dev)
     dtype = KDA_BF16 if q.dtype == torch.bfloat16 else KDA_F32
     args = (_ptr(q), _ptr(k), _ptr(v), dtype, _ptr(g_raw), _ptr(beta), _ptr(A), _ptr(S), N, H, dk, dv)
     if qk_l2norm or out_gate is not None or gate != "k3" or per_head or reverse_order or lr_u is not None:
@@ -343,4 +389,5 @@ def kda_decode_step(q, k, v, g_raw, beta, A, S, *, o=None, stream=None, qk_l2nor
     else:
         rc = lib.kda_decode_step(*args, _ptr(o), _stream(stream))
         _check(rc, "kda_decode_step")
+    _keep_for(stream, mine)
     return o

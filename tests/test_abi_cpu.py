@@ -265,3 +265,29 @@ def test_prefill_noalloc_limit_matches_the_header():
     lib = kda.load()
     assert lib.kda_chunk_fwd_workspace_bytes(4544, 1, 16, 0) <= limit < lib.kda_chunk_fwd_workspace_bytes(4608, 1, 16, 0)
     assert call_prefill_noalloc(prefill_args(B=0, N=0, T=0)) == OK
+
+
+def test_binding_refuses_host_tensors():
+    """Host tensors would hand host addresses to the kernels: the binding refuses them first."""
+    import torch
+    q = torch.zeros(64, 2, 128, dtype=torch.bfloat16)
+    z, beta, A = torch.zeros(64, 2, 128), torch.zeros(64, 2), torch.zeros(2)
+    with pytest.raises(ValueError, match="GPU"):
+        kda.kda_chunk_fwd(q, q, q, z, beta, A)
+    with pytest.raises(ValueError, match="GPU"):
+        kda.kda_chunk_fwd_noalloc(q, q, q, z, beta, A, torch.zeros(64, 2, 128))
+    with pytest.raises(ValueError, match="GPU"):
+        kda.kda_decode_step(q[:4], q[:4], q[:4], z[:4], beta[:4], A, torch.zeros(4, 2, 128, 128))
+
+
+@pytest.mark.parametrize("bad", ["dtype", "shape", "contiguous", "device"])
+def test_binding_checks_caller_outputs(bad):
+    """A caller-supplied output must be exactly what the kernels write: fp32, contiguous, the given shape."""
+    import torch
+    cpu = torch.device("cpu")
+    shape = (3, 2, 128)
+    t = {"dtype": torch.zeros(shape, dtype=torch.bfloat16), "shape": torch.zeros(3, 2, 64),
+         "contiguous": torch.zeros(2, 3, 128).transpose(0, 1), "device": torch.zeros(shape, device="meta")}[bad]
+    with pytest.raises((TypeError, ValueError)):
+        kda._out(t, "o", shape, cpu)
+    kda._out(torch.zeros(shape), "o", shape, cpu)  # the right one passes

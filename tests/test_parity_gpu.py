@@ -253,3 +253,32 @@ def test_serving_batch_mixed_lengths(io):
     o, Sf = run_prefill(d, cu=cu, S0=d["S0"], io=io)
     check(d, o, Sf, cu=cu, io=io, label="serving batch")
     assert np.array_equal(Sf[7], d["S0"][7])
+
+
+def test_side_stream_and_caller_outputs():
+    """A call on a side stream (the binding's own buffers recorded on it) gives the bits of the call on
+    the current stream; caller-supplied outputs of the wrong shape are refused."""
+    d = synth.prefill_inputs(3400, 300, 3, s0_std=0.02)
+    q, k, v = (to_dev(d[n], torch.bfloat16) for n in ("q", "k", "v"))
+    z, beta, A, S0 = (to_dev(d[n], torch.float32) for n in ("z", "beta", "A", "S0"))
+    say("case side stream")
+    o1, S1 = kda.kda_chunk_fwd(q, k, v, z, beta, A, S0)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    o2, S2 = kda.kda_chunk_fwd(q, k, v, z, beta, A, S0, stream=side)
+    x = synth.decode_tokens(3401, 0, 4, 3)
+    Sd = S1[[0, 0, 0, 0]].clone()
+    Sd2 = Sd.clone()
+    xd = [to_dev(x[n], torch.bfloat16) for n in ("q", "k", "v")] + [to_dev(x[n], torch.float32) for n in ("z", "beta")]
+    od1 = kda.kda_decode_step(*xd, A, Sd)
+    side.wait_stream(torch.cuda.current_stream())
+    od2 = kda.kda_decode_step(*xd, A, Sd2, stream=side)
+    side.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2) and torch.equal(od1, od2) and torch.equal(Sd, Sd2)
+    with pytest.raises(ValueError):
+        kda.kda_chunk_fwd(q, k, v, z, beta, A, S0, o=torch.empty((299, 3, 128), device=DEV))
+    with pytest.raises(ValueError):
+        kda.kda_chunk_fwd(q, k, v, z, beta, A, S0, S_final=torch.empty((1, 3, 128, 64), device=DEV))
+    with pytest.raises(TypeError):
+        kda.kda_decode_step(*xd, A, Sd, o=torch.empty((4, 3, 128), device=DEV, dtype=torch.bfloat16))
