@@ -1,6 +1,10 @@
 """Host-side checks of bench.py's accounting (no GPU): the algorithmic bytes of the prefill and how the
 path-level roofline splits them over the five kernels."""
+import os
+
 import bench
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 
 def test_algorithmic_bytes_of_the_64k_workload():
@@ -18,3 +22,13 @@ def test_per_kernel_split_adds_up_to_the_path():
     assert r["traffic"] is None
     tr = {n: 1e9 for n in bench.STAGES}
     assert bench.roofline(1.0, stage, 16, 1, tr)["traffic"] == 5e9
+
+
+def test_flop_figure_follows_the_pages_formula():
+    """The TFLOP/s bench.py reports counts the FLOP formula of the Kimi Linear summary, section 6.3
+    (6 T d^2 + 3 T C d + T C^2 per head), whose values at d = 128, C = 64 are in the golden file."""
+    for line in open(os.path.join(GOLDEN, "flops_formula.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        T, d, C, f = (int(x) for x in line.split())
+        assert d == 128 and C == 64 and bench.FLOPS_PER_TOKEN_HEAD * T == f

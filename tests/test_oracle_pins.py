@@ -388,12 +388,3 @@ def test_threads_do_not_change_results():
     o4, S4, n = oracle.recurrent(d["q"], d["k"], d["v"], d["z"], d["beta"], d["A"], d["S0"], threads=4,
                                  return_threads=True)
     assert n == 4 and np.array_equal(o1, o4) and np.array_equal(S1, S4)
-
-
-def test_flops_formula_golden():
-    """[KL 6.3] FLOPs_KDA(T; C, d) = 6 T d^2 + 3 T C d + T C^2 at the printed C = 64, d = 128."""
-    for line in open(os.path.join(GOLDEN, "flops_formula.txt")):
-        if line.startswith("#") or not line.strip():
-            continue
-        T, d, C, f = (int(x) for x in line.split())
-        assert 6 * T * d * d + 3 * T * C * d + T * C * C == f
