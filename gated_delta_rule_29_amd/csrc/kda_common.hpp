@@ -85,8 +85,7 @@ __device__ __forceinline__ S8 split8(const F8 &x) {
     for (int p = 0; p < 4; ++p) {
         const float a = x.v[2 * p], b = x.v[2 * p + 1];
         const bf16x2 hp = {(__bf16)a, (__bf16)b};
-        uint32_t u = __builtin_bit_cast(uint32_t, hp);
-        asm("" : "+v"(u));  // keep the packed pair: widen it instead of converting a again
+        const uint32_t u = __builtin_bit_cast(uint32_t, hp);
         const float fa = __builtin_bit_cast(float, u << 16), fb = __builtin_bit_cast(float, u & 0xffff0000u);
         const bf16x2 lp = {(__bf16)(a - fa), (__bf16)(b - fb)};
         s.hi[2 * p] = hp[0];
@@ -174,6 +173,18 @@ __device__ __forceinline__ float gate_of(float expA, float z) {
         return kda_gate(expA, z);
     else
         return softplus_gate(expA, z);
+}
+// 2^x (v_exp_f32: 2^-inf = 0, 2^inf = inf, NaN propagates).
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+constexpr float LOG2E = 1.44269504088896341f;
+// The log-decay in base 2, g log2 e: the K3 gate as g_min log2 e * Sigmoid(x)
+// with e^-x = 2^{-x log2 e} (same limits as kda_gate), the softplus decay scaled.
+template <int GK>
+__device__ __forceinline__ float gate_log2(float expA, float z) {
+    if constexpr (GK == GATE_K3)
+        return (GMIN * LOG2E) * __builtin_amdgcn_rcpf(1.f + ex2(-(expA * LOG2E) * z));
+    else
+        return softplus_gate(expA, z) * LOG2E;
 }
 
 }  // namespace kda

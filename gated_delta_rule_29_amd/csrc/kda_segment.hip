@@ -347,6 +347,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GK == GATE_
     char *blk = tab.blocks + ((size_t)c * H + h) * BLK;
     const float eA = __expf(A[h]);
     if (w == 0) sm.beta[l] = l < len ? beta[(size_t)(t0 + l) * H + h] : 0.f;
+    // Log-decays are carried in base 2 (g log2 e) from the gate on, so every
+    // factor e^{G_a - G_b} is one v_exp_f32 of a difference, with no multiply.
 
     // Phases 1 and 2 run twice, once per 64-channel half hf, so E1 and CB only
     // ever hold half the channels (that keeps three workgroups on a CU).
@@ -480,7 +482,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GK == GATE_
                         zv = __builtin_bit_cast(float, zu);
                     }
                     const uint16_t ku = kin[ks][e];
-                    gv[ks][e] = gate_of<GK>(eA, ok ? zv : -__builtin_inff());  // -inf: g = 0
+                    gv[ks][e] = gate_log2<GK>(eA, ok ? zv : -__builtin_inff());  // -inf: g = 0
                     kb[ks][e] = __builtin_bit_cast(__bf16, ku);
                 }
             // ---- phase 0 (QKN, first half only): the inverse L2 norms of the
@@ -549,8 +551,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GK == GATE_
             float eN[4];  // e^{G_n - R_{s+1}}
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                eRs[s] = __expf(Rs[s]);
-                eN[s] = __expf(Rs[4] - Rs[s + 1]);
+                eRs[s] = ex2(Rs[s]);
+                eN[s] = ex2(Rs[4] - Rs[s + 1]);
             }
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
@@ -560,9 +562,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GK == GATE_
                     const int s = 2 * ks + (e >> 2);
                     const int t = 32 * ks + 16 * (e >> 2) + 4 * g + (e & 3);
                     const float cs = gv[ks][e];
-                    const float e1 = __expf(cs);
+                    const float e1 = ex2(cs);
                     const float kf = QKN ? (float)kb[ks][e] * sm.nk[t] : (float)kb[ks][e];
-                    const float cb = kf * __expf(st[s] - cs);  // k e^{R_{s+1} - G_t}
+                    const float cb = kf * ex2(st[s] - cs);  // k e^{R_{s+1} - G_t}
                     // softplus decay: the log G_t - R_s and raw k instead (phase 2)
                     sm.a.E1[t * PEH + chl] = GK == GATE_K3 ? e1 : cs;
                     sm.CB[t * PEH + chl] = GK == GATE_K3 ? cb : kf;
@@ -588,12 +590,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GK == GATE_
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
                     for (int jj = 0; jj <= i; ++jj)
-                        sm.F[(i * (i + 1) / 2 + jj) * D + ch] = __expf(Rs[i] - Rs[jj + 1]);
+                        sm.F[(i * (i + 1) / 2 + jj) * D + ch] = ex2(Rs[i] - Rs[jj + 1]);
             } else {  // the references R_s themselves, as logs
 #pragma unroll
                 for (int s = 0; s < 4; ++s) sm.F[s * D + ch] = Rs[s];
             }
-            ((float *)(blk + BO_GM))[ch] = __expf(Rs[4]);
+            ((float *)(blk + BO_GM))[ch] = ex2(Rs[4]);
         }
         __syncthreads();
 
@@ -619,8 +621,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GK == GATE_
                 if constexpr (GK != GATE_K3)
 #pragma unroll
                     for (int m = 0; m < 4; ++m) {
-                        ea[m] = __expf(la[m]);
-                        eb[m] = __expf(lb[m]);
+                        ea[m] = ex2(la[m]);
+                        eb[m] = ex2(lb[m]);
                     }
                 const f32x4 pa = *(const f32x4 *)&sm.eR[i * D + c0], pb = *(const f32x4 *)&sm.eR[i * D + c0 + 16];
                 F8 xk, xq;
@@ -659,8 +661,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GK == GATE_
                         const f32x4 lc2 = *(const f32x4 *)&sm.a.E1[cc * PEH + cl + 16];
 #pragma unroll
                         for (int m = 0; m < 4; ++m) {
-                            xc.v[m] = ca[m] * __expf(ri[m] - rj[m] - lc[m]);
-                            xc.v[4 + m] = cbv[m] * __expf(ri2[m] - rj2[m] - lc2[m]);
+                            xc.v[m] = ca[m] * ex2(ri[m] - rj[m] - lc[m]);
+                            xc.v[4 + m] = cbv[m] * ex2(ri2[m] - rj2[m] - lc2[m]);
                         }
                     }
                     const S8 cs = split8(xc);
@@ -681,7 +683,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GK == GATE_
                     F8 yk, yq;
 #pragma unroll
                     for (int m = 0; m < 4; ++m) {
-                        const float fa = mr ? __expf(la[m] - pr0[m]) : 0.f, fb = mr ? __expf(lb[m] - pr1[m]) : 0.f;
+                        const float fa = mr ? ex2(la[m] - pr0[m]) : 0.f, fb = mr ? ex2(lb[m] - pr1[m]) : 0.f;
                         yk.v[m] = (QKN ? (float)k0[m] * nkr : (float)k0[m]) * fa;
                         yk.v[4 + m] = (QKN ? (float)k1[m] * nkr : (float)k1[m]) * fb;
                         yq.v[m] = (QKN ? (float)q0[m] * nqr : (float)q0[m]) * fa;
@@ -701,8 +703,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GK == GATE_
                         F8 xc;
 #pragma unroll
                         for (int m = 0; m < 4; ++m) {
-                            xc.v[m] = colin ? kc0[m] * __expf(p0[m] - lc0[m]) : 0.f;
-                            xc.v[4 + m] = colin ? kc1[m] * __expf(p1[m] - lc1[m]) : 0.f;
+                            xc.v[m] = colin ? kc0[m] * ex2(p0[m] - lc0[m]) : 0.f;
+                            xc.v[4 + m] = colin ? kc1[m] * ex2(p1[m] - lc1[m]) : 0.f;
                         }
                         const S8 cs = split8(xc);
                         const bool rowin = mr == mb;
@@ -729,7 +731,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GK == GATE_
                     const bf16x4 qv = ld_bf16x4(rq, prow * (int)ph + 2 * (64 * hf + cg));
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const float f = kc[e] * __expf(fminf(l4[e] - lc[e], 0.f));
+                        const float f = kc[e] * ex2(fminf(l4[e] - lc[e], 0.f));
                         sk += k4[e] * f;
                         sq += (float)qv[e] * f;
                     }
@@ -855,22 +857,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GK == GATE_
                     __bf16, (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rv, tl * ph + 2 * ch, tu * ph, 0));
             }
     {
+        // T diag(beta) as split bf16 fragments, each of the six (token tile rt,
+        // token block ks) tiles formed once, by wave p mod 4, into the CB region
+        // (dead since phase 2): every wave needs all six.
+        char *tbl = (char *)sm.CB;
+        static_assert(sizeof(sm.CB) >= 6 * 2048, "T diag(beta) fragments fit the CB region");
+#pragma unroll
+        for (int p = 0; p < 6; ++p) {
+            const int rt = p < 2 ? p : 2 + ((p - 2) >> 1), ks = p < 2 ? 0 : (p & 1);
+            if ((p & 3) != w) continue;
+            const int r = 16 * rt + lr, c0 = 32 * ks + 4 * g;
+            const f32x4 ta = *(const f32x4 *)&sm.a.T[r * PTT + c0], tc = *(const f32x4 *)&sm.a.T[r * PTT + c0 + 16];
+            const f32x4 ba = *(const f32x4 *)&sm.beta[c0], bb = *(const f32x4 *)&sm.beta[c0 + 16];
+            F8 x;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                x.v[m] = ta[m] * ba[m];
+                x.v[4 + m] = tc[m] * bb[m];
+            }
+            const S8 sp = split8(x);
+            *(bf16x8 *)(tbl + 2048 * p + 16 * l) = sp.hi;
+            *(bf16x8 *)(tbl + 2048 * p + 1024 + 16 * l) = sp.lo;
+        }
+        __syncthreads();
         S8 tb[4][2];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 if (ks > (rt >> 1)) continue;
-                const int r = 16 * rt + lr, c0 = 32 * ks + 4 * g;
-                const f32x4 ta = *(const f32x4 *)&sm.a.T[r * PTT + c0], tc = *(const f32x4 *)&sm.a.T[r * PTT + c0 + 16];
-                const f32x4 ba = *(const f32x4 *)&sm.beta[c0], bb = *(const f32x4 *)&sm.beta[c0 + 16];
-                F8 x;
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    x.v[m] = ta[m] * ba[m];
-                    x.v[4 + m] = tc[m] * bb[m];
-                }
-                tb[rt][ks] = split8(x);
+                const int p = rt < 2 ? rt : 2 + 2 * (rt - 2) + ks;
+                tb[rt][ks].hi = *(const bf16x8 *)(tbl + 2048 * p + 16 * l);
+                tb[rt][ks].lo = *(const bf16x8 *)(tbl + 2048 * p + 1024 + 16 * l);
             }
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
