@@ -26,6 +26,81 @@ constexpr float GMIN = -5.f;  // Kimi K3 lower bound of the log-decay
 
 __host__ __device__ constexpr size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS accesses
+// (lgkmcnt), not for its global loads in flight, which __syncthreads' fence
+// would also wait for.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// largest n in [0, N) with off[n] <= x (for off[0] <= x < off[N], the owner of x)
+__device__ inline int off_find(const int32_t *off, int N, int x) {
+    int lo = 0, hi = N - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (off[mid] <= x)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
+// The packed sequences of a prefill.  Sequence n spans tokens
+// [start(n), end(n)); its chunks are chunk0(n) .. chunk0(n + 1) - 1 of the
+// per-chunk operand blocks; its segments (L chunks each, the last one
+// shorter) are seg0(n) .. seg0(n + 1) - 1; and those with a successor, whose
+// transitions the scan composes, are numbered segA0(n) .. segA0(n + 1) - 1.
+// With cu_seqlens the offsets are arrays that seq_table_kernel builds on the
+// device (cu_seqlens is never read on the host).  Without, the call holds B
+// sequences of Tper tokens: every entry is arithmetic and nothing is built.
+struct SeqTable {
+    int32_t *seg_off, *segA_off, *chunk_off;  // [N + 1] (cu_seqlens only)
+    int64_t *seq_start, *seq_end;             // [N]     (cu_seqlens only)
+    int L;                                    // chunks per segment
+    int64_t Tper;                             // >= 0: fixed-length sequences; < 0: the arrays
+    int nchp, segp;                           // fixed length: chunks and segments per sequence
+
+    __device__ int64_t start(int n) const { return Tper >= 0 ? (int64_t)n * Tper : seq_start[n]; }
+    __device__ int64_t end(int n) const { return Tper >= 0 ? (int64_t)(n + 1) * Tper : seq_end[n]; }
+    __device__ int chunk0(int n) const { return Tper >= 0 ? n * nchp : chunk_off[n]; }
+    __device__ int seg0(int n) const { return Tper >= 0 ? n * segp : seg_off[n]; }
+    __device__ int segA0(int n) const { return Tper >= 0 ? n * max(segp - 1, 0) : segA_off[n]; }
+    // owners, for an index below the total (chunk0(N), seg0(N), segA0(N))
+    __device__ int seq_of_chunk(int c, int N) const { return Tper >= 0 ? c / nchp : off_find(chunk_off, N, c); }
+    __device__ int seq_of_seg(int x, int N) const { return Tper >= 0 ? x / segp : off_find(seg_off, N, x); }
+    __device__ int seq_of_segA(int a, int N) const {
+        return Tper >= 0 ? a / max(segp - 1, 1) : off_find(segA_off, N, a);
+    }
+};
+// Bytes of the table's arrays in a workspace, and their placement at p.
+__host__ inline size_t seq_table_bytes(int N) {
+    return 3 * align_up(4 * (size_t)(N + 1)) + 2 * align_up(8 * (size_t)N);
+}
+__host__ inline SeqTable seq_table_at(char *p, int N, int L) {
+    SeqTable t{};
+    t.seg_off = (int32_t *)p;
+    p += align_up(4 * (size_t)(N + 1));
+    t.segA_off = (int32_t *)p;
+    p += align_up(4 * (size_t)(N + 1));
+    t.chunk_off = (int32_t *)p;
+    p += align_up(4 * (size_t)(N + 1));
+    t.seq_start = (int64_t *)p;
+    p += align_up(8 * (size_t)N);
+    t.seq_end = (int64_t *)p;
+    t.L = L;
+    t.Tper = -1;
+    return t;
+}
+// Fill the table for a call: fixed-length sequences of T tokens (cu == nullptr)
+// set the arithmetic fields; with cu_seqlens seq_table_kernel is launched.
+int launch_seq_table(const int32_t *cu, int N, int64_t T_total, int64_t T, SeqTable &t, hipStream_t stream);
+// off[n] = sum over sequences m < n of floor(len_m / stride), n = 0 .. N.
+int launch_ckpt_prep(const SeqTable &t, int N, int64_t stride, int64_t *off, hipStream_t stream);
+
 // State snapshots at a chunk-aligned stride, for a KDA-aware prefix cache
 // (Kimi K3 paper review, Significance and Limitations paragraphs: the recurrent
 // state is kept only at sparse checkpoint boundaries).  Snapshot m of sequence

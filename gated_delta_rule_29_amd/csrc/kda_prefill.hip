@@ -19,8 +19,10 @@
 // fp32 / bf16 range, so the diagonal tiles are dense MFMA products too.
 //
 // Kernels (one launch each, in stream order):
-//   prep_kernel   sequence boundaries (clamped, non-decreasing), the first
-//                 chunk of every sequence and its first segment (L chunks);
+//   seq_table_kernel  (cu_seqlens only; shared with the bf16 path) sequence
+//                 boundaries (clamped, non-decreasing), the first chunk of
+//                 every sequence and its first segment (L chunks); fixed-length
+//                 batches need no table kernel;
 //   intra_kernel  one workgroup per (chunk, head), all chunks in parallel:
 //                 gate + sub-chunk cumsums, the two Gram tiles on MFMA, the
 //                 blocked forward substitution, W and U on MFMA; writes the
@@ -58,11 +60,7 @@ constexpr size_t BLK_BYTES = 147968;   // multiple of 256
 __host__ __device__ constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Table {  // workspace header
-    int32_t *chunk_off;  // [N+1] first chunk of each sequence; chunk_off[N] = total
-    int32_t *seg_off;    // [N+1] first segment of each sequence
-    int32_t *segA_off;   // [N+1] first map segment (every segment but a sequence's last)
-    int64_t *seq_start;  // [N]
-    int64_t *seq_end;    // [N]
+    SeqTable sq;         // the sequences, their chunks and segments
     int64_t *ckpt_off;   // [N+1] first snapshot slot of each sequence
     char *blocks;        // chain operands, block (c, h) at (c * H + h) * BLK_BYTES
     float *Mseg;         // [nseg][H][128][128] segment transitions
@@ -73,27 +71,16 @@ struct Table {  // workspace header
     Layer ly;
 };
 
-__host__ __device__ inline size_t table_bytes(int N) {
-    return 3 * align256(4 * (size_t)(N + 1)) + 2 * align256(8 * (size_t)N) + align256(8 * (size_t)(N + 1));
-}
-__host__ __device__ inline Table carve(void *ws, int N) {
+__host__ inline size_t table_bytes(int N) { return seq_table_bytes(N) + align256(8 * (size_t)(N + 1)); }
+__host__ inline Table carve(void *ws, int N) {
     char *p = (char *)ws;
     Table t;
-    t.chunk_off = (int32_t *)p;
-    p += align256(4 * (size_t)(N + 1));
-    t.seg_off = (int32_t *)p;
-    p += align256(4 * (size_t)(N + 1));
-    t.segA_off = (int32_t *)p;
-    p += align256(4 * (size_t)(N + 1));
-    t.seq_start = (int64_t *)p;
-    p += align256(8 * (size_t)N);
-    t.seq_end = (int64_t *)p;
-    p += align256(8 * (size_t)N);
+    t.sq = seq_table_at(p, N, 1);
+    p += seq_table_bytes(N);
     t.ckpt_off = (int64_t *)p;
     p += align256(8 * (size_t)(N + 1));
     t.blocks = p;
     t.Mseg = t.Bseg = t.Sin = nullptr;
-    t.L = 1;
     t.ck = Ckpt{nullptr, t.ckpt_off, 1, 0};
     t.ly = Layer{false, 0.f, nullptr, nullptr, 0.f};
     return t;
@@ -115,14 +102,14 @@ __host__ inline int64_t seg32_max(int64_t T_total, int N, int H) {
 
 // ------------------------------------------------------------------- prep --
 
-// Sequence n spans [s_n, s_{n+1}) with s_m = max_{m' <= m} clamp(cu[m'], 0, T),
-// so sequences never overlap and the chunk count is at most ceil(T/64) + N.
-// cu == nullptr means B equal sequences of Tper tokens.  One workgroup walks
-// the N + 1 offsets in tiles of 256 with a running max and a running sum.
-// It also writes seg_off and segA_off: the exclusive prefix sums of each
-// sequence's segment count ceil(chunks / L) and of that count less one.
-__global__ __launch_bounds__(256) void prep_kernel(const int32_t *__restrict__ cu, int N, int64_t T_total,
-                                                   int64_t Tper, Table tab) {
+// The sequence table of a cu_seqlens call (both I/O paths).  Sequence n spans
+// [s_n, s_{n+1}) with s_m = max_{m' <= m} clamp(cu[m'], 0, T), so sequences
+// never overlap and the chunk count is at most ceil(T/64) + N.  One workgroup
+// walks the N + 1 offsets in tiles of 256 with a running max, and writes the
+// exclusive prefix sums of each sequence's chunk count ceil(len / 64), of its
+// segment count ceil(chunks / L) and of that count less one.
+__global__ __launch_bounds__(256) void seq_table_kernel(const int32_t *__restrict__ cu, int N, int64_t T_total,
+                                                        SeqTable tab) {
     __shared__ int64_t s_scan[256], s_seg[256], s_sa[256];
     __shared__ int64_t s_prev_max, s_prev_sum, s_prev_seg, s_prev_sa;
     const int tid = threadIdx.x;
@@ -137,7 +124,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const int32_t *__restrict__ c
         const int m = base + tid;
         int64_t c = 0;
         if (m <= N) {
-            c = cu ? (int64_t)cu[m] : (int64_t)m * Tper;
+            c = (int64_t)cu[m];
             c = c < 0 ? 0 : (c > T_total ? T_total : c);
         }
         // running max over the tile (Hillis-Steele), then fold in the previous tiles
@@ -189,11 +176,22 @@ __global__ __launch_bounds__(256) void prep_kernel(const int32_t *__restrict__ c
     }
 }
 
+int launch_seq_table(const int32_t *cu, int N, int64_t T_total, int64_t T, SeqTable &t, hipStream_t stream) {
+    if (!cu) {  // B sequences of T tokens: arithmetic, nothing to build
+        t.Tper = T;
+        t.nchp = (int)((T + CH - 1) / CH);
+        t.segp = (t.nchp + t.L - 1) / t.L;
+        return 0;
+    }
+    t.Tper = -1;
+    hipLaunchKernelGGL(seq_table_kernel, dim3(1), dim3(256), 0, stream, cu, N, T_total, t);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 // off[n] = sum over sequences m < n of floor(len_m / stride), n = 0 .. N: the
 // first snapshot slot of each sequence.  One workgroup, tiles of 256 with a
 // running sum.
-__global__ __launch_bounds__(256) void ckpt_prep_kernel(const int64_t *__restrict__ seq_start,
-                                                        const int64_t *__restrict__ seq_end, int N, int64_t stride,
+__global__ __launch_bounds__(256) void ckpt_prep_kernel(SeqTable t, int N, int64_t stride,
                                                         int64_t *__restrict__ off) {
     __shared__ int64_t s_scan[256];
     __shared__ int64_t s_prev;
@@ -202,7 +200,7 @@ __global__ __launch_bounds__(256) void ckpt_prep_kernel(const int64_t *__restric
     __syncthreads();
     for (int base = 0; base <= N; base += 256) {
         const int m = base + tid;  // off[m] sums sequences < m: exclusive scan
-        s_scan[tid] = (m >= 1 && m <= N) ? (seq_end[m - 1] - seq_start[m - 1]) / stride : 0;
+        s_scan[tid] = (m >= 1 && m <= N) ? (t.end(m - 1) - t.start(m - 1)) / stride : 0;
         __syncthreads();
         for (int d = 1; d < 256; d <<= 1) {
             const int64_t x = tid >= d ? s_scan[tid - d] : 0;
@@ -218,23 +216,9 @@ __global__ __launch_bounds__(256) void ckpt_prep_kernel(const int64_t *__restric
     }
 }
 
-int launch_ckpt_prep(const int64_t *seq_start, const int64_t *seq_end, int N, int64_t stride, int64_t *off,
-                     hipStream_t stream) {
-    hipLaunchKernelGGL(ckpt_prep_kernel, dim3(1), dim3(256), 0, stream, seq_start, seq_end, N, stride, off);
+int launch_ckpt_prep(const SeqTable &t, int N, int64_t stride, int64_t *off, hipStream_t stream) {
+    hipLaunchKernelGGL(ckpt_prep_kernel, dim3(1), dim3(256), 0, stream, t, N, stride, off);
     return hipGetLastError() == hipSuccess ? 0 : -1;
-}
-
-// locate chunk c: sequence n with chunk_off[n] <= c < chunk_off[n+1]
-__device__ inline int find_seq(const int32_t *chunk_off, int N, int c) {
-    int lo = 0, hi = N - 1;
-    while (lo < hi) {
-        int mid = (lo + hi + 1) >> 1;
-        if (chunk_off[mid] <= c)
-            lo = mid;
-        else
-            hi = mid - 1;
-    }
-    return lo;
 }
 
 // ----------------------------------------------------------------- intra --
@@ -295,11 +279,11 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
     IntraSmem<IO> &sm = *reinterpret_cast<IntraSmem<IO> *>(smem_raw);
 
     const int c = blockIdx.x, h = blockIdx.y;
-    const int total = tab.chunk_off[N];
+    const int total = tab.sq.chunk0(N);
     if (c >= total) return;
-    const int n = find_seq(tab.chunk_off, N, c);
-    const int64_t t0 = tab.seq_start[n] + (int64_t)(c - tab.chunk_off[n]) * CH;
-    const int len = (int)min((int64_t)CH, tab.seq_end[n] - t0);
+    const int n = tab.sq.seq_of_chunk(c, N);
+    const int64_t t0 = tab.sq.start(n) + (int64_t)(c - tab.sq.chunk0(n)) * CH;
+    const int len = (int)min((int64_t)CH, tab.sq.end(n) - t0);
     char *blk = tab.blocks + ((size_t)c * H + h) * BLK_BYTES;
 
     const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63, g = l >> 4, lr = l & 15;
@@ -671,29 +655,6 @@ struct ChainSmem {
     float Dl[NB * 68];  // Delta, transposed [column][token]
 };
 
-// Workgroup barrier for LDS traffic only: waits for this wave's LDS accesses
-// (lgkmcnt), not for its global loads in flight, which __syncthreads' fence
-// would also wait for.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_barrier();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
-// largest n in [0, N) with off[n] <= x (for x < off[N] that is the owner of x)
-__device__ inline int seq_of(const int32_t *off, int N, int x) {
-    int lo = 0, hi = N - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (off[mid] <= x)
-            lo = mid;
-        else
-            hi = mid - 1;
-    }
-    return lo;
-}
-
 // The chain over one segment of a sequence, 32 state columns per workgroup
 // (each operand fragment loaded serves both 16-column tiles), exact fp32 MFMA
 // throughout.  The segment map carries a state S entering the segment to
@@ -712,12 +673,11 @@ __global__ __launch_bounds__(256) void chain_kernel(int N, int H, Table tab, flo
     const int Lw = blockIdx.x;
     const int p = (Lw & 7) + 8 * (Lw / (8 * NCB)), cb = (Lw >> 3) % NCB;
     const int a = p / H, h = p % H;
-    const int32_t *soff = MAP ? tab.segA_off : tab.seg_off;
-    if (a >= soff[N]) return;
-    const int n = seq_of(soff, N, a);
-    const int j = a - soff[n];
-    const int x = tab.seg_off[n] + j;  // segment index of the maps and states
-    const int pn = tab.seg_off[n + 1] - tab.seg_off[n];
+    if (a >= (MAP ? tab.sq.segA0(N) : tab.sq.seg0(N))) return;
+    const int n = MAP ? tab.sq.seq_of_segA(a, N) : tab.sq.seq_of_seg(a, N);
+    const int j = a - (MAP ? tab.sq.segA0(n) : tab.sq.seg0(n));
+    const int x = tab.sq.seg0(n) + j;  // segment index of the maps and states
+    const int pn = tab.sq.seg0(n + 1) - tab.sq.seg0(n);
     const bool bcol = MAP && cb >= NCB / 2;              // columns of B (U enters)
     const int col0 = NB * (MAP ? cb % (NCB / 2) : cb);  // first column within M, B or the state
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, lr = l & 15;
@@ -736,9 +696,9 @@ __global__ __launch_bounds__(256) void chain_kernel(int N, int H, Table tab, flo
                 Sr[ct][u][m] = MAP ? (!bcol && r == cc ? 1.f : 0.f) : tab.Sin[sblk + (size_t)r * D + cc];
             }
 
-    const int cseq = tab.chunk_off[n];  // the sequence's first chunk
-    const int cbeg = cseq + j * tab.L, cend = min(tab.chunk_off[n + 1], cbeg + tab.L);
-    const int64_t sstart = tab.seq_start[n], send = tab.seq_end[n];
+    const int cseq = tab.sq.chunk0(n);  // the sequence's first chunk
+    const int cbeg = cseq + j * tab.sq.L, cend = min(tab.sq.chunk0(n + 1), cbeg + tab.sq.L);
+    const int64_t sstart = tab.sq.start(n), send = tab.sq.end(n);
     const int nks_aq = w < 2 ? 1 : 2;  // 32-token k-steps of Aqk row tile w
     const int64_t ck_base = tab.ck.S ? tab.ck.off[n] : 0;
 
@@ -928,7 +888,7 @@ int launch_segment_prefill(const __bf16 *q, const __bf16 *k, const __bf16 *v, co
                            float *o, float *S_final, const Ckpt &ck, const Layer &ly, void *ws,
                            hipStream_t stream, hipEvent_t *ev);
 int set_segment_attributes();
-int launch_seg_scan(const float *S0, int N, int H, const int32_t *seg_off, float *Mseg, float *Bseg, float *Sin,
+int launch_seg_scan(const float *S0, int N, int H, const SeqTable &sq, float *Mseg, float *Bseg, float *Sin,
                     float *S_final, hipStream_t stream);
 
 // bf16 q/k/v run the segment-parallel fused path (kda_segment.hip); fp32 q/k/v
@@ -954,7 +914,7 @@ int launch_prefill(const void *q, const void *k, const void *v, bool f32io, cons
     Table tab = carve(ws, N);
     tab.ck = Ckpt{ck.S, tab.ckpt_off, ck.stride_chunks, ck.cap};
     tab.ly = ly;
-    tab.L = seg32_len(T_total, N, H);
+    tab.sq.L = seg32_len(T_total, N, H);
     const int64_t nsm = seg32_max(T_total, N, H);
     const size_t st = (size_t)nsm * H * D * D;
     tab.Mseg = (float *)(tab.blocks + (size_t)max_chunks(T_total, N) * (size_t)H * BLK_BYTES);
@@ -965,10 +925,8 @@ int launch_prefill(const void *q, const void *k, const void *v, bool f32io, cons
     const int64_t slots8 = (nsm * H + 7) / 8;
     if (slots8 * 128 > (int64_t)(UINT32_MAX / 256) || max_chunks(T_total, N) * H > (int64_t)UINT32_MAX) return -1;
     if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return -1;
-    hipLaunchKernelGGL(prep_kernel, dim3(1), dim3(256), 0, stream, cu, N, T_total, cu ? (int64_t)0 : T, tab);
-    if (ck.S && launch_ckpt_prep(tab.seq_start, tab.seq_end, N, (int64_t)ck.stride_chunks * CH, tab.ckpt_off,
-                                 stream) != 0)
-        return -1;
+    if (launch_seq_table(cu, N, T_total, T, tab.sq, stream) != 0) return -1;
+    if (ck.S && launch_ckpt_prep(tab.sq, N, (int64_t)ck.stride_chunks * CH, tab.ckpt_off, stream) != 0) return -1;
     const int64_t nc = max_chunks(T_total, N);
     if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return -1;
     if (T_total > 0) {
@@ -980,7 +938,7 @@ int launch_prefill(const void *q, const void *k, const void *v, bool f32io, cons
     hipLaunchKernelGGL(chain_kernel<true>, dim3((unsigned)(8 * (2 * D / NB) * slots8)), dim3(256), 0, stream, N, H,
                        tab, o, S_final);
     if (ev && hipEventRecord(ev[3], stream) != hipSuccess) return -1;
-    if (launch_seg_scan(S0, N, H, tab.seg_off, tab.Mseg, tab.Bseg, tab.Sin, S_final, stream) != 0) return -1;
+    if (launch_seg_scan(S0, N, H, tab.sq, tab.Mseg, tab.Bseg, tab.Sin, S_final, stream) != 0) return -1;
     if (ev && hipEventRecord(ev[4], stream) != hipSuccess) return -1;
     hipLaunchKernelGGL(chain_kernel<false>, dim3((unsigned)(8 * (D / NB) * slots8)), dim3(256), 0, stream, N, H,
                        tab, o, S_final);

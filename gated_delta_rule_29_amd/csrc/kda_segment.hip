@@ -17,7 +17,7 @@
 // M = Diag(gamma) - K~^T W and B = K~^T U.
 //
 // Kernels, in stream order:
-//   seg_prep_kernel   sequence bounds, per-sequence first chunk and first
+//   seq_table_kernel  (with cu_seqlens; kda_prefill.hip) sequence bounds, per-sequence first chunk and first
 //                     segment (a segment = L consecutive chunks of a sequence);
 //   wy_kernel         one workgroup per (chunk, head), all chunks in parallel:
 //                     gate and cumulative sums, the two decay-scaled Gram
@@ -179,105 +179,14 @@ __device__ __forceinline__ void static_for(F &&f) {
 }
 
 struct SegTable {
-    int32_t *seg_off;    // [N+1] first segment of each sequence
-    int32_t *segA_off;   // [N+1] first pass-A segment (pass A skips a sequence's last)
-    int32_t *chunk_off;  // [N+1] first chunk of each sequence
-    int64_t *seq_start;  // [N]
-    int64_t *seq_end;    // [N]
+    SeqTable sq;         // the sequences, their chunks and segments (pass A: those with a successor)
     char *blocks;        // chain operands, block (c, h) at (c * H + h) * BLK
     float *Mseg;         // [nseg][H][128][128] segment transitions
     float *Bseg;         // [nseg][H][128][128] segment offsets
     float *Sin;          // [nseg][H][128][128] state entering each segment
-    int L;               // chunks per segment
     Ckpt ck;             // state snapshots (ck.S == nullptr: none)
     Layer ly;            // fused layer steps around the operator
 };
-
-// ------------------------------------------------------------------ prep --
-
-// Sequences: s_m = running max of the clamped offsets.  chunk_off, seg_off and
-// segA_off are exclusive prefix sums of ceil(len / 64), of the segment counts
-// ceil(ceil(len / 64) / L), and of those less one (pass A skips a sequence's
-// last segment).
-__global__ __launch_bounds__(256) void seg_prep_kernel(const int32_t *__restrict__ cu, int N, int64_t T_total,
-                                                       int64_t Tper, SegTable tab) {
-    __shared__ int64_t s_a[256], s_b[256], s_c[256];
-    __shared__ int64_t s_prev_max, s_prev_a, s_prev_b, s_prev_c;
-    const int tid = threadIdx.x;
-    if (tid == 0) {
-        s_prev_max = 0;
-        s_prev_a = 0;
-        s_prev_b = 0;
-        s_prev_c = 0;
-    }
-    __syncthreads();
-    for (int base = 0; base <= N; base += 256) {
-        const int m = base + tid;
-        int64_t c = 0;
-        if (m <= N) {
-            c = cu ? (int64_t)cu[m] : (int64_t)m * Tper;
-            c = c < 0 ? 0 : (c > T_total ? T_total : c);
-        }
-        s_a[tid] = c;
-        __syncthreads();
-        for (int off = 1; off < 256; off <<= 1) {
-            const int64_t x = tid >= off ? s_a[tid - off] : 0;
-            __syncthreads();
-            if (x > s_a[tid]) s_a[tid] = x;
-            __syncthreads();
-        }
-        const int64_t pm = s_prev_max;
-        const int64_t sm = s_a[tid] > pm ? s_a[tid] : pm;
-        const int64_t sp = tid > 0 ? (s_a[tid - 1] > pm ? s_a[tid - 1] : pm) : pm;
-        if (m < N) tab.seq_start[m] = sm;
-        if (m >= 1 && m <= N) tab.seq_end[m - 1] = sm;
-        int64_t nch = 0;
-        if (m >= 1 && m <= N) nch = (sm - sp + CH - 1) / CH;
-        const int64_t ns = (nch + tab.L - 1) / tab.L;
-        __syncthreads();
-        s_a[tid] = ns;
-        s_b[tid] = nch;
-        s_c[tid] = ns > 0 ? ns - 1 : 0;
-        __syncthreads();
-        for (int off = 1; off < 256; off <<= 1) {
-            const int64_t x = tid >= off ? s_a[tid - off] : 0;
-            const int64_t y = tid >= off ? s_b[tid - off] : 0;
-            const int64_t z = tid >= off ? s_c[tid - off] : 0;
-            __syncthreads();
-            s_a[tid] += x;
-            s_b[tid] += y;
-            s_c[tid] += z;
-            __syncthreads();
-        }
-        const int64_t seg = s_a[tid] + s_prev_a, chk = s_b[tid] + s_prev_b, sa = s_c[tid] + s_prev_c;
-        if (m <= N) {
-            tab.seg_off[m] = (int32_t)seg;
-            tab.chunk_off[m] = (int32_t)chk;
-            tab.segA_off[m] = (int32_t)sa;
-        }
-        __syncthreads();
-        if (tid == 255) {
-            s_prev_max = sm;
-            s_prev_a = seg;
-            s_prev_b = chk;
-            s_prev_c = sa;
-        }
-        __syncthreads();
-    }
-}
-
-// largest n in [0, N) with off[n] <= x (for x < off[N] that is the owner of x)
-__device__ inline int seg_find(const int32_t *off, int N, int x) {
-    int lo = 0, hi = N - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (off[mid] <= x)
-            lo = mid;
-        else
-            hi = mid - 1;
-    }
-    return lo;
-}
 
 // -------------------------------------------------------------- WY / UT --
 
@@ -334,10 +243,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GK == GATE_
     SegTable tab) {
     __shared__ WySmem<GK> sm;
     const int c = (int)(blockIdx.x / (unsigned)H), h = (int)(blockIdx.x % (unsigned)H);
-    if (c >= tab.chunk_off[N]) return;
-    const int n = seg_find(tab.chunk_off, N, c);
-    const int64_t t0 = tab.seq_start[n] + (int64_t)(c - tab.chunk_off[n]) * CH;
-    const int len = (int)min((int64_t)CH, tab.seq_end[n] - t0);
+    if (c >= tab.sq.chunk0(N)) return;
+    const int n = tab.sq.seq_of_chunk(c, N);
+    const int64_t t0 = tab.sq.start(n) + (int64_t)(c - tab.sq.chunk0(n)) * CH;
+    const int len = (int)min((int64_t)CH, tab.sq.end(n) - t0);
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, g = l >> 4, lr = l & 15;
     // Row-block role of this wave in the Gram and inverse phases, whose work
     // grows with the row block: rotated from workgroup to workgroup.
@@ -1018,14 +927,16 @@ __device__ __forceinline__ void chain_dma(const char *__restrict__ blk, int byte
 // One workgroup (8 waves) per (segment, head).  Pass A: wave w owns columns
 // 32w .. 32w+31 of X = [M | B] (waves 0-3: M, from I; waves 4-7: B, from 0, with
 // U); pass B: wave w owns value columns 16w .. 16w+15 of the state.
-template <bool PASS_A>
+// NBA: pass A's image count, 3 (a six-step loop body, segments a multiple of
+// 6 chunks) or 2 (two steps, for the short segments of short inputs).
+template <bool PASS_A, int NBA = CHAIN_NBUF_A>
 __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void seg_chain_kernel(
     int N, int H, SegTable tab, float *__restrict__ o, float *__restrict__ S_final) {
     using Lo = ChainLds<PASS_A>;
     // Pass A rotates three LDS images (its image is small), pass B two.
     // Distinct arrays (not one array indexed by step): a read of one then
     // provably does not alias a copy in flight into another.
-    constexpr int NBUF = PASS_A ? CHAIN_NBUF_A : 2;
+    constexpr int NBUF = PASS_A ? NBA : 2;
     __shared__ __align__(16) char buf0[Lo::BYTES];
     __shared__ __align__(16) char buf1[Lo::BYTES];
     __shared__ __align__(16) char buf2[NBUF == 3 ? Lo::BYTES : 16];
@@ -1040,18 +951,17 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     // over the XCDs and none waits behind an empty one.  Pass A has no work for
     // a sequence's last segment (its map is not needed).
     const int a = blockIdx.x / H, h = blockIdx.x % H;
-    const int32_t *soff = PASS_A ? tab.segA_off : tab.seg_off;
-    if (a >= soff[N]) return;
-    const int n = seg_find(soff, N, a);
-    const int j = a - soff[n];
-    const int x = tab.seg_off[n] + j;  // segment index of the maps and states
-    const int pn = tab.seg_off[n + 1] - tab.seg_off[n];
-    const int L = tab.L;
-    const int64_t s0 = tab.seq_start[n], s1 = tab.seq_end[n];
+    if (a >= (PASS_A ? tab.sq.segA0(N) : tab.sq.seg0(N))) return;
+    const int n = PASS_A ? tab.sq.seq_of_segA(a, N) : tab.sq.seq_of_seg(a, N);
+    const int j = a - (PASS_A ? tab.sq.segA0(n) : tab.sq.seg0(n));
+    const int x = tab.sq.seg0(n) + j;  // segment index of the maps and states
+    const int pn = tab.sq.seg0(n + 1) - tab.sq.seg0(n);
+    const int L = tab.sq.L;
+    const int64_t s0 = tab.sq.start(n), s1 = tab.sq.end(n);
     const int nch = (int)((s1 - s0 + CH - 1) / CH);
     const int cbeg = j * L, cend = min(nch, cbeg + L);
     const size_t bstride = (size_t)H * BLK;
-    const char *blk0 = tab.blocks + ((size_t)tab.chunk_off[n] * H + h) * BLK;
+    const char *blk0 = tab.blocks + ((size_t)tab.sq.chunk0(n) * H + h) * BLK;
 
     const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, g = l >> 4,
               lr = l & 15;
@@ -1392,7 +1302,7 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
         }
     };
     // Unrolled so that every step's image and U set are fixed arrays.
-    constexpr int UNROLL = PASS_A ? CHAIN_UNROLL_A : 2;
+    constexpr int UNROLL = PASS_A && NBUF == 3 ? 6 : 2;
     auto buf = [&](auto ic) -> char * {
         constexpr int b = decltype(ic)::value % NBUF;
         if constexpr (b == 0) return buf0;
@@ -1453,73 +1363,84 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
 // One workgroup per (sequence, head, 16 value columns): S_in[0] = S0 and
 // S_in[p+1] = M_p S_in[p] + B_p over the sequence's segments, with exact fp32
 // MFMA products (an identity transition reproduces the state bit for bit).
-// An empty sequence gets S_final = S0 here.
-__global__ __launch_bounds__(256) void seg_scan_kernel(const float *__restrict__ S0, int N, int H, SegTable tab,
-                                                       float *__restrict__ S_final) {
+// An empty sequence gets S_final = S0 here.  Eight waves of 16 rows each: a
+// step is 32 products per wave, and one map is 12 loads per wave, so the maps
+// of the next two steps stay in flight (the vmcnt counter holds 63).
+constexpr int SCAN_NT = 512;
+__global__ __launch_bounds__(SCAN_NT) void seg_scan_kernel(const float *__restrict__ S0, int N, int H, SegTable tab,
+                                                           float *__restrict__ S_final) {
     __shared__ float Ss[16 * 132];  // S^T [column][row]
     const int nh = blockIdx.x, cb = blockIdx.y;
     const int n = nh / H, h = nh % H;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, lr = l & 15;
-    const int col = 16 * cb + lr;
-    const int first = tab.seg_off[n], pn = tab.seg_off[n + 1] - first;
-    f32x4 Sr[2];
+    const int col = 16 * cb + lr, r0 = 16 * w;
+    const int first = tab.sq.seg0(n), pn = tab.sq.seg0(n + 1) - first;
+    f32x4 Sr;
     const size_t s0b = ((size_t)n * H + h) * D * D;
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-            Sr[u][m] = S0 ? S0[s0b + (size_t)(32 * w + 16 * u + 4 * g + m) * D + col] : 0.f;
+    for (int m = 0; m < 4; ++m) Sr[m] = S0 ? S0[s0b + (size_t)(r0 + 4 * g + m) * D + col] : 0.f;
     if (pn == 0) {
         if (S_final)
 #pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-                for (int m = 0; m < 4; ++m) S_final[s0b + (size_t)(32 * w + 16 * u + 4 * g + m) * D + col] = Sr[u][m];
+            for (int m = 0; m < 4; ++m) S_final[s0b + (size_t)(r0 + 4 * g + m) * D + col] = Sr[m];
         return;
     }
-    // M_p and B_p of the step after next are loaded while this step computes:
-    // two register sets, loads always issued (past the last map they re-read it).
-    F8 Mr[2][2][4];
-    f32x4 Br[2][2];
+    // M_p and B_p are loaded two steps ahead into three rotating register sets
+    // (loads always issued: past the last map they re-read it).
+    F8 Mr[3][4];
+    f32x4 Br[3];
     auto load_map = [&](int p, int set) __attribute__((always_inline)) {
         const size_t b = ((size_t)(first + min(p, max(pn - 2, 0))) * H + h) * D * D;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int r0 = 32 * w + 16 * u;
+        for (int m = 0; m < 4; ++m) Br[set][m] = tab.Bseg[b + (size_t)(r0 + 4 * g + m) * D + col];
 #pragma unroll
-            for (int m = 0; m < 4; ++m) Br[set][u][m] = tab.Bseg[b + (size_t)(r0 + 4 * g + m) * D + col];
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) Mr[set][u][ks] = ld_f8(&tab.Mseg[b + (size_t)(r0 + lr) * D + 32 * ks + 8 * g]);
-        }
+        for (int ks = 0; ks < 4; ++ks) Mr[set][ks] = ld_f8(&tab.Mseg[b + (size_t)(r0 + lr) * D + 32 * ks + 8 * g]);
     };
-    auto step = [&](int p, int set) __attribute__((always_inline)) {
+    auto step = [&](int p, auto setc) __attribute__((always_inline)) {
+        constexpr int set = decltype(setc)::value;
         const size_t b = ((size_t)(first + p) * H + h) * D * D;
+        float *sin = tab.Sin + b + (size_t)(r0 + 4 * g) * D + col;
+        if (p == pn - 1) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int m = 0; m < 4; ++m) tab.Sin[b + (size_t)(32 * w + 16 * u + 4 * g + m) * D + col] = Sr[u][m];
-        if (p == pn - 1) return;
-        load_map(p + 1, set ^ 1);
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-            *(f32x4 *)&Ss[lr * 132 + 32 * w + 16 * u + 4 * g] = Sr[u];
-        __syncthreads();
+            for (int m = 0; m < 4; ++m) sin[(size_t)m * D] = Sr[m];
+            return;
+        }
+        load_map(p + 2, (set + 2) % 3);
+        const f32x4 Sp = Sr;  // S_in[p]
+        // LDS-only barriers: a __syncthreads fence would also wait for the map
+        // loads just issued.
+        *(f32x4 *)&Ss[lr * 132 + r0 + 4 * g] = Sr;
+        lds_barrier();
         F8 sb[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) sb[ks] = ld_f8(&Ss[lr * 132 + 32 * ks + 8 * g]);
-        __syncthreads();
+        lds_barrier();
+        // One accumulator per 32-row block of M (chains of 8 products, not 32),
+        // added at the end: with M = I exactly one partial is nonzero, so an
+        // identity transition still gives the state bit for bit.
+        f32x4 a[4];
+        a[0] = Br[set];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            f32x4 acc = Br[set][u];
+        for (int ks = 1; ks < 4; ++ks) a[ks] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) acc = mma_ff(acc, Mr[set][u][ks], sb[ks]);
-            Sr[u] = acc;
-        }
+        for (int ks = 0; ks < 4; ++ks) a[ks] = mma_ff(a[ks], Mr[set][ks], sb[ks]);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) Sr[m] = (a[0][m] + a[1][m]) + (a[2][m] + a[3][m]);
+        // (Stores and loads share the in-order vmcnt counter: before the
+        // registers a pending store reads are rewritten, everything issued
+        // before that store must complete, the map loads included.  The
+        // compiler reuses those registers within a step, so in practice the
+        // maps arrive one step ahead, and a step takes about one load latency,
+        // 2.9 us, wherever the stores are placed.)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) sin[(size_t)m * D] = Sp[m];
     };
     load_map(0, 0);
-    for (int p = 0; p < pn; p += 2) {
-        step(p, 0);
-        if (p + 1 < pn) step(p + 1, 1);
+    load_map(1, 1);
+    for (int p = 0; p < pn; p += 3) {
+        step(p, std::integral_constant<int, 0>{});
+        if (p + 1 < pn) step(p + 1, std::integral_constant<int, 1>{});
+        if (p + 2 < pn) step(p + 2, std::integral_constant<int, 2>{});
     }
 }
 
@@ -1527,11 +1448,21 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(const float *__restrict__
 
 constexpr int SEG_TARGET_WGS = 256;  // chain workgroups in flight: one per CU (LDS-bound)
 
+// Segments of at least 4 chunks: at 2K x 16, 4-chunk segments (8 per head)
+// gave 87 us against 103 us with 2-chunk segments (16 per head; the scan's
+// steps cost about 2.9 us each) and 91 us with 6.
+#ifndef SEG_L_MIN
+#define SEG_L_MIN 4
+#endif
+// Chunks per segment: about SEG_TARGET_WGS (segment, head) pairs in all, and a
+// whole number of pass-A loop bodies: a multiple of 6 (three images) from 6
+// chunks on, else of 2 (the two-image pass A of short inputs).
 static inline int seg_len(int64_t T_total, int H) {
     const int64_t nc = (T_total + CH - 1) / CH;
     const int64_t per_head = SEG_TARGET_WGS / (H > 0 ? H : 1) > 0 ? SEG_TARGET_WGS / H : 1;
     int64_t L = (nc + per_head - 1) / per_head;
-    L = (L + CHAIN_UNROLL_A - 1) / CHAIN_UNROLL_A * CHAIN_UNROLL_A;  // whole groups of pass-A steps
+    L = L < SEG_L_MIN ? SEG_L_MIN : L;
+    L = L >= CHAIN_UNROLL_A ? (L + CHAIN_UNROLL_A - 1) / CHAIN_UNROLL_A * CHAIN_UNROLL_A : (L + 1) / 2 * 2;
     return (int)L;
 }
 static inline int64_t seg_chunks_max(int64_t T_total, int N) { return (T_total + CH - 1) / CH + N; }
@@ -1541,13 +1472,10 @@ static inline int64_t seg_max(int64_t T_total, int N, int H) {
 }
 
 size_t seg_workspace_bytes(int64_t T_total, int N, int H) {
-    const size_t tab = 3 * align_up(4 * (size_t)(N + 1)) + 2 * align_up(8 * (size_t)N) + align_up(8 * (size_t)(N + 1));
+    const size_t tab = seq_table_bytes(N) + align_up(8 * (size_t)(N + 1));
     return tab + (size_t)seg_chunks_max(T_total, N) * H * BLK +
            3 * (size_t)seg_max(T_total, N, H) * H * D * D * sizeof(float);
 }
-
-int launch_ckpt_prep(const int64_t *seq_start, const int64_t *seq_end, int N, int64_t stride, int64_t *off,
-                     hipStream_t stream);
 
 int launch_segment_prefill(const __bf16 *q, const __bf16 *k, const __bf16 *v, const float *z, const float *beta,
                            const float *A, const float *S0, const int32_t *cu, int B, int64_t T, int H, int N,
@@ -1559,16 +1487,8 @@ int launch_segment_prefill(const __bf16 *q, const __bf16 *k, const __bf16 *v, co
     const int64_t ncm = seg_chunks_max(T_total, N);
     char *p = (char *)ws;
     SegTable tab;
-    tab.seg_off = (int32_t *)p;
-    p += align_up(4 * (size_t)(N + 1));
-    tab.segA_off = (int32_t *)p;
-    p += align_up(4 * (size_t)(N + 1));
-    tab.chunk_off = (int32_t *)p;
-    p += align_up(4 * (size_t)(N + 1));
-    tab.seq_start = (int64_t *)p;
-    p += align_up(8 * (size_t)N);
-    tab.seq_end = (int64_t *)p;
-    p += align_up(8 * (size_t)N);
+    tab.sq = seq_table_at(p, N, L);
+    p += seq_table_bytes(N);
     int64_t *ckpt_off = (int64_t *)p;
     p += align_up(8 * (size_t)(N + 1));
     tab.ck = Ckpt{ck.S, ckpt_off, ck.stride_chunks, ck.cap};
@@ -1579,13 +1499,11 @@ int launch_segment_prefill(const __bf16 *q, const __bf16 *k, const __bf16 *v, co
     tab.Mseg = (float *)p;
     tab.Bseg = tab.Mseg + st;
     tab.Sin = tab.Bseg + st;
-    tab.L = L;
     // a launch covers at most 2^32 - 1 work-items (unreachable within a GPU's memory)
     if (ncm * H > (int64_t)(UINT32_MAX / 256) || nsm * H > (int64_t)(UINT32_MAX / CH_NT)) return -1;
     if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return -1;
-    hipLaunchKernelGGL(seg_prep_kernel, dim3(1), dim3(256), 0, stream, cu, N, T_total, cu ? (int64_t)0 : T, tab);
-    if (ck.S && launch_ckpt_prep(tab.seq_start, tab.seq_end, N, (int64_t)ck.stride_chunks * CH, ckpt_off, stream) != 0)
-        return -1;
+    if (launch_seq_table(cu, N, T_total, T, tab.sq, stream) != 0) return -1;
+    if (ck.S && launch_ckpt_prep(tab.sq, N, (int64_t)ck.stride_chunks * CH, ckpt_off, stream) != 0) return -1;
     if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return -1;
     if (T_total > 0) {
         const dim3 grid((unsigned)(ncm * H)), blk(256);
@@ -1608,10 +1526,13 @@ int launch_segment_prefill(const __bf16 *q, const __bf16 *k, const __bf16 *v, co
     }
     if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return -1;
     const dim3 cgrid((unsigned)(nsm * H));
-    hipLaunchKernelGGL(seg_chain_kernel<true>, cgrid, dim3(CH_NT), 0, stream, N, H, tab,
-                       o, S_final);
+    if (L % CHAIN_UNROLL_A == 0)
+        hipLaunchKernelGGL((seg_chain_kernel<true, CHAIN_NBUF_A>), cgrid, dim3(CH_NT), 0, stream, N, H, tab, o,
+                           S_final);
+    else
+        hipLaunchKernelGGL((seg_chain_kernel<true, 2>), cgrid, dim3(CH_NT), 0, stream, N, H, tab, o, S_final);
     if (ev && hipEventRecord(ev[3], stream) != hipSuccess) return -1;
-    hipLaunchKernelGGL(seg_scan_kernel, dim3((unsigned)(N * H), 8), dim3(256), 0, stream, S0, N, H, tab, S_final);
+    hipLaunchKernelGGL(seg_scan_kernel, dim3((unsigned)(N * H), 8), dim3(SCAN_NT), 0, stream, S0, N, H, tab, S_final);
     if (ev && hipEventRecord(ev[4], stream) != hipSuccess) return -1;
     hipLaunchKernelGGL(seg_chain_kernel<false>, cgrid, dim3(CH_NT), 0, stream, N, H, tab,
                        o, S_final);
@@ -1622,15 +1543,15 @@ int launch_segment_prefill(const __bf16 *q, const __bf16 *k, const __bf16 *v, co
 
 // The scan over segments on its own, for the fp32 path (which has its own
 // per-chunk operands and chain passes but the same segment maps).
-int launch_seg_scan(const float *S0, int N, int H, const int32_t *seg_off, float *Mseg, float *Bseg, float *Sin,
+int launch_seg_scan(const float *S0, int N, int H, const SeqTable &sq, float *Mseg, float *Bseg, float *Sin,
                     float *S_final, hipStream_t stream) {
     if ((int64_t)N * H > (int64_t)(UINT32_MAX / 256)) return -1;
     SegTable tab{};
-    tab.seg_off = const_cast<int32_t *>(seg_off);
+    tab.sq = sq;
     tab.Mseg = Mseg;
     tab.Bseg = Bseg;
     tab.Sin = Sin;
-    hipLaunchKernelGGL(seg_scan_kernel, dim3((unsigned)(N * H), 8), dim3(256), 0, stream, S0, N, H, tab, S_final);
+    hipLaunchKernelGGL(seg_scan_kernel, dim3((unsigned)(N * H), 8), dim3(SCAN_NT), 0, stream, S0, N, H, tab, S_final);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
