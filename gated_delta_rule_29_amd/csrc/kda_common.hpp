@@ -28,12 +28,16 @@ __host__ __device__ constexpr size_t align_up(size_t x) { return (x + 255) & ~(s
 
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS accesses
 // (lgkmcnt), not for its global loads in flight, which __syncthreads' fence
-// would also wait for.
+// would also wait for.  The empty asm statements with a memory clobber keep
+// the compiler from moving memory accesses across the barrier: s_barrier
+// itself is not a memory operation to it, and a single-thread fence did not
+// stop it from sinking an LDS read past the barrier into a later branch that
+// uses the value.
 __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __asm__ volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __asm__ volatile("" ::: "memory");
 }
 
 // largest n in [0, N) with off[n] <= x (for off[0] <= x < off[N], the owner of x)
@@ -170,12 +174,6 @@ __device__ __forceinline__ S8 split8(const F8 &x) {
     }
     return s;
 }
-__device__ __forceinline__ bf16x8 round8(const F8 &x) {
-    bf16x8 h;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) h[e] = (__bf16)x.v[e];
-    return h;
-}
 
 // Products of fragments.  "s" = split (hi + lo), "1" = single bf16.
 // hi*lo and lo*hi are kept, lo*lo is dropped (below fp32 rounding of the sum).
@@ -207,17 +205,7 @@ __device__ __forceinline__ F8 ld_f8(const float *p) {  // 32-byte aligned
     r.v[4] = b.x; r.v[5] = b.y; r.v[6] = b.z; r.v[7] = b.w;
     return r;
 }
-__device__ __forceinline__ bf16x8 ld_b8(const __bf16 *p) { return *(const bf16x8 *)p; }
 
-// load 8 consecutive inputs of type IO as fp32
-__device__ __forceinline__ F8 ld_io8(const float *p) { return ld_f8(p); }
-__device__ __forceinline__ F8 ld_io8(const __bf16 *p) {
-    bf16x8 b = ld_b8(p);
-    F8 r;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) r.v[e] = (float)b[e];
-    return r;
-}
 __device__ __forceinline__ float to_f(float x) { return x; }
 __device__ __forceinline__ float to_f(__bf16 x) { return (float)x; }
 

@@ -37,23 +37,19 @@
 //                 state with MFMA.
 //
 // This file serves fp32 q/k/v (bf16 q/k/v take kda_segment.hip's path): every
-// product is an exact fp32 MFMA.  intra_kernel is written over the I/O type
-// (with bf16, fp32 intermediates would enter MFMA as hi + lo bf16 pairs); the
-// library instantiates it for fp32 only.
+// operand is fp32 and every product an exact fp32 MFMA.
 #include "kda_common.hpp"
 
 namespace kda {
 
 // ----------------------------------------------------------------- layout --
 
-// Per (chunk, head) block of chain operands in the workspace (bytes).  "Split"
-// arrays hold the bf16 hi part followed by the bf16 lo part in the bf16 build
-// and plain fp32 in the fp32 build; both use 4 bytes per element.
-constexpr size_t OFF_W = 0;            // W      [64][128]  bf16 (fp32 build: fp32)
-constexpr size_t OFF_U = 32768;        // U      [64][128]  fp32
-constexpr size_t OFF_KT = 65536;       // K~^T   [128][64]  split, K~ = K * e^{G_n - G}
-constexpr size_t OFF_QT = 98304;       // Q~     [64][128]  split, Q~ = Q * Gam
-constexpr size_t OFF_AQ = 131072;      // Aqk    [64][64]   split, zero above the diagonal
+// Per (chunk, head) block of chain operands in the workspace (bytes), all fp32.
+constexpr size_t OFF_W = 0;            // W      [64][128]
+constexpr size_t OFF_U = 32768;        // U      [64][128]
+constexpr size_t OFF_KT = 65536;       // K~^T   [128][64]  K~ = K * e^{G_n - G}
+constexpr size_t OFF_QT = 98304;       // Q~     [64][128]  Q~ = Q * Gam
+constexpr size_t OFF_AQ = 131072;      // Aqk    [64][64]   zero above the diagonal
 constexpr size_t OFF_GM = 147456;      // gamma  [128]      fp32, e^{G_n}
 constexpr size_t BLK_BYTES = 147968;   // multiple of 256
 
@@ -227,7 +223,6 @@ constexpr int PG = 132;  // LDS pitch (floats) of [64][128] token-major arrays
 constexpr int PT = 68;   // LDS pitch (floats) of [*][64] arrays
 
 // 77.6 KB, so that two workgroups share a CU.
-template <typename IO>
 struct IntraSmem {
     union {
         float E1[CH * PG];   // e^{G_t - R_{s(t)}}: row factor, in [e^-80, 1] (phases 1-2)
@@ -242,41 +237,17 @@ struct IntraSmem {
 
 __device__ __forceinline__ int pair_index(int i, int j) { return i * (i - 1) / 2 + j; }  // j < i
 
-// store a split (hi | lo) or fp32 value quad at element offset e of an array of
-// n_elems elements starting at base
-template <bool F32>
-__device__ __forceinline__ void st_split4(char *base, size_t n_elems, size_t e, float a, float b, float c,
-                                          float d) {
-    if constexpr (F32) {
-        *(float4 *)((float *)base + e) = make_float4(a, b, c, d);
-    } else {
-        bf16x4 h, l;
-        h[0] = (__bf16)a; h[1] = (__bf16)b; h[2] = (__bf16)c; h[3] = (__bf16)d;
-        l[0] = (__bf16)(a - (float)h[0]); l[1] = (__bf16)(b - (float)h[1]);
-        l[2] = (__bf16)(c - (float)h[2]); l[3] = (__bf16)(d - (float)h[3]);
-        *(bf16x4 *)((__bf16 *)base + e) = h;
-        *(bf16x4 *)((__bf16 *)base + n_elems + e) = l;
-    }
-}
-template <bool F32>
-__device__ __forceinline__ void st_split1(char *base, size_t n_elems, size_t e, float a) {
-    if constexpr (F32) {
-        ((float *)base)[e] = a;
-    } else {
-        __bf16 h = (__bf16)a;
-        ((__bf16 *)base)[e] = h;
-        ((__bf16 *)base)[n_elems + e] = (__bf16)(a - (float)h);
-    }
+// store a value quad at element offset e of the fp32 array at base
+__device__ __forceinline__ void st4(char *base, size_t e, float a, float b, float c, float d) {
+    *(float4 *)((float *)base + e) = make_float4(a, b, c, d);
 }
 
-template <typename IO>
-__global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, const IO *__restrict__ k,
-                                                    const IO *__restrict__ v, const float *__restrict__ z,
+__global__ __launch_bounds__(256) void intra_kernel(const float *__restrict__ q, const float *__restrict__ k,
+                                                    const float *__restrict__ v, const float *__restrict__ z,
                                                     const float *__restrict__ beta,
                                                     const float *__restrict__ A, int N, int H, Table tab) {
-    constexpr bool F32 = sizeof(IO) == 4;
     extern __shared__ __align__(16) char smem_raw[];
-    IntraSmem<IO> &sm = *reinterpret_cast<IntraSmem<IO> *>(smem_raw);
+    IntraSmem &sm = *reinterpret_cast<IntraSmem *>(smem_raw);
 
     const int c = blockIdx.x, h = blockIdx.y;
     const int total = tab.sq.chunk0(N);
@@ -287,8 +258,16 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
     char *blk = tab.blocks + ((size_t)c * H + h) * BLK_BYTES;
 
     const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63, g = l >> 4, lr = l & 15;
-    const size_t HD = (size_t)H * D;
-    auto tok = [&](int t) -> size_t { return (size_t)(t0 + t) * HD + (size_t)h * D; };
+    // q, k, v and a per-channel z from this chunk's first token and this head
+    // on: token t of the chunk starts at t * H * D, a 32-bit offset (the host
+    // admits only 64 H D < 2^31).
+    const size_t base = (size_t)t0 * H * D + (size_t)h * D;
+    q += base;
+    k += base;
+    v += base;
+    const float *zc = z ? z + base : z;
+    const int HD = H * D;
+    auto tok = [&](int t) -> int { return t * HD; };
 
     // ---- phase 0: inverse L2 norms of the key and query rows when the layer's
     // normalisation is fused in (wave w: rows 16 w .. 16 w + 15, four lanes of 32
@@ -298,12 +277,20 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
         float nk = 1.f, nq = 1.f;
         if (tab.ly.qk_norm) {
             float sk = 0.f, sq = 0.f;
-            if (tr < len) {
-                for (int c2 = 0; c2 < 32; ++c2) {
-                    const float a = to_f(k[tok(tr) + cq + c2]), b = to_f(q[tok(tr) + cq + c2]);
-                    sk += a * a;
-                    sq += b * b;
+            if (tr < len) {  // all 32 channels of both rows loaded first
+                F8 ka[4], qa[4];
+#pragma unroll
+                for (int c4 = 0; c4 < 4; ++c4) {
+                    ka[c4] = ld_f8(k + tok(tr) + cq + 8 * c4);
+                    qa[c4] = ld_f8(q + tok(tr) + cq + 8 * c4);
                 }
+#pragma unroll
+                for (int c4 = 0; c4 < 4; ++c4)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        sk += ka[c4].v[e] * ka[c4].v[e];
+                        sq += qa[c4].v[e] * qa[c4].v[e];
+                    }
             }
             sk += __shfl_xor(sk, 1);
             sk += __shfl_xor(sk, 2);
@@ -342,7 +329,7 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
 #pragma unroll
         for (int u = 0; u < SUB; ++u) {
             const int t = (half + 2 * si) * SUB + u, tc = t < len ? t : 0;
-            zr[si][u] = tab.ly.zu ? 0.f : (zh ? z[(size_t)(t0 + tc) * H + h] : z[tok(tc) + ch]);
+            zr[si][u] = tab.ly.zu ? 0.f : (zh ? z[(size_t)(t0 + tc) * H + h] : zc[tok(tc) + ch]);
         }
 #pragma unroll
     for (int si = 0; si < 2; ++si) {
@@ -400,8 +387,8 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
 #pragma unroll
             for (int u = 0; u < SUB; ++u) {  // loads first (rows past the end read row 0)
                 const int t = s * SUB + u, tc = t < len ? t : 0;
-                kr[u] = to_f(k[tok(tc) + ch]);
-                qr[u] = to_f(q[tok(tc) + ch]);
+                kr[u] = k[tok(tc) + ch];
+                qr[u] = q[tok(tc) + ch];
             }
 #pragma unroll
             for (int u = 0; u < SUB; ++u) {
@@ -412,13 +399,12 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
                 const float kv = ok ? kr[u] * sm.nk[t] : 0.f;
                 const float qv = ok ? qr[u] * sm.nq[t] : 0.f;
                 sm.KG[ch * PT + t] = kv * gam;
-                st_split1<F32>(qt, CH * D, (size_t)t * D + ch, qv * gam);
+                ((float *)qt)[(size_t)t * D + ch] = qv * gam;
                 kt_vals[u] = kv * __expf((float)(Gn - Gt));
             }
 #pragma unroll
             for (int u = 0; u < SUB; u += 4)
-                st_split4<F32>(kt, D * CH, (size_t)ch * CH + s * SUB + u, kt_vals[u], kt_vals[u + 1],
-                               kt_vals[u + 2], kt_vals[u + 3]);
+                st4(kt, (size_t)ch * CH + s * SUB + u, kt_vals[u], kt_vals[u + 1], kt_vals[u + 2], kt_vals[u + 3]);
         }
         if (half == 0) ((float *)(blk + OFF_GM))[ch] = __expf((float)Gn);
     }
@@ -428,7 +414,7 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
         const int ti = tile < 3 ? 0 : (tile < 5 ? 1 : 2);
         const int tj = tile < 3 ? tile + 1 : (tile < 5 ? tile - 1 : 3);
         const int r = 16 * ti + (quad >> 2), c0 = 16 * tj + 4 * (quad & 3);
-        st_split4<F32>(blk + OFF_AQ, CH * CH, (size_t)r * CH + c0, 0.f, 0.f, 0.f, 0.f);
+        st4(blk + OFF_AQ, (size_t)r * CH + c0, 0.f, 0.f, 0.f, 0.f);
     }
     __syncthreads();
 
@@ -439,15 +425,39 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
     // Akk shares its LDS with E1: the tiles of Akk wait in registers until every
     // wave is done with E1.
     f32x4 kkv[3];
+    // The tile of step it: wave-uniform (mat, i, j), or false past the last.
+    auto tile_at = [&](int it, int &mat, int &i, int &j) {
+        const int tix = wv + 4 * it;
+        if (tix >= 20) return false;
+        mat = tix / 10;
+        const int rem = tix % 10;
+        i = 0;
+        while ((i + 1) * (i + 2) / 2 <= rem) ++i;
+        j = rem - i * (i + 1) / 2;
+        return true;
+    };
+    // A tile's row fragments for all four k-steps (rows past the end read row 0
+    // and are zeroed when used).  The next tile's are loaded while this one is
+    // formed, so one load latency is waited out per wave, not one per tile.
+    auto fetch = [&](int it, F8 (&kc)[4], F8 (&xr)[4]) __attribute__((always_inline)) {
+        int mat, i, j;
+        if (!tile_at(it, mat, i, j)) return;
+        const float *X = mat == 0 ? k : q;
+        const int cr = 16 * j + lr, rr = 16 * i + lr;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            kc[ks] = ld_f8(k + tok(cr < len ? cr : 0) + 32 * ks + 8 * g);
+            xr[ks] = ld_f8(X + tok(rr < len ? rr : 0) + 32 * ks + 8 * g);
+        }
+    };
+    F8 kcb[2][4], xrb[2][4];
+    fetch(0, kcb[0], xrb[0]);
 #pragma unroll
     for (int it = 0; it < 5; ++it) {
-        const int tix = wv + 4 * it;
-        if (tix >= 20) break;
-        const int mat = tix / 10, rem = tix % 10;
-        int i = 0;
-        while ((i + 1) * (i + 2) / 2 <= rem) ++i;
-        const int j = rem - i * (i + 1) / 2;
-        const IO *X = mat == 0 ? k : q;
+        int mat, i, j;
+        if (!tile_at(it, mat, i, j)) break;
+        fetch(it + 1, kcb[(it + 1) & 1], xrb[(it + 1) & 1]);
+        const float *X = mat == 0 ? k : q;
         const int cr = 16 * j + lr;  // column-side token (A operand row)
         const int rr = 16 * i + lr;  // row-side token (B operand column)
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -457,23 +467,17 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
             const float nr = mat == 0 ? sm.nk[rr] : sm.nq[rr];
             const int c0 = 16 * i + 4 * g;
             for (int e = 0; e < D; ++e) {
-                const float xr = rr < len ? to_f(X[tok(rr) + e]) * nr : 0.f, lrr = sm.u.E1[rr * PG + e];
+                const float xr = rr < len ? X[tok(rr) + e] * nr : 0.f, lrr = sm.u.E1[rr * PG + e];
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const int cc = c0 + m;
-                    const float kc = cc < len ? to_f(k[tok(cc) + e]) * sm.nk[cc] : 0.f;
+                    const float kc = cc < len ? k[tok(cc) + e] * sm.nk[cc] : 0.f;
                     acc[m] += xr * kc * __expf(fminf(lrr - sm.u.E1[cc * PG + e], 0.f));
                 }
             }
         } else {
-        // the tile's row fragments for all four k-steps, loaded before the first
-        // product (rows past the end read row 0 and are zeroed)
-        F8 kcs[4], xrs[4];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            kcs[ks] = ld_io8(k + tok(cr < len ? cr : 0) + 32 * ks + 8 * g);
-            xrs[ks] = ld_io8(X + tok(rr < len ? rr : 0) + 32 * ks + 8 * g);
-        }
+        const F8(&kcs)[4] = kcb[it & 1];
+        const F8(&xrs)[4] = xrb[it & 1];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const int c0 = 32 * ks + 8 * g;
@@ -488,17 +492,14 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
                     inv = __expf((float)(sm.R[i * D + c0 + e] - sm.R[j * D + c0 + e]) - sm.u.E1[cr * PG + c0 + e]);
                     er = __expf(sm.u.E1[rr * PG + c0 + e]);
                 } else {
-                    inv = __frcp_rn(sm.u.E1[cr * PG + c0 + e]);  // e^{R_j - G_c}
+                    inv = __builtin_amdgcn_rcpf(sm.u.E1[cr * PG + c0 + e]);  // e^{R_j - G_c}, within 1 ulp
                     if (j < i) inv *= sm.PF[pair_index(i, j) * D + c0 + e];
                     er = sm.u.E1[rr * PG + c0 + e];
                 }
                 a.v[e] = kc.v[e] * nc * inv;
                 b.v[e] = xr.v[e] * nr * er;
             }
-            if constexpr (F32)
-                acc = mma_ff(acc, a, b);
-            else
-                acc = mma_ss(acc, split8(a), split8(b));
+            acc = mma_ff(acc, a, b);
         }
         }
         // acc[m] = M[r = rr][c = 16 j + 4 g + m]
@@ -515,7 +516,7 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
         if (mat == 0) {
             if (it < 3) kkv[it] = f32x4{val[0], val[1], val[2], val[3]};
         } else {
-            st_split4<F32>(blk + OFF_AQ, CH * CH, (size_t)rr * CH + cb, val[0], val[1], val[2], val[3]);
+            st4(blk + OFF_AQ, (size_t)rr * CH + cb, val[0], val[1], val[2], val[3]);
         }
     }
     __syncthreads();  // E1 is dead: Akk takes its place
@@ -576,11 +577,24 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
     }
 
     // ---- phase 4: W = T diag(beta) (K*Gam), U = T diag(beta) V, formed transposed ----
-    // wave wv: row tile rt = wv for W and 3 - wv for U; 8 column tiles each
+    // wave wv: row tile rt = wv for W and 3 - wv for U; 8 column tiles each.
+    // (K * Gam)^T comes from LDS, V^T from global memory: a column tile's V
+    // values are loaded one tile ahead (the first during the W products), rows
+    // past the end of the sequence read row 0 and are zeroed when used.
+    auto fetch_v = [&](int ct, F8 (&vc)[2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int t = 32 * ks + 8 * g + e;
+                vc[ks].v[e] = v[tok(t < len ? t : 0) + 16 * ct + lr];
+            }
+    };
+    F8 vb[2][2];
+    fetch_v(0, vb[0]);
+#pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
         const int rt = pass == 0 ? wv : 3 - wv;
-        // pass 0: (K * Gam)^T from LDS; pass 1: V^T read from global memory
-        // (rows past the end of the sequence as 0)
         const int nks = rt < 2 ? 1 : 2;
         const int r = 16 * rt + lr;
         F8 tb[2];
@@ -592,26 +606,9 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
                 tb[ks].v[e] = (ks < nks && cc <= r) ? sm.u.Akk[r * PT + cc] * sm.beta[cc] : 0.f;
             }
         }
-        S8 tbs[2];
-        if constexpr (!F32) {
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) tbs[ks] = split8(tb[ks]);
-        }
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct) {
-            // pass 1: this column tile's V values, all loaded before its products
-            // (rows past the end read row 0 and are zeroed)
-            F8 vcol[2];
-            if (pass == 1) {
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int t = 32 * ks + 8 * g + e;
-                        const float x = to_f(v[tok(t < len ? t : 0) + 16 * ct + lr]);
-                        vcol[ks].v[e] = t < len ? x : 0.f;
-                    }
-            }
+            if (pass == 1 && ct + 1 < 8) fetch_v(ct + 1, vb[(ct + 1) & 1]);
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
@@ -620,27 +617,14 @@ __global__ __launch_bounds__(256) void intra_kernel(const IO *__restrict__ q, co
                 if (pass == 0) {
                     xa = ld_f8(&sm.KG[(16 * ct + lr) * PT + 32 * ks + 8 * g]);
                 } else {
-                    xa = vcol[ks];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) xa.v[e] = 32 * ks + 8 * g + e < len ? vb[ct & 1][ks].v[e] : 0.f;
                 }
-                if constexpr (F32)
-                    acc = mma_ff(acc, xa, tb[ks]);
-                else
-                    acc = mma_1s(acc, round8(xa), tbs[ks]);
+                acc = mma_ff(acc, xa, tb[ks]);
             }
             // acc[m] = out[row r][col 16 ct + 4 g + m]
             const size_t e0 = (size_t)r * D + 16 * ct + 4 * g;
-            if (pass == 0) {
-                if constexpr (F32) {
-                    *(float4 *)((float *)(blk + OFF_W) + e0) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-                } else {
-                    bf16x4 hv;
-                    hv[0] = (__bf16)acc[0]; hv[1] = (__bf16)acc[1];
-                    hv[2] = (__bf16)acc[2]; hv[3] = (__bf16)acc[3];
-                    *(bf16x4 *)((__bf16 *)(blk + OFF_W) + e0) = hv;
-                }
-            } else {
-                *(float4 *)((float *)(blk + OFF_U) + e0) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-            }
+            st4(blk + (pass == 0 ? OFF_W : OFF_U), e0, acc[0], acc[1], acc[2], acc[3]);
         }
     }
 }
@@ -923,15 +907,17 @@ int launch_prefill(const void *q, const void *k, const void *v, bool f32io, cons
     // chain grids: 4 (state) or 8 (map) workgroups of 256 per (segment, head)
     // slot; a launch covers at most 2^32 - 1 work-items
     const int64_t slots8 = (nsm * H + 7) / 8;
-    if (slots8 * 128 > (int64_t)(UINT32_MAX / 256) || max_chunks(T_total, N) * H > (int64_t)UINT32_MAX) return -1;
+    if (slots8 * 128 > (int64_t)(UINT32_MAX / 256) || max_chunks(T_total, N) * H > (int64_t)UINT32_MAX ||
+        (int64_t)CH * H * D > (int64_t)INT32_MAX)
+        return -1;
     if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return -1;
     if (launch_seq_table(cu, N, T_total, T, tab.sq, stream) != 0) return -1;
     if (ck.S && launch_ckpt_prep(tab.sq, N, (int64_t)ck.stride_chunks * CH, tab.ckpt_off, stream) != 0) return -1;
     const int64_t nc = max_chunks(T_total, N);
     if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return -1;
     if (T_total > 0) {
-        const size_t smem = sizeof(IntraSmem<float>);
-        hipLaunchKernelGGL(intra_kernel<float>, dim3((unsigned)nc, (unsigned)H), dim3(256), smem, stream,
+        const size_t smem = sizeof(IntraSmem);
+        hipLaunchKernelGGL(intra_kernel, dim3((unsigned)nc, (unsigned)H), dim3(256), smem, stream,
                            (const float *)q, (const float *)k, (const float *)v, z, beta, A, N, H, tab);
     }
     if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return -1;
@@ -952,8 +938,8 @@ int launch_prefill(const void *q, const void *k, const void *v, bool f32io, cons
 
 int set_prefill_attributes() {
     if (set_segment_attributes() != 0) return -1;
-    const int smem = (int)sizeof(IntraSmem<float>);
-    if (hipFuncSetAttribute((const void *)intra_kernel<float>, hipFuncAttributeMaxDynamicSharedMemorySize, smem) !=
+    const int smem = (int)sizeof(IntraSmem);
+    if (hipFuncSetAttribute((const void *)intra_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, smem) !=
         hipSuccess)
         return -1;
     return 0;

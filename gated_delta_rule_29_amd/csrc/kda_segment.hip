@@ -1363,85 +1363,142 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
 // One workgroup per (sequence, head, 16 value columns): S_in[0] = S0 and
 // S_in[p+1] = M_p S_in[p] + B_p over the sequence's segments, with exact fp32
 // MFMA products (an identity transition reproduces the state bit for bit).
-// An empty sequence gets S_final = S0 here.  Eight waves of 16 rows each: a
-// step is 32 products per wave, and one map is 12 loads per wave, so the maps
-// of the next two steps stay in flight (the vmcnt counter holds 63).
-constexpr int SCAN_NT = 512;
+// An empty sequence gets S_final = S0 here.
+//
+// Eight compute waves of 16 rows each (a step is 32 products per wave) and one
+// store wave.  A compute wave copies its own 16 rows of M_p and of B_p's 16
+// columns straight into LDS (9 KB) and reads nothing else of the maps, so it
+// waits only for its own copies: a slot is refilled with the map two steps on
+// as soon as the wave has read it, and two slots keep two maps in flight.
+// Loads and stores share the in-order vmcnt counter; the store wave, which
+// copies S_in[p] out of the exchange buffer, keeps the state stores off the
+// compute waves' counter.
+constexpr int SCAN_NT = 576;
+constexpr int SCAN_WAVE_BYTES = 9216;              // 16 rows of M (swizzled), then the 16 x 16 tile of B
+constexpr int SCAN_SLOT_BYTES = 8 * SCAN_WAVE_BYTES;  // one map
+constexpr int SCAN_COPIES = 9;                       // copy instructions per wave and map
 __global__ __launch_bounds__(SCAN_NT) void seg_scan_kernel(const float *__restrict__ S0, int N, int H, SegTable tab,
                                                            float *__restrict__ S_final) {
-    __shared__ float Ss[16 * 132];  // S^T [column][row]
+    // Distinct arrays: a read of one provably does not alias a copy in flight into the other.
+    __shared__ __align__(16) char slot0[SCAN_SLOT_BYTES];
+    __shared__ __align__(16) char slot1[SCAN_SLOT_BYTES];
+    __shared__ __align__(16) float Ss[16 * 132];  // S_in[p]^T [column][row]
     const int nh = blockIdx.x, cb = blockIdx.y;
     const int n = nh / H, h = nh % H;
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, lr = l & 15;
-    const int col = 16 * cb + lr, r0 = 16 * w;
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, g = l >> 4,
+              lr = l & 15;
+    __builtin_assume(w >= 0 && w < 9);
+    const bool storer = w == 8;
+    const int col = 16 * cb + lr, r0 = 16 * (w & 7);
     const int first = tab.sq.seg0(n), pn = tab.sq.seg0(n + 1) - first;
     f32x4 Sr;
     const size_t s0b = ((size_t)n * H + h) * D * D;
 #pragma unroll
     for (int m = 0; m < 4; ++m) Sr[m] = S0 ? S0[s0b + (size_t)(r0 + 4 * g + m) * D + col] : 0.f;
     if (pn == 0) {
-        if (S_final)
+        if (S_final && !storer)
 #pragma unroll
             for (int m = 0; m < 4; ++m) S_final[s0b + (size_t)(r0 + 4 * g + m) * D + col] = Sr[m];
         return;
     }
-    // M_p and B_p are loaded two steps ahead into three rotating register sets
-    // (loads always issued: past the last map they re-read it).
-    F8 Mr[3][4];
-    f32x4 Br[3];
-    auto load_map = [&](int p, int set) __attribute__((always_inline)) {
-        const size_t b = ((size_t)(first + min(p, max(pn - 2, 0))) * H + h) * D * D;
+    // Steps run in pairs (one per slot), pn rounded up to even: an odd count
+    // ends with a step whose state nobody stores.  Every wave passes the same
+    // number of barriers.
+    const int pe = (pn + 1) & ~1;
+    if (storer) {
+        // Lane (row group l / 4, column quad l % 4) writes rows 16 k + l / 4,
+        // k = 0..7, four columns each; all read before the first store, so the
+        // stores issue back to back.  One pair of barriers per step, as below.
+        for (int p = 0; p < pe; ++p) {
+            lds_barrier();
+            f32x4 x[8];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) Br[set][m] = tab.Bseg[b + (size_t)(r0 + 4 * g + m) * D + col];
+            for (int k = 0; k < 8; ++k)
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) Mr[set][ks] = ld_f8(&tab.Mseg[b + (size_t)(r0 + lr) * D + 32 * ks + 8 * g]);
-    };
-    auto step = [&](int p, auto setc) __attribute__((always_inline)) {
-        constexpr int set = decltype(setc)::value;
-        const size_t b = ((size_t)(first + p) * H + h) * D * D;
-        float *sin = tab.Sin + b + (size_t)(r0 + 4 * g) * D + col;
-        if (p == pn - 1) {
+                for (int i = 0; i < 4; ++i) x[k][i] = Ss[(4 * (l & 3) + i) * 132 + 16 * k + (l >> 2)];
+            lds_barrier();
+            if (p < pn) {
+                float *sin = tab.Sin + ((size_t)(first + p) * H + h) * D * D + 16 * cb + 4 * (l & 3);
 #pragma unroll
-            for (int m = 0; m < 4; ++m) sin[(size_t)m * D] = Sr[m];
-            return;
+                for (int k = 0; k < 8; ++k) *(f32x4 *)(sin + (size_t)(16 * k + (l >> 2)) * D) = x[k];
+            }
         }
-        load_map(p + 2, (set + 2) % 3);
-        const f32x4 Sp = Sr;  // S_in[p]
-        // LDS-only barriers: a __syncthreads fence would also wait for the map
-        // loads just issued.
-        *(f32x4 *)&Ss[lr * 132 + r0 + 4 * g] = Sr;
+        return;
+    }
+    // The copies: M_p rows r0 + 2i, r0 + 2i + 1 by instruction i (lane l lands at
+    // 16 l), 16-byte column granule c of a row at granule c ^ (row & 7) of its
+    // LDS row, so the 16 rows one operand read touches fall in different banks;
+    // then B_p's tile, row l / 4, columns 4 (l % 4) ...  From the sequence's
+    // first map on: lane offsets fixed, the map offset (below 2^31: a sequence
+    // has at most 256 / H + 1 segments per head) a scalar.  Past the last map
+    // the copies re-read it.
+    const size_t mbase = ((size_t)first * H + h) * D * D;
+    const int mbytes = ((max(pn - 2, 0) * H) * D * D + D * D) * 4;
+    const __amdgpu_buffer_rsrc_t rM = __builtin_amdgcn_make_buffer_rsrc((void *)(tab.Mseg + mbase), 0, mbytes, BUF_RSRC3);
+    const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc((void *)(tab.Bseg + mbase), 0, mbytes, BUF_RSRC3);
+    const int wb = SCAN_WAVE_BYTES * w;
+    int vM[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int row = 2 * i + (l >> 5), c = (l & 31) ^ (row & 7);
+        vM[i] = (r0 + row) * D * 4 + 16 * c;
+    }
+    const int vB = ((r0 + (l >> 2)) * D + 16 * cb) * 4 + 16 * (l & 3);
+    auto copy_map = [&](int p, char *slot) __attribute__((always_inline)) {
+        const int so = min(p, max(pn - 2, 0)) * H * D * D * 4;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rM, (lds_void *)(slot + wb + 1024 * i), 16, vM[i], so, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_void *)(slot + wb + 8192), 16, vB, so, 0, 0);
+    };
+    auto step = [&](int p, char *slot) __attribute__((always_inline)) {
+        *(f32x4 *)&Ss[lr * 132 + r0 + 4 * g] = Sr;  // S_in[p]
         lds_barrier();
         F8 sb[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) sb[ks] = ld_f8(&Ss[lr * 132 + 32 * ks + 8 * g]);
-        lds_barrier();
+        lds_barrier();  // (its LDS wait also covers the reads of sb)
+        // (Steps at p >= pn - 1 compute states nobody reads, from the last
+        // map: no branch may come between the reads of sb above and their use,
+        // or the compiler may sink them below the barrier.)
+        // This map's copies have landed; the next map's (issued a step ago) may run.
+        __builtin_amdgcn_s_waitcnt(0x0F70 | SCAN_COPIES);
+        const char *mrow = slot + wb + 512 * lr;
+        F8 mr[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int c0 = 8 * ks + 2 * g;
+            const f32x4 lo = *(const f32x4 *)(mrow + 16 * (c0 ^ (lr & 7)));
+            const f32x4 hi = *(const f32x4 *)(mrow + 16 * ((c0 + 1) ^ (lr & 7)));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                mr[ks].v[e] = lo[e];
+                mr[ks].v[4 + e] = hi[e];
+            }
+        }
+        f32x4 a[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) a[0][m] = ((const float *)(slot + wb + 8192))[(4 * g + m) * 16 + lr];
+        // The slot is read: refill it with the map two steps on.
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        copy_map(p + 2, slot);
         // One accumulator per 32-row block of M (chains of 8 products, not 32),
         // added at the end: with M = I exactly one partial is nonzero, so an
         // identity transition still gives the state bit for bit.
-        f32x4 a[4];
-        a[0] = Br[set];
 #pragma unroll
         for (int ks = 1; ks < 4; ++ks) a[ks] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) a[ks] = mma_ff(a[ks], Mr[set][ks], sb[ks]);
+        for (int ks = 0; ks < 4; ++ks) a[ks] = mma_ff(a[ks], mr[ks], sb[ks]);
 #pragma unroll
         for (int m = 0; m < 4; ++m) Sr[m] = (a[0][m] + a[1][m]) + (a[2][m] + a[3][m]);
-        // (Stores and loads share the in-order vmcnt counter: before the
-        // registers a pending store reads are rewritten, everything issued
-        // before that store must complete, the map loads included.  The
-        // compiler reuses those registers within a step, so in practice the
-        // maps arrive one step ahead, and a step takes about one load latency,
-        // 2.9 us, wherever the stores are placed.)
-#pragma unroll
-        for (int m = 0; m < 4; ++m) sin[(size_t)m * D] = Sp[m];
     };
-    load_map(0, 0);
-    load_map(1, 1);
-    for (int p = 0; p < pn; p += 3) {
-        step(p, std::integral_constant<int, 0>{});
-        if (p + 1 < pn) step(p + 1, std::integral_constant<int, 1>{});
-        if (p + 2 < pn) step(p + 2, std::integral_constant<int, 2>{});
+    copy_map(0, slot0);
+    copy_map(1, slot1);
+    for (int p = 0; p < pe; p += 2) {
+        step(p, slot0);
+        step(p + 1, slot1);
     }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no copy may land after the workgroup ends
 }
 
 // ------------------------------------------------------------------ host --
