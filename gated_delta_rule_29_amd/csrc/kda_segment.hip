@@ -1189,10 +1189,17 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
             }
         }
         f32x4 Dl[4][NCT];  // Delta = U - W S accumulates onto this chunk's U
+        if (!PASS_A || colw >= 128) {
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
+            for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) Dl[rt][ct] = u_decode(Dcur[rt][ct], E);
+                for (int ct = 0; ct < NCT; ++ct) Dl[rt][ct] = u_decode(Dcur[rt][ct], E);
+        } else {  // pass A's columns of M: no U (their copies read nothing), nothing to decode
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) Dl[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
         if constexpr (!PASS_A) {
             if (chunk > cbeg) store_o(O, t0_prev, len_prev, (chunk - 1) & 1);
             if (ep) dma_gate(chunk);
