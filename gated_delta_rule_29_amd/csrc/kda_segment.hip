@@ -885,9 +885,6 @@ struct ChainTiles {
 #ifndef CHAIN_NBUF_A
 #define CHAIN_NBUF_A 3
 #endif
-// Image-copy instructions one wave issues per chunk in pass A (32 KB over 8
-// waves, and gamma).
-constexpr int CHAIN_DMA_OPS = 5;
 // Pass A's loop body: a common multiple of its image count and the two U
 // register sets.  The segment length L is a multiple of it.
 constexpr int CHAIN_UNROLL_A = CHAIN_NBUF_A == 3 ? 6 : 2;
@@ -911,14 +908,14 @@ constexpr int CH_NT = 64 * CH_NW;
 // waits for every LDS read to complete before the first use of any.
 // With `bytes` = 0 nothing is read and the copy writes zeros: issuing it
 // anyway keeps the number of copies in flight the same at every step.
-template <bool PASS_A>
+template <bool PASS_A, int NW>
 __device__ __forceinline__ void chain_dma(const char *__restrict__ blk, int bytes, char *lds, int wv, int l) {
     using Lo = ChainLds<PASS_A>;
     constexpr int NKB = Lo::GM / 1024;
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void *)blk, 0, bytes, BUF_RSRC3);
 #pragma unroll
-    for (int i = 0; i < (NKB + CH_NW - 1) / CH_NW; ++i) {
-        const int kb = wv + CH_NW * i;
+    for (int i = 0; i < (NKB + NW - 1) / NW; ++i) {
+        const int kb = wv + NW * i;
         if (kb < NKB) {
             const int x = 1024 * kb;
             const int src = (PASS_A && x >= Lo::KT) ? BO_KT + (x - Lo::KT) : x;
@@ -936,7 +933,14 @@ __device__ __forceinline__ void chain_dma(const char *__restrict__ blk, int byte
 // U); pass B: wave w owns value columns 16w .. 16w+15 of the state.
 // NBA: pass A's image count, 3 (a six-step loop body, segments a multiple of
 // 6 chunks) or 2 (two steps, for the short segments of short inputs).
-template <bool PASS_A, int NBA = CHAIN_NBUF_A>
+// SPLIT: for inputs with fewer (segment, head) pairs than half the CUs, two
+// workgroups per pair, each with half of the columns, so that twice as many
+// CUs share the work: pass A's eight waves take 16 columns each of M or of B,
+// pass B's four waves 16 value columns each.  The grid is then two halves of
+// G2 workgroups (G2 a multiple of 8, so that the two workgroups of a pair land
+// on one XCD and share its L2); the fused output step (which needs a row's 128
+// values in one workgroup) is not split.
+template <bool PASS_A, int NBA = CHAIN_NBUF_A, bool SPLIT = false>
 __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void seg_chain_kernel(
     int N, int H, SegTable tab, float *__restrict__ o, float *__restrict__ S_final) {
     using Lo = ChainLds<PASS_A>;
@@ -951,13 +955,23 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     // squares [parity][wave][row], and each wave's gate tile [wave][row][16].
     __shared__ __align__(16) float opart[PASS_A ? 4 : 2 * CH_NW * CH];
     __shared__ __align__(16) char ogate[PASS_A ? 16 : CH_NW * CH * 64];
-    constexpr int NCT = PASS_A ? 2 : 1;
+    // Column tiles per wave and waves per workgroup: split, pass A keeps its
+    // eight waves with one tile each, pass B runs four.
+    constexpr int NCT = PASS_A && !SPLIT ? 2 : 1;
+    constexpr int NW = SPLIT && !PASS_A ? 4 : CH_NW;
+    // Image-copy instructions one wave issues per chunk in pass A (its 32 KB
+    // over the waves, and gamma).
+    constexpr int DMA_OPS = (32 + NW - 1) / NW + 1;
+    static_assert(!SPLIT || NBA == 2 || DMA_OPS < 16, "vmcnt immediate");
 
     // Workgroup i takes head i mod H of the pass's (i / H)-th segment: the
     // workgroups with work come first and in one block, so they spread evenly
     // over the XCDs and none waits behind an empty one.  Pass A has no work for
     // a sequence's last segment (its map is not needed).
-    const int a = blockIdx.x / H, h = blockIdx.x % H;
+    const int G2 = (int)gridDim.x / 2;
+    const int half = SPLIT ? (int)blockIdx.x / G2 : 0;
+    const int bidx = SPLIT ? (int)blockIdx.x - half * G2 : (int)blockIdx.x;
+    const int a = bidx / H, h = bidx % H;
     if (a >= (PASS_A ? tab.sq.segA0(N) : tab.sq.seg0(N))) return;
     const int n = PASS_A ? tab.sq.seq_of_segA(a, N) : tab.sq.seq_of_seg(a, N);
     const int j = a - (PASS_A ? tab.sq.segA0(n) : tab.sq.seg0(n));
@@ -972,14 +986,15 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
 
     const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, g = l >> 4,
               lr = l & 15;
-    __builtin_assume(wv >= 0 && wv < CH_NW);
+    __builtin_assume(wv >= 0 && wv < NW);
     const size_t HD = (size_t)H * D;
     const size_t sblk = ((size_t)x * H + h) * D * D;
-    const int colw = 16 * NCT * wv;  // pass A: columns 0..127 are M, 128..255 are B
+    // pass A: columns 0..127 are M, 128..255 are B
+    const int colw = 16 * NCT * wv + (SPLIT ? (PASS_A ? 128 : 64) * half : 0);
     // U is read through a buffer resource that covers one block, or nothing for
     // the waves of M (their loads then return 0 without touching memory).
     const int u_records = (!PASS_A || colw >= 128) ? (int)BLK : 0;
-    const int utile = PASS_A ? max(colw - 128, 0) / 16 : wv;
+    const int utile = PASS_A ? max(colw - 128, 0) / 16 : colw / 16;
 
     f32x4 X[8][NCT];
 #pragma unroll
@@ -1054,7 +1069,7 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     // squares in LDS, and the deferred store adds the eight partials in wave
     // order (so the result does not depend on timing).  The gate tile of the
     // wave's columns is copied into LDS during the step before.
-    const bool ep = !PASS_A && tab.ly.gate != nullptr;
+    const bool ep = !PASS_A && !SPLIT && tab.ly.gate != nullptr;  // (the host never splits with it)
     const float wcol = ep ? tab.ly.weight[colw + lr] : 1.f;
     auto store_o = [&](const f32x4 (&O)[4], int64_t t0, int len, int par) {
         f32x4 Y[4];
@@ -1133,7 +1148,7 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     // next one.  Issue order (U of chunk n + 1, then the image of chunk
     // n + NBUF - 1) lets a step wait for everything but the newest image.
     auto dma = [&](int chunk, char *lds) __attribute__((always_inline)) {
-        chain_dma<PASS_A>(blk0 + (size_t)chunk * bstride, chunk < cend ? (int)BLK : 0, lds, wv, l);
+        chain_dma<PASS_A, NW>(blk0 + (size_t)chunk * bstride, chunk < cend ? (int)BLK : 0, lds, wv, l);
     };
     if (cbeg < cend) {
         dma(cbeg, buf0);
@@ -1152,9 +1167,9 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
         // This wave's copies of this chunk and its U have landed (waits in a
         // form the compiler sees, so it adds none of its own for them), then
         // every wave's have, and `nxt` is free.  With three images the newest
-        // copy (at most CHAIN_DMA_OPS instructions of this wave) may still run.
+        // copy (at most DMA_OPS instructions of this wave) may still run.
         // (Pass B also waits for its LDS writes: the output-step partials.)
-        __builtin_amdgcn_s_waitcnt(PASS_A ? 0x0F70 | (NBUF == 3 ? CHAIN_DMA_OPS : 0) : 0x0070);
+        __builtin_amdgcn_s_waitcnt(PASS_A ? 0x0F70 | (NBUF == 3 ? DMA_OPS : 0) : 0x0070);
         // The barrier is a bare s_barrier between compiler-only fences: the
         // waits above are the only memory ordering needed (no wave writes LDS
         // but by these copies, and every LDS read of the previous step has
@@ -1596,17 +1611,47 @@ int launch_segment_prefill(const __bf16 *q, const __bf16 *k, const __bf16 *v, co
         }
     }
     if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return -1;
+    // (segment, head) pairs of each chain pass: exact for a fixed-length batch,
+    // bounded by the table's capacity with cu_seqlens.  A pass whose pairs fill
+    // at most half the CUs runs split (two workgroups per pair).
+    int ncu = 0;
+    {
+        int dev = 0;
+        if (hipStreamGetDevice(stream, &dev) != hipSuccess ||
+            hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return -1;
+    }
+    int64_t pairsB = nsm * H, pairsA = nsm * H;
+    if (!cu) {
+        const int64_t segs = ((T + CH - 1) / CH + L - 1) / L;
+        pairsB = (int64_t)B * segs * H;
+        pairsA = (int64_t)B * (segs - 1) * H;
+    }
+    const bool splitA = 2 * pairsA <= ncu, splitB = 2 * pairsB <= ncu && ly.gate == nullptr;
     const dim3 cgrid((unsigned)(nsm * H));
-    if (L % CHAIN_UNROLL_A == 0)
-        hipLaunchKernelGGL((seg_chain_kernel<true, CHAIN_NBUF_A>), cgrid, dim3(CH_NT), 0, stream, N, H, tab, o,
-                           S_final);
-    else
-        hipLaunchKernelGGL((seg_chain_kernel<true, 2>), cgrid, dim3(CH_NT), 0, stream, N, H, tab, o, S_final);
+    const dim3 sgrid((unsigned)(2 * ((nsm * H + 7) / 8 * 8)));  // two halves, each a multiple of 8
+    if (L % CHAIN_UNROLL_A == 0) {
+        if (splitA)
+            hipLaunchKernelGGL((seg_chain_kernel<true, CHAIN_NBUF_A, true>), sgrid, dim3(CH_NT), 0, stream, N, H,
+                               tab, o, S_final);
+        else
+            hipLaunchKernelGGL((seg_chain_kernel<true, CHAIN_NBUF_A>), cgrid, dim3(CH_NT), 0, stream, N, H, tab, o,
+                               S_final);
+    } else {
+        if (splitA)
+            hipLaunchKernelGGL((seg_chain_kernel<true, 2, true>), sgrid, dim3(CH_NT), 0, stream, N, H, tab, o,
+                               S_final);
+        else
+            hipLaunchKernelGGL((seg_chain_kernel<true, 2>), cgrid, dim3(CH_NT), 0, stream, N, H, tab, o, S_final);
+    }
     if (ev && hipEventRecord(ev[3], stream) != hipSuccess) return -1;
     hipLaunchKernelGGL(seg_scan_kernel, dim3((unsigned)(N * H), 8), dim3(SCAN_NT), 0, stream, S0, N, H, tab, S_final);
     if (ev && hipEventRecord(ev[4], stream) != hipSuccess) return -1;
-    hipLaunchKernelGGL(seg_chain_kernel<false>, cgrid, dim3(CH_NT), 0, stream, N, H, tab,
-                       o, S_final);
+    if (splitB)
+        hipLaunchKernelGGL((seg_chain_kernel<false, CHAIN_NBUF_A, true>), sgrid, dim3(CH_NT / 2), 0, stream, N, H,
+                           tab, o, S_final);
+    else
+        hipLaunchKernelGGL(seg_chain_kernel<false>, cgrid, dim3(CH_NT), 0, stream, N, H, tab, o, S_final);
     if (hipGetLastError() != hipSuccess) return -1;
     if (ev && hipEventRecord(ev[5], stream) != hipSuccess) return -1;
     return 0;

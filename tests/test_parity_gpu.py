@@ -224,6 +224,20 @@ def test_head_counts(H, T, io):
 
 
 @pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("lens", [[768], [2112], [768, 1280, 320]])
+def test_odd_segment_counts(lens, io):
+    """Sequences cut into an odd number of segments above one (3, 9; a pack with 3, 5
+    and 2 at H = 16 with bf16 q/k/v): the scan runs its steps in pairs and pads an odd
+    count with a step whose state is not stored."""
+    H = 16
+    cu = synth.cu_seqlens(lens) if len(lens) > 1 else None
+    d = synth.prefill_inputs(3700 + sum(lens), sum(lens), H, dtype=io, s0_std=0.02, n_seqs=len(lens))
+    say(f"case odd segments lens={lens} io={io}")
+    o, Sf = run_prefill(d, S0=d["S0"], cu=cu, io=io)
+    check(d, o, Sf, cu=cu, io=io, label=f"lens={lens}")
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
 def test_many_short_sequences(io):
     """1,500 sequences of lengths 0..40 (a third of them empty): the sequence tables are
     built by scans over several 256-wide blocks, and most sequences hold one partial chunk."""
