@@ -932,7 +932,7 @@ __device__ __forceinline__ void chain_dma(const char *__restrict__ blk, int byte
 // 32w .. 32w+31 of X = [M | B] (waves 0-3: M, from I; waves 4-7: B, from 0, with
 // U); pass B: wave w owns value columns 16w .. 16w+15 of the state.
 // NBA: pass A's image count, 3 (a six-step loop body, segments a multiple of
-// 6 chunks) or 2 (two steps, for the short segments of short inputs).
+// 6 chunks) or 2 (a two-step body, any even segment length).
 // SPLIT: for inputs with fewer (segment, head) pairs than half the CUs, two
 // workgroups per pair, each with half of the columns, so that twice as many
 // CUs share the work: pass A's eight waves take 16 columns each of M or of B,
@@ -1540,15 +1540,18 @@ constexpr int SEG_TARGET_WGS = 256;  // chain workgroups in flight: one per CU (
 #ifndef SEG_L_MIN
 #define SEG_L_MIN 4
 #endif
-// Chunks per segment: about SEG_TARGET_WGS (segment, head) pairs in all, and a
-// whole number of pass-A loop bodies: a multiple of 6 (three images) from 6
-// chunks on, else of 2 (the two-image pass A of short inputs).
+// Chunks per segment: about SEG_TARGET_WGS (segment, head) pairs in all,
+// rounded up to even (a whole number of two-step pass-A loop bodies; the
+// three-image pass A runs when L is also a multiple of 6).  Its steps take the
+// same time with two images as with three, so L is not rounded further: at
+// 64K x 16, L = 64 (16 equal segments per head) ran pass A in 0.202 ms against
+// 0.209 ms with L = 66.
 static inline int seg_len(int64_t T_total, int H) {
     const int64_t nc = (T_total + CH - 1) / CH;
     const int64_t per_head = SEG_TARGET_WGS / (H > 0 ? H : 1) > 0 ? SEG_TARGET_WGS / H : 1;
     int64_t L = (nc + per_head - 1) / per_head;
     L = L < SEG_L_MIN ? SEG_L_MIN : L;
-    L = L >= CHAIN_UNROLL_A ? (L + CHAIN_UNROLL_A - 1) / CHAIN_UNROLL_A * CHAIN_UNROLL_A : (L + 1) / 2 * 2;
+    L = (L + 1) / 2 * 2;
     return (int)L;
 }
 static inline int64_t seg_chunks_max(int64_t T_total, int N) { return (T_total + CH - 1) / CH + N; }
