@@ -146,6 +146,48 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+
+__device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// fp16 hi/lo split of a pair of floats: hi = fp16(a), fp16(b), lo = fp16 of the
+// remainders.  a - fp32(hi) is exact in fp32, so one mixed-precision FMA per
+// element (fp16 hi and fp32 a as sources, fp16 result) gives the same lo as a
+// subtraction in fp32 followed by a conversion, in one instruction.
+__device__ __forceinline__ void split_f16_pair(float a, float b, uint32_t &hi, uint32_t &lo) {
+    const f16x2 h = {(_Float16)a, (_Float16)b};
+    hi = __builtin_bit_cast(uint32_t, h);
+    asm("v_fma_mixlo_f16 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mixhi_f16 %0, -%1, 1.0, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+        : "=&v"(lo)
+        : "v"(hi), "v"(a), "v"(b));
+}
+
+// Unsigned maximum over one DPP row (16 lanes with equal lane / 16), in every lane.
+__device__ __forceinline__ uint32_t row_umax16(uint32_t x) {
+    x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x141, 0xF, 0xF, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x140, 0xF, 0xF, false));
+    return x;
+}
+// Unsigned maximum over the whole wave, wave-uniform (so the compiler keeps it
+// in a scalar register and branches on it without divergence).
+__device__ __forceinline__ uint32_t wave_umax(uint32_t x) {
+    x = row_umax16(x);
+    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)x, 0), b = (uint32_t)__builtin_amdgcn_readlane((int)x, 16),
+                   c = (uint32_t)__builtin_amdgcn_readlane((int)x, 32), d = (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
+    return max(max(a, b), max(c, d));
+}
+// Buffer resource word 3 for raw (untyped) buffer access on gfx9-family chips:
+// 32-bit data format, so accesses past num_records read 0 and drop writes.
+constexpr int BUF_RSRC3 = 0x00020000;
 // Eight fp32 values of one lane's 32-deep k slice.
 struct F8 {
     float v[8];

@@ -28,29 +28,42 @@
 //                 blocked forward substitution, W and U on MFMA; writes the
 //                 per-chunk operands of the chain to the workspace;
 //   chain_kernel<true>   the affine map S -> M S + B of every segment but a
-//                 sequence's last, one workgroup per (segment, head, 32 of
+//                 sequence's last, one workgroup per (segment, head, 64 of
 //                 the 256 columns of [M | B]);
 //   seg_scan_kernel (kda_segment.hip)  the state entering each segment;
 //   chain_kernel<false>  one workgroup per (segment, head, 32 value columns):
 //                 keeps its 128 x 32 fp32 state slice in registers across the
 //                 segment's chunks and forms Delta, the output and the next
 //                 state with MFMA.
+//   (The scan and the layer's output step as in the bf16 path.)
 //
-// This file serves fp32 q/k/v (bf16 q/k/v take kda_segment.hip's path): every
-// operand is fp32 and every product an exact fp32 MFMA.
+// This file serves fp32 q/k/v (bf16 q/k/v take kda_segment.hip's path).
+// intra_kernel computes in fp32 with exact fp32 MFMA products.  The chain
+// kernels multiply fp16 hi + lo pairs (x = hi + lo, hi = fp16(x), lo =
+// fp16(x - hi): 22 significant bits) with three v_mfma_f32_16x16x32_f16 per
+// product, hi*hi + hi*lo + lo*hi, accumulating in fp32; the dropped lo*lo term
+// is below 2^-22 of the product.  That is 16 times the fp32 MFMA rate for a
+// third of it.  W, Q~, K~ and Aqk are stored as such pairs; under the operator's
+// preconditions (unit-length q and k, beta in [0, 1], decay factors <= 1)
+// their entries are at most about 1 in magnitude, where fp16 holds them to 22
+// bits down to 2^-3 and to 2^-25 absolutely below.  The state and Delta are
+// split on the fly at a power-of-two scale per workgroup that keeps them inside
+// fp16's range.
 #include "kda_common.hpp"
 
 namespace kda {
 
 // ----------------------------------------------------------------- layout --
 
-// Per (chunk, head) block of chain operands in the workspace (bytes), all fp32.
-constexpr size_t OFF_W = 0;            // W      [64][128]
-constexpr size_t OFF_U = 32768;        // U      [64][128]
-constexpr size_t OFF_KT = 65536;       // K~^T   [128][64]  K~ = K * e^{G_n - G}
-constexpr size_t OFF_QT = 98304;       // Q~     [64][128]  Q~ = Q * Gam
-constexpr size_t OFF_AQ = 131072;      // Aqk    [64][64]   zero above the diagonal
+// Per (chunk, head) block of chain operands in the workspace (bytes).  "hi/lo":
+// the array of fp16 hi values, then the array of fp16 lo values (n entries each).
+constexpr size_t OFF_W = 0;            // -W     [64][128]  hi/lo, n = 8192
+constexpr size_t OFF_U = 32768;        // U      [64][128]  fp32
+constexpr size_t OFF_KT = 65536;       // K~^T   [128][64]  hi/lo, n = 8192; K~ = K * e^{G_n - G}
+constexpr size_t OFF_QT = 98304;       // Q~     [64][128]  hi/lo, n = 8192; Q~ = Q * Gam
+constexpr size_t OFF_AQ = 131072;      // Aqk    [64][64]   hi/lo, n = 4096; zero above the diagonal
 constexpr size_t OFF_GM = 147456;      // gamma  [128]      fp32, e^{G_n}
+constexpr size_t NW_ = 8192, NAQ = 4096;  // entries of the [64][128] and [64][64] hi/lo arrays
 constexpr size_t BLK_BYTES = 147968;   // multiple of 256
 
 __host__ __device__ constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -241,6 +254,15 @@ __device__ __forceinline__ int pair_index(int i, int j) { return i * (i - 1) / 2
 __device__ __forceinline__ void st4(char *base, size_t e, float a, float b, float c, float d) {
     *(float4 *)((float *)base + e) = make_float4(a, b, c, d);
 }
+// the same into the hi/lo arrays at base (n entries each)
+__device__ __forceinline__ void st4h(char *base, size_t e, size_t n, float a, float b, float c, float d) {
+    uint32_t h0, l0, h1, l1;
+    split_f16_pair(a, b, h0, l0);
+    split_f16_pair(c, d, h1, l1);
+    *(u32x2 *)((_Float16 *)base + e) = u32x2{h0, h1};
+    *(u32x2 *)((_Float16 *)base + n + e) = u32x2{l0, l1};
+}
+
 
 __global__ __launch_bounds__(256) void intra_kernel(const float *__restrict__ q, const float *__restrict__ k,
                                                     const float *__restrict__ v, const float *__restrict__ z,
@@ -399,12 +421,21 @@ __global__ __launch_bounds__(256) void intra_kernel(const float *__restrict__ q,
                 const float kv = ok ? kr[u] * sm.nk[t] : 0.f;
                 const float qv = ok ? qr[u] * sm.nq[t] : 0.f;
                 sm.KG[ch * PT + t] = kv * gam;
-                ((float *)qt)[(size_t)t * D + ch] = qv * gam;
+                // Q~ pairs channels ch, ch ^ 1 (lanes l, l ^ 1): the even lane
+                // stores the pair's hi values, the odd lane its lo values
+                const float qg = qv * gam;
+                const float qo = __builtin_bit_cast(
+                    float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, qg), 0xB1, 0xF, 0xF, false));
+                const bool odd = ch & 1;
+                uint32_t hi2, lo2;
+                split_f16_pair(odd ? qo : qg, odd ? qg : qo, hi2, lo2);
+                *(uint32_t *)((_Float16 *)qt + (odd ? NW_ : 0) + (size_t)t * D + (ch & ~1)) = odd ? lo2 : hi2;
                 kt_vals[u] = kv * __expf((float)(Gn - Gt));
             }
 #pragma unroll
             for (int u = 0; u < SUB; u += 4)
-                st4(kt, (size_t)ch * CH + s * SUB + u, kt_vals[u], kt_vals[u + 1], kt_vals[u + 2], kt_vals[u + 3]);
+                st4h(kt, (size_t)ch * CH + s * SUB + u, NW_, kt_vals[u], kt_vals[u + 1], kt_vals[u + 2],
+                     kt_vals[u + 3]);
         }
         if (half == 0) ((float *)(blk + OFF_GM))[ch] = __expf((float)Gn);
     }
@@ -414,7 +445,7 @@ __global__ __launch_bounds__(256) void intra_kernel(const float *__restrict__ q,
         const int ti = tile < 3 ? 0 : (tile < 5 ? 1 : 2);
         const int tj = tile < 3 ? tile + 1 : (tile < 5 ? tile - 1 : 3);
         const int r = 16 * ti + (quad >> 2), c0 = 16 * tj + 4 * (quad & 3);
-        st4(blk + OFF_AQ, (size_t)r * CH + c0, 0.f, 0.f, 0.f, 0.f);
+        st4h(blk + OFF_AQ, (size_t)r * CH + c0, NAQ, 0.f, 0.f, 0.f, 0.f);
     }
     __syncthreads();
 
@@ -516,7 +547,7 @@ __global__ __launch_bounds__(256) void intra_kernel(const float *__restrict__ q,
         if (mat == 0) {
             if (it < 3) kkv[it] = f32x4{val[0], val[1], val[2], val[3]};
         } else {
-            st4(blk + OFF_AQ, (size_t)rr * CH + cb, val[0], val[1], val[2], val[3]);
+            st4h(blk + OFF_AQ, (size_t)rr * CH + cb, NAQ, val[0], val[1], val[2], val[3]);
         }
     }
     __syncthreads();  // E1 is dead: Akk takes its place
@@ -624,35 +655,71 @@ __global__ __launch_bounds__(256) void intra_kernel(const float *__restrict__ q,
             }
             // acc[m] = out[row r][col 16 ct + 4 g + m]
             const size_t e0 = (size_t)r * D + 16 * ct + 4 * g;
-            st4(blk + (pass == 0 ? OFF_W : OFF_U), e0, acc[0], acc[1], acc[2], acc[3]);
+            if (pass == 0)
+                st4h(blk + OFF_W, e0, NW_, -acc[0], -acc[1], -acc[2], -acc[3]);
+            else
+                st4(blk + OFF_U, e0, acc[0], acc[1], acc[2], acc[3]);
         }
     }
 }
 
 // ----------------------------------------------------------------- chain --
 
-constexpr int NCT = 2;         // 16-column tiles per workgroup
-constexpr int NB = 16 * NCT;  // state columns per workgroup
+// 16-column tiles per workgroup: the map pass takes 64 of its 256 columns
+// (with 32, its 896 workgroups at 64K x 16 ran in two rounds: 1.05 against
+// 0.70 ms), the state pass 32 (its registers allow no more).
+template <bool MAP>
+constexpr int chain_nct() { return MAP ? 4 : 2; }
+constexpr int PSH = 136;      // pitch (halves) of the state arrays
+constexpr int PDH = 72;       // pitch (halves) of the Delta arrays
 
+template <int NB>
 struct ChainSmem {
-    float S[NB * 132];  // the state slice, transposed [column][key row]
-    float Dl[NB * 68];  // Delta, transposed [column][token]
+    // the state slice times 2^E as fp16 hi + lo, transposed [column][key row]
+    __attribute__((aligned(16))) _Float16 Sh[NB * PSH], Slo[NB * PSH];
+    // Delta times 2^E as fp16 hi + lo, transposed [column][token]
+    __attribute__((aligned(16))) _Float16 Dh[NB * PDH], Dlo[NB * PDH];
+    uint32_t ex[4];  // per wave: exponent bound of its state rows and U rows
 };
 
-// The chain over one segment of a sequence, 32 state columns per workgroup
-// (each operand fragment loaded serves both 16-column tiles), exact fp32 MFMA
-// throughout.  The segment map carries a state S entering the segment to
-// M S + B; MAP = true computes the columns of X = [M | B] (128 x 256) by
+// A fragment as fp16 hi + lo.
+struct H8 {
+    f16x8 hi, lo;
+};
+// k slice at entry e of the hi/lo arrays at base (n entries each), 16-byte aligned
+__device__ __forceinline__ H8 ld_h8(const char *base, size_t e, size_t n) {
+    return {*(const f16x8 *)((const _Float16 *)base + e), *(const f16x8 *)((const _Float16 *)base + n + e)};
+}
+// c + a b with a, b as hi + lo: the two cross terms, then hi * hi
+__device__ __forceinline__ f32x4 mma_hh(f32x4 c, const H8 &a, const H8 &b) {
+    c = mfma_f16(a.lo, b.hi, c);
+    c = mfma_f16(a.hi, b.lo, c);
+    return mfma_f16(a.hi, b.hi, c);
+}
+__device__ __forceinline__ uint32_t abs_bits(float x) { return __builtin_bit_cast(uint32_t, x) & 0x7FFFFFFFu; }
+
+// The chain over one segment of a sequence, 16 NCT state columns per
+// workgroup (each operand fragment loaded serves all NCT column tiles),
+// products as fp16 hi + lo pairs.  The segment map carries a state S entering the segment
+// to M S + B; MAP = true computes the columns of X = [M | B] (128 x 256) by
 // running the chain step from X = [I | 0], with U entering only the B columns;
 // MAP = false runs it from the state the scan gave the segment and writes o
 // (and snapshots, and S_final after a sequence's last segment).  Workgroups
 // are numbered so that the column blocks of one (segment, head) share an XCD
 // (and its L2, which serves their common operand block), and the (segment,
 // head) pairs with work come first.
+//
+// The workgroup carries its state columns, U, Delta and O times 2^E.  The map
+// is linear in (S, U) column by column, so any power-of-two scale is exact; E
+// is re-picked whenever the largest |S| or |U| of the workgroup leaves
+// [2^7, 2^11).  Then |Delta| = |U - W S| < 2^11 (1 + sqrt(128)) < 2^15 (each
+// row of W has norm <= 1 with unit keys and beta in [0, 1]), inside fp16's
+// range, and values 2^-10 below the largest keep all 22 bits of the pair.
 template <bool MAP>
-__global__ __launch_bounds__(256) void chain_kernel(int N, int H, Table tab, float *__restrict__ o,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void chain_kernel(int N, int H, Table tab, float *__restrict__ o,
                                                     float *__restrict__ S_final) {
-    __shared__ ChainSmem sm;
+    constexpr int NCT = chain_nct<MAP>(), NB = 16 * NCT;  // state columns per workgroup
+    __shared__ ChainSmem<NB> sm;
     constexpr int NCB = (MAP ? 2 * D : D) / NB;  // column blocks per (segment, head)
     const int Lw = blockIdx.x;
     const int p = (Lw & 7) + 8 * (Lw / (8 * NCB)), cb = (Lw >> 3) % NCB;
@@ -663,6 +730,7 @@ __global__ __launch_bounds__(256) void chain_kernel(int N, int H, Table tab, flo
     const int x = tab.sq.seg0(n) + j;  // segment index of the maps and states
     const int pn = tab.sq.seg0(n + 1) - tab.sq.seg0(n);
     const bool bcol = MAP && cb >= NCB / 2;              // columns of B (U enters)
+    const bool use_u = !MAP || bcol;
     const int col0 = NB * (MAP ? cb % (NCB / 2) : cb);  // first column within M, B or the state
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, lr = l & 15;
 
@@ -679,6 +747,7 @@ __global__ __launch_bounds__(256) void chain_kernel(int N, int H, Table tab, flo
                 const int r = 32 * w + 16 * u + 4 * g + m, cc = col0 + 16 * ct + lr;
                 Sr[ct][u][m] = MAP ? (!bcol && r == cc ? 1.f : 0.f) : tab.Sin[sblk + (size_t)r * D + cc];
             }
+    int E = 0;
 
     const int cseq = tab.sq.chunk0(n);  // the sequence's first chunk
     const int cbeg = cseq + j * tab.sq.L, cend = min(tab.sq.chunk0(n + 1), cbeg + tab.sq.L);
@@ -687,103 +756,163 @@ __global__ __launch_bounds__(256) void chain_kernel(int N, int H, Table tab, flo
     const int64_t ck_base = tab.ck.S ? tab.ck.off[n] : 0;
 
     // Operands of one chunk, in registers.  The barriers wait only for LDS
-    // traffic, so loads stay in flight across them.  The map pass loads each
-    // group for chunk c + 1 as soon as chunk c has used it (the last chunk
-    // re-reads itself); the state pass, which has no registers to spare for
-    // that, issues all of chunk c's loads at the top of its step.
+    // traffic, so loads stay in flight across them.  U is loaded one chunk
+    // ahead (its largest value sets the step's scale before the first barrier).
+    // The map pass loads each other group for chunk c + 1 as soon as chunk c has
+    // used it (the last chunk re-reads itself); the state pass, which has no
+    // registers to spare for that, issues all of chunk c's loads at the top of
+    // its step.
     constexpr bool PF = MAP;
     const int row = 16 * w + lr;
-    F8 wf[4], qf[4], kf[2][2], af[2];
+    H8 wf[4], qf[4], kf[2][2], af[2];
     float uv[NCT][4], gmv[2][4];
-    auto load_wq = [&](const char *blk) __attribute__((always_inline)) {
+    auto load_w = [&](const char *blk) __attribute__((always_inline)) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            wf[ks] = ld_f8((const float *)(blk + OFF_W) + row * D + 32 * ks + 8 * g);
-            if constexpr (!MAP) qf[ks] = ld_f8((const float *)(blk + OFF_QT) + row * D + 32 * ks + 8 * g);
+            wf[ks] = ld_h8(blk + OFF_W, row * D + 32 * ks + 8 * g, NW_);
+            if constexpr (!MAP) qf[ks] = ld_h8(blk + OFF_QT, row * D + 32 * ks + 8 * g, NW_);
         }
+    };
+    // (the map's M columns read nothing: a buffer of no records reads 0)
+    auto load_u = [&](const char *blk) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t ru = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(blk + OFF_U + 4 * (16 * w * D + col0)), 0, use_u ? 16 * D * 4 : 0, BUF_RSRC3);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
             for (int m = 0; m < 4; ++m)
-                uv[ct][m] = (!MAP || bcol)
-                                ? ((const float *)(blk + OFF_U))[(16 * w + 4 * g + m) * D + col0 + 16 * ct + lr]
-                                : 0.f;
+                uv[ct][m] = __builtin_bit_cast(
+                    float, __builtin_amdgcn_raw_buffer_load_b32(ru, 4 * ((4 * g + m) * D + 16 * ct + lr), 0, 0));
     };
     auto load_ka = [&](const char *blk) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int kr = 32 * w + 16 * u;
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-                kf[u][ks] = ld_f8((const float *)(blk + OFF_KT) + (kr + lr) * CH + 32 * ks + 8 * g);
+            for (int ks = 0; ks < 2; ++ks) kf[u][ks] = ld_h8(blk + OFF_KT, (kr + lr) * CH + 32 * ks + 8 * g, NW_);
 #pragma unroll
             for (int m = 0; m < 4; ++m) gmv[u][m] = ((const float *)(blk + OFF_GM))[kr + 4 * g + m];
         }
         if constexpr (!MAP)
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) af[ks] = ld_f8((const float *)(blk + OFF_AQ) + row * CH + 32 * ks + 8 * g);
+            for (int ks = 0; ks < 2; ++ks) af[ks] = ld_h8(blk + OFF_AQ, row * CH + 32 * ks + 8 * g, NAQ);
     };
     auto block = [&](int cc) { return tab.blocks + ((size_t)cc * H + h) * BLK_BYTES; };
-    if (PF && cbeg < cend) {
-        load_wq(block(cbeg));
-        load_ka(block(cbeg));
+    // This wave's rows of the state slice, split, into the B-operand arrays.
+    // (Values past fp16's range become inf here; the step then rescales and
+    // publishes again before anything reads them.)
+    auto publish_state = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                uint32_t h0, l0, h1, l1;
+                split_f16_pair(Sr[ct][u][0], Sr[ct][u][1], h0, l0);
+                split_f16_pair(Sr[ct][u][2], Sr[ct][u][3], h1, l1);
+                const int e0 = (16 * ct + lr) * PSH + 32 * w + 16 * u + 4 * g;
+                *(u32x2 *)&sm.Sh[e0] = u32x2{h0, h1};
+                *(u32x2 *)&sm.Slo[e0] = u32x2{l0, l1};
+            }
+    };
+    if (cbeg < cend) {
+        load_u(block(cbeg));
+        if (PF) {
+            load_w(block(cbeg));
+            load_ka(block(cbeg));
+        }
     }
 
     for (int c = cbeg; c < cend; ++c) {
         const char *nblk = block(min(c + 1, cend - 1));
         if (!PF) {
-            load_wq(block(c));
+            load_w(block(c));
             load_ka(block(c));
         }
         const int64_t t0 = sstart + (int64_t)(c - cseq) * CH;
         const int len = (int)min((int64_t)CH, send - t0);
 
-        // (1) publish the state slice as the B operand of W S and Q~ S
+        // (1) publish the state slice as the B operand of W S and Q~ S, and this
+        // wave's exponent bound: the fp32 exponent field of max(|S|, |U| 2^E)
+        // (255: inf or NaN present, which keeps E: the result is not finite).
+        {
+            uint32_t ms = 0, mu = 0;
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
+            for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-            for (int u = 0; u < 2; ++u)
-                *(float4 *)&sm.S[(16 * ct + lr) * 132 + 32 * w + 16 * u + 4 * g] =
-                    make_float4(Sr[ct][u][0], Sr[ct][u][1], Sr[ct][u][2], Sr[ct][u][3]);
+                for (int m = 0; m < 4; ++m) {
+                    ms = max(ms, max(abs_bits(Sr[ct][0][m]), abs_bits(Sr[ct][1][m])));
+                    mu = max(mu, abs_bits(uv[ct][m]));
+                }
+            const int es = (int)(ms >> 23), eu = (int)(mu >> 23);
+            const int el = (es == 255 || eu == 255) ? 0xFFFF : max(es, eu ? max(eu + E, 0) : 0);
+            const uint32_t ew = wave_umax((uint32_t)el);
+            publish_state();
+            if (l == 0) sm.ex[w] = ew;
+        }
         lds_barrier();
+        {
+            const uint32_t e = __builtin_amdgcn_readfirstlane(max(max(sm.ex[0], sm.ex[1]), max(sm.ex[2], sm.ex[3])));
+            if (e != 0xFFFF && e != 0 && (e < 134 || e > 137)) {  // rescale (every wave takes this branch)
+                const int sh = 136 - (int)e;
+                E += sh;
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                    for (int u = 0; u < 2; ++u)
+#pragma unroll
+                        for (int m = 0; m < 4; ++m) Sr[ct][u][m] = __builtin_amdgcn_ldexpf(Sr[ct][u][m], sh);
+                publish_state();
+                lds_barrier();
+            }
+        }
 
-        // (2) Delta rows [16w, 16w+16) = U - W S ;  O = Q~ S
+        // (2) Delta rows [16w, 16w+16) = U 2^E - W S (W stored negated, the
+        // accumulator starts at U 2^E);  O = Q~ S
         f32x4 ws[NCT], oacc[NCT];
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) ws[ct] = oacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) ws[ct][m] = __builtin_amdgcn_ldexpf(uv[ct][m], E);
+            oacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        load_u(nblk);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
-                const F8 sb = ld_f8(&sm.S[(16 * ct + lr) * 132 + 32 * ks + 8 * g]);
-                ws[ct] = mma_ff(ws[ct], wf[ks], sb);
-                if constexpr (!MAP) oacc[ct] = mma_ff(oacc[ct], qf[ks], sb);
+                const int e0 = (16 * ct + lr) * PSH + 32 * ks + 8 * g;
+                const H8 sb = {*(const f16x8 *)&sm.Sh[e0], *(const f16x8 *)&sm.Slo[e0]};
+                ws[ct] = mma_hh(ws[ct], wf[ks], sb);
+                if constexpr (!MAP) oacc[ct] = mma_hh(oacc[ct], qf[ks], sb);
             }
         }
-        f32x4 dl[NCT];
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-            for (int m = 0; m < 4; ++m) dl[ct][m] = uv[ct][m] - ws[ct][m];
-        if (PF) load_wq(nblk);
+        if (PF) load_w(nblk);
         // (3) publish Delta as the B operand of Aqk Delta and K~^T Delta
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-            *(float4 *)&sm.Dl[(16 * ct + lr) * 68 + 16 * w + 4 * g] =
-                make_float4(dl[ct][0], dl[ct][1], dl[ct][2], dl[ct][3]);
+        for (int ct = 0; ct < NCT; ++ct) {
+            uint32_t h0, l0, h1, l1;
+            split_f16_pair(ws[ct][0], ws[ct][1], h0, l0);
+            split_f16_pair(ws[ct][2], ws[ct][3], h1, l1);
+            const int e0 = (16 * ct + lr) * PDH + 16 * w + 4 * g;
+            *(u32x2 *)&sm.Dh[e0] = u32x2{h0, h1};
+            *(u32x2 *)&sm.Dlo[e0] = u32x2{l0, l1};
+        }
         lds_barrier();
-        F8 dF[NCT][2];
+        H8 dF[NCT][2];
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) dF[ct][ks] = ld_f8(&sm.Dl[(16 * ct + lr) * 68 + 32 * ks + 8 * g]);
+            for (int ks = 0; ks < 2; ++ks) {
+                const int e0 = (16 * ct + lr) * PDH + 32 * ks + 8 * g;
+                dF[ct][ks] = {*(const f16x8 *)&sm.Dh[e0], *(const f16x8 *)&sm.Dlo[e0]};
+            }
         // (4) O += Aqk Delta  (row tile w; Aqk is zero above the diagonal)
         if constexpr (!MAP)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
                 if (ks < nks_aq)
 #pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct) oacc[ct] = mma_ff(oacc[ct], af[ks], dF[ct][ks]);
+                    for (int ct = 0; ct < NCT; ++ct) oacc[ct] = mma_hh(oacc[ct], af[ks], dF[ct][ks]);
         // (5) S <- Diag(gamma) S + K~^T Delta  (key rows [32w, 32w+32))
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -795,7 +924,7 @@ __global__ __launch_bounds__(256) void chain_kernel(int N, int H, Table tab, flo
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) acc[ct] = mma_ff(acc[ct], kf[u][ks], dF[ct][ks]);
+                for (int ct = 0; ct < NCT; ++ct) acc[ct] = mma_hh(acc[ct], kf[u][ks], dF[ct][ks]);
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) Sr[ct][u] = acc[ct];
         }
@@ -812,7 +941,8 @@ __global__ __launch_bounds__(256) void chain_kernel(int N, int H, Table tab, flo
                         for (int u = 0; u < 2; ++u)
 #pragma unroll
                             for (int m = 0; m < 4; ++m)
-                                dst[(size_t)(32 * w + 16 * u + 4 * g + m) * D + col0 + 16 * ct + lr] = Sr[ct][u][m];
+                                dst[(size_t)(32 * w + 16 * u + 4 * g + m) * D + col0 + 16 * ct + lr] =
+                                    __builtin_amdgcn_ldexpf(Sr[ct][u][m], -E);
                 }
             }
             // (6) output rows of this chunk
@@ -821,7 +951,8 @@ __global__ __launch_bounds__(256) void chain_kernel(int N, int H, Table tab, flo
                 const int t = 16 * w + 4 * g + m;
                 if (t < len)
 #pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct) o[((size_t)(t0 + t) * H + h) * D + col0 + 16 * ct + lr] = oacc[ct][m];
+                    for (int ct = 0; ct < NCT; ++ct)
+                        o[((size_t)(t0 + t) * H + h) * D + col0 + 16 * ct + lr] = __builtin_amdgcn_ldexpf(oacc[ct][m], -E);
             }
         }
     }
@@ -837,7 +968,8 @@ __global__ __launch_bounds__(256) void chain_kernel(int N, int H, Table tab, flo
             for (int u = 0; u < 2; ++u)
 #pragma unroll
                 for (int m = 0; m < 4; ++m)
-                    dst[(size_t)(32 * w + 16 * u + 4 * g + m) * D + col0 + 16 * ct + lr] = Sr[ct][u][m];
+                    dst[(size_t)(32 * w + 16 * u + 4 * g + m) * D + col0 + 16 * ct + lr] =
+                        __builtin_amdgcn_ldexpf(Sr[ct][u][m], -E);
     }
 }
 
@@ -904,7 +1036,7 @@ int launch_prefill(const void *q, const void *k, const void *v, bool f32io, cons
     tab.Mseg = (float *)(tab.blocks + (size_t)max_chunks(T_total, N) * (size_t)H * BLK_BYTES);
     tab.Bseg = tab.Mseg + st;
     tab.Sin = tab.Bseg + st;
-    // chain grids: 4 (state) or 8 (map) workgroups of 256 per (segment, head)
+    // chain grids: 4 (state or map) workgroups of 256 per (segment, head)
     // slot; a launch covers at most 2^32 - 1 work-items
     const int64_t slots8 = (nsm * H + 7) / 8;
     if (slots8 * 128 > (int64_t)(UINT32_MAX / 256) || max_chunks(T_total, N) * H > (int64_t)UINT32_MAX ||
@@ -921,13 +1053,13 @@ int launch_prefill(const void *q, const void *k, const void *v, bool f32io, cons
                            (const float *)q, (const float *)k, (const float *)v, z, beta, A, N, H, tab);
     }
     if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return -1;
-    hipLaunchKernelGGL(chain_kernel<true>, dim3((unsigned)(8 * (2 * D / NB) * slots8)), dim3(256), 0, stream, N, H,
-                       tab, o, S_final);
+    hipLaunchKernelGGL(chain_kernel<true>, dim3((unsigned)(8 * (2 * D / (16 * chain_nct<true>())) * slots8)),
+                       dim3(256), 0, stream, N, H, tab, o, S_final);
     if (ev && hipEventRecord(ev[3], stream) != hipSuccess) return -1;
     if (launch_seg_scan(S0, N, H, tab.sq, tab.Mseg, tab.Bseg, tab.Sin, S_final, stream) != 0) return -1;
     if (ev && hipEventRecord(ev[4], stream) != hipSuccess) return -1;
-    hipLaunchKernelGGL(chain_kernel<false>, dim3((unsigned)(8 * (D / NB) * slots8)), dim3(256), 0, stream, N, H,
-                       tab, o, S_final);
+    hipLaunchKernelGGL(chain_kernel<false>, dim3((unsigned)(8 * (D / (16 * chain_nct<false>())) * slots8)),
+                       dim3(256), 0, stream, N, H, tab, o, S_final);
     if (ly.gate && T_total > 0)
         hipLaunchKernelGGL(gated_rmsnorm_kernel, dim3((unsigned)((T_total * H + 3) / 4)), dim3(256), 0, stream, o,
                            ly.gate, ly.weight, ly.norm_eps, T_total * H);

@@ -57,15 +57,7 @@
 
 namespace kda {
 
-typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
-typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
-typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
-typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
 typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
 
 // Byte layout of the chain-operand block of one (chunk, head).
 constexpr int BO_W = 0;        // -W   A tiles (token tile rt 0..3, key block s 0..3), fp16, k = perm32(channel)
@@ -81,47 +73,13 @@ constexpr size_t BLK = 78848;  // multiple of 256
 __device__ __forceinline__ int aq_tile(int rt, int s) { return rt < 2 ? rt : 2 * rt - 2 + s; }
 __device__ __forceinline__ int frag(int tile, int lane) { return (tile * 64 + lane) * 16; }
 
-// Buffer resource word 3 for raw (untyped) buffer access on gfx9-family chips:
-// 32-bit data format, so accesses past num_records read 0 and drop writes.
-constexpr int BUF_RSRC3 = 0x00020000;
 __device__ __forceinline__ bf16x4 ld_bf16x4(__amdgpu_buffer_rsrc_t r, int off) {
     typedef __attribute__((ext_vector_type(2))) int i32x2;
     return __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }
 
-// fp16 hi/lo split of a pair of floats: hi = fp16(a), fp16(b), lo = fp16 of the
-// remainders.  a - fp32(hi) is exact in fp32, so one mixed-precision FMA per
-// element (fp16 hi and fp32 a as sources, fp16 result) gives the same lo as a
-// subtraction in fp32 followed by a conversion, in one instruction.
-typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
-typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
-__device__ __forceinline__ void split_f16_pair(float a, float b, uint32_t &hi, uint32_t &lo) {
-    const f16x2 h = {(_Float16)a, (_Float16)b};
-    hi = __builtin_bit_cast(uint32_t, h);
-    asm("v_fma_mixlo_f16 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]\n\t"
-        "v_fma_mixhi_f16 %0, -%1, 1.0, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
-        : "=&v"(lo)
-        : "v"(hi), "v"(a), "v"(b));
-}
-
 constexpr int PTT = 68;  // pitch (floats) of T [64][64]
 
-// Unsigned maximum over one DPP row (16 lanes with equal lane / 16), in every lane.
-__device__ __forceinline__ uint32_t row_umax16(uint32_t x) {
-    x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false));
-    x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false));
-    x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x141, 0xF, 0xF, false));
-    x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x140, 0xF, 0xF, false));
-    return x;
-}
-// Unsigned maximum over the whole wave, wave-uniform (so the compiler keeps it
-// in a scalar register and branches on it without divergence).
-__device__ __forceinline__ uint32_t wave_umax(uint32_t x) {
-    x = row_umax16(x);
-    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)x, 0), b = (uint32_t)__builtin_amdgcn_readlane((int)x, 16),
-                   c = (uint32_t)__builtin_amdgcn_readlane((int)x, 32), d = (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
-    return max(max(a, b), max(c, d));
-}
 // max |u| over a lane's four values as the bits of a non-negative float: as
 // unsigned integers these order like the values, and NaN orders above inf, so
 // a NaN is kept (fmaxf would drop it).

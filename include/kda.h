@@ -39,8 +39,10 @@
  *     accuracy for v and S0 of any magnitude whose states and outputs stay in
  *     fp32's normal range (tested from 2^-60 to 2^60 times unit scale).  That
  *     bound relies on the documented preconditions: unit-length keys and
- *     beta in [0, 1].  The fp32 path and the decode step compute in fp32
- *     throughout.
+ *     beta in [0, 1].  With fp32 q/k/v the chunk-local work is fp32 and the
+ *     chain's products take fp16 hi + lo pairs (22-bit operands, fp32
+ *     accumulation) under the same per-workgroup state scale and the same
+ *     preconditions.  The decode step computes in fp32 throughout.
  *   - z = -inf gives alpha = 1 exactly and z = +inf gives alpha = e^-5; both are
  *     valid.  NaN inputs propagate to the outputs.
  *   - Pointers must be 16-byte aligned (KDA_ERR_ALIGN otherwise).
