@@ -55,15 +55,22 @@ namespace kda {
 
 // ----------------------------------------------------------------- layout --
 
-// Per (chunk, head) block of chain operands in the workspace (bytes).  "hi/lo":
-// the array of fp16 hi values, then the array of fp16 lo values (n entries each).
-constexpr size_t OFF_W = 0;            // -W     [64][128]  hi/lo, n = 8192
+// Per (chunk, head) block of chain operands in the workspace (bytes).  The
+// MFMA A operands are stored as fp16 hi + lo tiles, fragment-major: the 16 B
+// of lane l = (lr, g) of tile i at 1024 i + 16 l, holding row 16 rt + lr and,
+// in slot e = 0..7, k index 32 s + 16 (e >> 2) + 4 g + (e & 3) of the tile's
+// k-step s.  Under that permutation of k a pair of C-layout tiles (rows
+// 16 (2 s) + 4 g + m and 16 (2 s + 1) + 4 g + m) is a B operand as it stands.
+// Each array of hi tiles is followed by the array of its lo tiles.
+constexpr size_t OFF_W = 0;            // -W     tile 4 rt + s (rt: tokens, s: channels), lo at +16 KB
 constexpr size_t OFF_U = 32768;        // U      [64][128]  fp32
-constexpr size_t OFF_KT = 65536;       // K~^T   [128][64]  hi/lo, n = 8192; K~ = K * e^{G_n - G}
-constexpr size_t OFF_QT = 98304;       // Q~     [64][128]  hi/lo, n = 8192; Q~ = Q * Gam
-constexpr size_t OFF_AQ = 131072;      // Aqk    [64][64]   hi/lo, n = 4096; zero above the diagonal
+constexpr size_t OFF_KT = 65536;       // K~^T   tile 2 rt + s (rt: channels, s: tokens), lo at +16 KB;
+                                       //        K~ = K * e^{G_n - G}
+constexpr size_t OFF_QT = 98304;       // Q~     as W, lo at +16 KB; Q~ = Q * Gam
+constexpr size_t OFF_AQ = 131072;      // Aqk    tile 2 rt + s (rows and k both tokens), lo at +8 KB;
+                                       //        zero above the diagonal
 constexpr size_t OFF_GM = 147456;      // gamma  [128]      fp32, e^{G_n}
-constexpr size_t NW_ = 8192, NAQ = 4096;  // entries of the [64][128] and [64][64] hi/lo arrays
+constexpr int LO_128 = 16384, LO_AQ = 8192;  // offsets of the lo tiles
 constexpr size_t BLK_BYTES = 147968;   // multiple of 256
 
 __host__ __device__ constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -254,13 +261,16 @@ __device__ __forceinline__ int pair_index(int i, int j) { return i * (i - 1) / 2
 __device__ __forceinline__ void st4(char *base, size_t e, float a, float b, float c, float d) {
     *(float4 *)((float *)base + e) = make_float4(a, b, c, d);
 }
-// the same into the hi/lo arrays at base (n entries each)
-__device__ __forceinline__ void st4h(char *base, size_t e, size_t n, float a, float b, float c, float d) {
+// Four values as fp16 hi + lo into slots 4 h .. 4 h + 3 of lane l of tile
+// `tile` of the hi tiles at base (the lo tiles lo bytes further)
+__device__ __forceinline__ void st_pair4(char *base, int lo, int tile, int l, int h, float a, float b, float c,
+                                         float d) {
     uint32_t h0, l0, h1, l1;
     split_f16_pair(a, b, h0, l0);
     split_f16_pair(c, d, h1, l1);
-    *(u32x2 *)((_Float16 *)base + e) = u32x2{h0, h1};
-    *(u32x2 *)((_Float16 *)base + n + e) = u32x2{l0, l1};
+    char *p = base + 1024 * tile + 16 * l + 8 * h;
+    *(u32x2 *)p = u32x2{h0, h1};
+    *(u32x2 *)(p + lo) = u32x2{l0, l1};
 }
 
 
@@ -421,31 +431,33 @@ __global__ __launch_bounds__(256) void intra_kernel(const float *__restrict__ q,
                 const float kv = ok ? kr[u] * sm.nk[t] : 0.f;
                 const float qv = ok ? qr[u] * sm.nq[t] : 0.f;
                 sm.KG[ch * PT + t] = kv * gam;
-                // Q~ pairs channels ch, ch ^ 1 (lanes l, l ^ 1): the even lane
-                // stores the pair's hi values, the odd lane its lo values
+                // Q~ pairs channels ch, ch ^ 1 (lanes l, l ^ 1, adjacent slots
+                // of one fragment lane): the even lane stores the pair's hi
+                // values, the odd lane its lo values
                 const float qg = qv * gam;
                 const float qo = __builtin_bit_cast(
                     float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, qg), 0xB1, 0xF, 0xF, false));
                 const bool odd = ch & 1;
                 uint32_t hi2, lo2;
                 split_f16_pair(odd ? qo : qg, odd ? qg : qo, hi2, lo2);
-                *(uint32_t *)((_Float16 *)qt + (odd ? NW_ : 0) + (size_t)t * D + (ch & ~1)) = odd ? lo2 : hi2;
+                const int qoff = 1024 * (4 * s + (ch >> 5)) + 16 * (u + 16 * ((ch >> 2) & 3)) +
+                                 2 * (4 * ((ch >> 4) & 1) + (ch & 2));
+                *(uint32_t *)(qt + (odd ? LO_128 : 0) + qoff) = odd ? lo2 : hi2;
                 kt_vals[u] = kv * __expf((float)(Gn - Gt));
             }
 #pragma unroll
             for (int u = 0; u < SUB; u += 4)
-                st4h(kt, (size_t)ch * CH + s * SUB + u, NW_, kt_vals[u], kt_vals[u + 1], kt_vals[u + 2],
-                     kt_vals[u + 3]);
+                st_pair4(kt, LO_128, 2 * (ch >> 4) + (s >> 1), (ch & 15) + 4 * u, s & 1, kt_vals[u], kt_vals[u + 1],
+                         kt_vals[u + 2], kt_vals[u + 3]);
         }
         if (half == 0) ((float *)(blk + OFF_GM))[ch] = __expf((float)Gn);
     }
-    // the six tiles of Aqk above the diagonal are zero
+    // the six 16 x 16 blocks (ti, tj > ti) of Aqk above the diagonal are zero
     for (int e = tid; e < 6 * 64; e += 256) {
-        const int tile = e >> 6, quad = e & 63;
-        const int ti = tile < 3 ? 0 : (tile < 5 ? 1 : 2);
-        const int tj = tile < 3 ? tile + 1 : (tile < 5 ? tile - 1 : 3);
-        const int r = 16 * ti + (quad >> 2), c0 = 16 * tj + 4 * (quad & 3);
-        st4h(blk + OFF_AQ, (size_t)r * CH + c0, NAQ, 0.f, 0.f, 0.f, 0.f);
+        const int blk6 = e >> 6, ln = e & 63;
+        const int ti = blk6 < 3 ? 0 : (blk6 < 5 ? 1 : 2);
+        const int tj = blk6 < 3 ? blk6 + 1 : (blk6 < 5 ? blk6 - 1 : 3);
+        st_pair4(blk + OFF_AQ, LO_AQ, 2 * ti + (tj >> 1), ln, tj & 1, 0.f, 0.f, 0.f, 0.f);
     }
     __syncthreads();
 
@@ -547,7 +559,7 @@ __global__ __launch_bounds__(256) void intra_kernel(const float *__restrict__ q,
         if (mat == 0) {
             if (it < 3) kkv[it] = f32x4{val[0], val[1], val[2], val[3]};
         } else {
-            st4h(blk + OFF_AQ, (size_t)rr * CH + cb, NAQ, val[0], val[1], val[2], val[3]);
+            st_pair4(blk + OFF_AQ, LO_AQ, 2 * i + (j >> 1), l, j & 1, val[0], val[1], val[2], val[3]);
         }
     }
     __syncthreads();  // E1 is dead: Akk takes its place
@@ -654,11 +666,10 @@ __global__ __launch_bounds__(256) void intra_kernel(const float *__restrict__ q,
                 acc = mma_ff(acc, xa, tb[ks]);
             }
             // acc[m] = out[row r][col 16 ct + 4 g + m]
-            const size_t e0 = (size_t)r * D + 16 * ct + 4 * g;
             if (pass == 0)
-                st4h(blk + OFF_W, e0, NW_, -acc[0], -acc[1], -acc[2], -acc[3]);
+                st_pair4(blk + OFF_W, LO_128, 4 * rt + (ct >> 1), l, ct & 1, -acc[0], -acc[1], -acc[2], -acc[3]);
             else
-                st4(blk + OFF_U, e0, acc[0], acc[1], acc[2], acc[3]);
+                st4(blk + OFF_U, (size_t)r * D + 16 * ct + 4 * g, acc[0], acc[1], acc[2], acc[3]);
         }
     }
 }
@@ -675,9 +686,13 @@ constexpr int PDH = 72;       // pitch (halves) of the Delta arrays
 
 template <int NB>
 struct ChainSmem {
-    // the state slice times 2^E as fp16 hi + lo, transposed [column][key row]
+    // the state slice times 2^E as fp16 hi + lo, transposed [column][key row],
+    // key rows in the operand tiles' k order (position 32 s + 8 g + e holds row
+    // 32 s + 16 (e >> 2) + 4 g + (e & 3)), so that a lane's 16 B at 32 s + 8 g are
+    // its B-operand slice of k-step s
     __attribute__((aligned(16))) _Float16 Sh[NB * PSH], Slo[NB * PSH];
-    // Delta times 2^E as fp16 hi + lo, transposed [column][token]
+    // Delta times 2^E as fp16 hi + lo, transposed [column][token], tokens in the
+    // same order
     __attribute__((aligned(16))) _Float16 Dh[NB * PDH], Dlo[NB * PDH];
     uint32_t ex[4];  // per wave: exponent bound of its state rows and U rows
 };
@@ -686,15 +701,15 @@ struct ChainSmem {
 struct H8 {
     f16x8 hi, lo;
 };
-// k slice at entry e of the hi/lo arrays at base (n entries each), 16-byte aligned
-__device__ __forceinline__ H8 ld_h8(const char *base, size_t e, size_t n) {
-    return {*(const f16x8 *)((const _Float16 *)base + e), *(const f16x8 *)((const _Float16 *)base + n + e)};
+// A lane's fragment at p (hi) and p + lo
+__device__ __forceinline__ H8 ld_frag(const char *p, int lo) {
+    return {*(const f16x8 *)p, *(const f16x8 *)(p + lo)};
 }
-// c + a b with a, b as hi + lo: the two cross terms, then hi * hi
-__device__ __forceinline__ f32x4 mma_hh(f32x4 c, const H8 &a, const H8 &b) {
-    c = mfma_f16(a.lo, b.hi, c);
-    c = mfma_f16(a.hi, b.lo, c);
-    return mfma_f16(a.hi, b.hi, c);
+// Term t of a b with a, b as hi + lo: t = 0: lo * hi, 1: hi * lo, 2: hi * hi.
+// The products below run term by term over several independent accumulators,
+// so that no MFMA waits for the result of the one issued just before it.
+__device__ __forceinline__ f32x4 mma_term(int t, f32x4 c, const H8 &a, const H8 &b) {
+    return mfma_f16(t == 0 ? a.lo : a.hi, t == 1 ? b.lo : b.hi, c);
 }
 __device__ __forceinline__ uint32_t abs_bits(float x) { return __builtin_bit_cast(uint32_t, x) & 0x7FFFFFFFu; }
 
@@ -762,15 +777,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
     // used it (the last chunk re-reads itself); the state pass, which has no
     // registers to spare for that, issues all of chunk c's loads at the top of
     // its step.
-    constexpr bool PF = MAP;
-    const int row = 16 * w + lr;
+    constexpr bool PF = true;
     H8 wf[4], qf[4], kf[2][2], af[2];
     float uv[NCT][4], gmv[2][4];
     auto load_w = [&](const char *blk) __attribute__((always_inline)) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            wf[ks] = ld_h8(blk + OFF_W, row * D + 32 * ks + 8 * g, NW_);
-            if constexpr (!MAP) qf[ks] = ld_h8(blk + OFF_QT, row * D + 32 * ks + 8 * g, NW_);
+            wf[ks] = ld_frag(blk + OFF_W + 1024 * (4 * w + ks) + 16 * l, LO_128);
+            if constexpr (!MAP) qf[ks] = ld_frag(blk + OFF_QT + 1024 * (4 * w + ks) + 16 * l, LO_128);
         }
     };
     // (the map's M columns read nothing: a buffer of no records reads 0)
@@ -789,13 +803,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
         for (int u = 0; u < 2; ++u) {
             const int kr = 32 * w + 16 * u;
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) kf[u][ks] = ld_h8(blk + OFF_KT, (kr + lr) * CH + 32 * ks + 8 * g, NW_);
+            for (int ks = 0; ks < 2; ++ks) kf[u][ks] = ld_frag(blk + OFF_KT + 1024 * (2 * (2 * w + u) + ks) + 16 * l, LO_128);
 #pragma unroll
             for (int m = 0; m < 4; ++m) gmv[u][m] = ((const float *)(blk + OFF_GM))[kr + 4 * g + m];
         }
         if constexpr (!MAP)
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) af[ks] = ld_h8(blk + OFF_AQ, row * CH + 32 * ks + 8 * g, NAQ);
+            for (int ks = 0; ks < 2; ++ks) af[ks] = ld_frag(blk + OFF_AQ + 1024 * (2 * w + ks) + 16 * l, LO_AQ);
     };
     auto block = [&](int cc) { return tab.blocks + ((size_t)cc * H + h) * BLK_BYTES; };
     // This wave's rows of the state slice, split, into the B-operand arrays.
@@ -809,7 +823,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
                 uint32_t h0, l0, h1, l1;
                 split_f16_pair(Sr[ct][u][0], Sr[ct][u][1], h0, l0);
                 split_f16_pair(Sr[ct][u][2], Sr[ct][u][3], h1, l1);
-                const int e0 = (16 * ct + lr) * PSH + 32 * w + 16 * u + 4 * g;
+                const int e0 = (16 * ct + lr) * PSH + 32 * w + 8 * g + 4 * u;  // key row 32 w + 16 u + 4 g + m
                 *(u32x2 *)&sm.Sh[e0] = u32x2{h0, h1};
                 *(u32x2 *)&sm.Slo[e0] = u32x2{l0, l1};
             }
@@ -878,13 +892,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
         load_u(nblk);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
+            H8 sb[NCT];
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
                 const int e0 = (16 * ct + lr) * PSH + 32 * ks + 8 * g;
-                const H8 sb = {*(const f16x8 *)&sm.Sh[e0], *(const f16x8 *)&sm.Slo[e0]};
-                ws[ct] = mma_hh(ws[ct], wf[ks], sb);
-                if constexpr (!MAP) oacc[ct] = mma_hh(oacc[ct], qf[ks], sb);
+                sb[ct] = {*(const f16x8 *)&sm.Sh[e0], *(const f16x8 *)&sm.Slo[e0]};
             }
+#pragma unroll
+            for (int t = 0; t < 3; ++t)
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) {
+                    ws[ct] = mma_term(t, ws[ct], wf[ks], sb[ct]);
+                    if constexpr (!MAP) oacc[ct] = mma_term(t, oacc[ct], qf[ks], sb[ct]);
+                }
         }
         if (PF) load_w(nblk);
         // (3) publish Delta as the B operand of Aqk Delta and K~^T Delta
@@ -893,7 +913,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
             uint32_t h0, l0, h1, l1;
             split_f16_pair(ws[ct][0], ws[ct][1], h0, l0);
             split_f16_pair(ws[ct][2], ws[ct][3], h1, l1);
-            const int e0 = (16 * ct + lr) * PDH + 16 * w + 4 * g;
+            const int e0 = (16 * ct + lr) * PDH + 32 * (w >> 1) + 8 * g + 4 * (w & 1);  // token 16 w + 4 g + m
             *(u32x2 *)&sm.Dh[e0] = u32x2{h0, h1};
             *(u32x2 *)&sm.Dlo[e0] = u32x2{l0, l1};
         }
@@ -906,28 +926,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
                 const int e0 = (16 * ct + lr) * PDH + 32 * ks + 8 * g;
                 dF[ct][ks] = {*(const f16x8 *)&sm.Dh[e0], *(const f16x8 *)&sm.Dlo[e0]};
             }
-        // (4) O += Aqk Delta  (row tile w; Aqk is zero above the diagonal)
-        if constexpr (!MAP)
+        // (4) S <- Diag(gamma) S + K~^T Delta  (key rows [32w, 32w+32)), and
+        // (5) O += Aqk Delta  (row tile w; Aqk is zero above the diagonal)
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-                if (ks < nks_aq)
-#pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct) oacc[ct] = mma_hh(oacc[ct], af[ks], dF[ct][ks]);
-        // (5) S <- Diag(gamma) S + K~^T Delta  (key rows [32w, 32w+32))
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            f32x4 acc[NCT];
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-                for (int m = 0; m < 4; ++m) acc[ct][m] = gmv[u][m] * Sr[ct][u][m];
+                for (int m = 0; m < 4; ++m) Sr[ct][u][m] *= gmv[u][m];
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
+        for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) acc[ct] = mma_hh(acc[ct], kf[u][ks], dF[ct][ks]);
+            for (int t = 0; t < 3; ++t) {
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) Sr[ct][u] = acc[ct];
-        }
+                for (int u = 0; u < 2; ++u)
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct) Sr[ct][u] = mma_term(t, Sr[ct][u], kf[u][ks], dF[ct][ks]);
+                if constexpr (!MAP)
+                    if (ks < nks_aq)
+#pragma unroll
+                        for (int ct = 0; ct < NCT; ++ct) oacc[ct] = mma_term(t, oacc[ct], af[ks], dF[ct][ks]);
+            }
         if (PF) load_ka(nblk);
         if constexpr (!MAP) {
             // (5b) snapshot after a full chunk that ends a stride

@@ -74,7 +74,6 @@ __device__ __forceinline__ int aq_tile(int rt, int s) { return rt < 2 ? rt : 2 *
 __device__ __forceinline__ int frag(int tile, int lane) { return (tile * 64 + lane) * 16; }
 
 __device__ __forceinline__ bf16x4 ld_bf16x4(__amdgpu_buffer_rsrc_t r, int off) {
-    typedef __attribute__((ext_vector_type(2))) int i32x2;
     return __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }
 
