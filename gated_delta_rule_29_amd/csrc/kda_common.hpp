@@ -188,6 +188,8 @@ __device__ __forceinline__ uint32_t wave_umax(uint32_t x) {
 // Buffer resource word 3 for raw (untyped) buffer access on gfx9-family chips:
 // 32-bit data format, so accesses past num_records read 0 and drop writes.
 constexpr int BUF_RSRC3 = 0x00020000;
+typedef __attribute__((address_space(3))) void lds_void;
+
 // Eight fp32 values of one lane's 32-deep k slice.
 struct F8 {
     float v[8];

@@ -27,15 +27,15 @@
 //                 gate + sub-chunk cumsums, the two Gram tiles on MFMA, the
 //                 blocked forward substitution, W and U on MFMA; writes the
 //                 per-chunk operands of the chain to the workspace;
-//   chain_kernel<true>   the affine map S -> M S + B of every segment but a
-//                 sequence's last, one workgroup per (segment, head, 64 of
-//                 the 256 columns of [M | B]);
+//   map_kernel    the affine map S -> M S + B of every segment but a
+//                 sequence's last, one workgroup of eight waves per
+//                 (segment, head), the chunk's operand tiles copied into LDS;
 //   seg_scan_kernel (kda_segment.hip)  the state entering each segment;
-//   chain_kernel<false>  one workgroup per (segment, head, 32 value columns):
-//                 keeps its 128 x 32 fp32 state slice in registers across the
-//                 segment's chunks and forms Delta, the output and the next
-//                 state with MFMA.
-//   (The scan and the layer's output step as in the bf16 path.)
+//   chain_kernel  the state pass, one workgroup per (segment, head, 32 value
+//                 columns): keeps its 128 x 32 fp32 state slice in registers
+//                 across the segment's chunks and forms Delta, the output and
+//                 the next state with MFMA;
+//   gated_rmsnorm_kernel  (with the layer's output step) in place on o.
 //
 // This file serves fp32 q/k/v (bf16 q/k/v take kda_segment.hip's path).
 // intra_kernel computes in fp32 with exact fp32 MFMA products.  The chain
@@ -102,14 +102,18 @@ __host__ inline Table carve(void *ws, int N) {
     return t;
 }
 __host__ inline int64_t max_chunks(int64_t T_total, int N) { return (T_total + CH - 1) / CH + N; }
-// Segments of the chain: about SEG32_TARGET (segment, head) pairs in all, so
-// that the chain passes have over a thousand workgroups (8 and 16 per pair).
-// Their time at 64K x 16 is the same from 128 to 1,024 pairs (they are bound
-// by throughput, not by the length of the chain); fewer pairs shorten the scan.
-constexpr int SEG32_TARGET = 128;
+// Segments of the chain: about SEG32_TARGET (segment, head) pairs in all.  The
+// map pass runs one workgroup (133 KB of LDS, one per CU) per pair with a
+// successor: at 64K x 16, 240 of them fill the chip once (0.39 ms; with 128
+// pairs, 112 workgroups took 0.70 ms).  The state pass (four workgroups per
+// pair) took the same time from 128 to 1,024 pairs; fewer pairs shorten the scan.
+constexpr int SEG32_TARGET = 256;
+// The segment length is even: the map pass runs its chain two steps per loop
+// iteration (one per LDS image).
 __host__ inline int seg32_len(int64_t T_total, int N, int H) {
     const int64_t per_head = SEG32_TARGET / (H > 0 ? H : 1) > 0 ? SEG32_TARGET / H : 1;
-    return (int)((max_chunks(T_total, N) + per_head - 1) / per_head);
+    const int L = (int)((max_chunks(T_total, N) + per_head - 1) / per_head);
+    return (L + 1) / 2 * 2;
 }
 __host__ inline int64_t seg32_max(int64_t T_total, int N, int H) {
     const int L = seg32_len(T_total, N, H);
@@ -676,15 +680,11 @@ __global__ __launch_bounds__(256) void intra_kernel(const float *__restrict__ q,
 
 // ----------------------------------------------------------------- chain --
 
-// 16-column tiles per workgroup: the map pass takes 64 of its 256 columns
-// (with 32, its 896 workgroups at 64K x 16 ran in two rounds: 1.05 against
-// 0.70 ms), the state pass 32 (its registers allow no more).
-template <bool MAP>
-constexpr int chain_nct() { return MAP ? 4 : 2; }
+constexpr int NCT = 2;         // 16-column tiles per state-pass workgroup (its registers allow no more)
+constexpr int NB = 16 * NCT;  // state columns per workgroup
 constexpr int PSH = 136;      // pitch (halves) of the state arrays
 constexpr int PDH = 72;       // pitch (halves) of the Delta arrays
 
-template <int NB>
 struct ChainSmem {
     // the state slice times 2^E as fp16 hi + lo, transposed [column][key row],
     // key rows in the operand tiles' k order (position 32 s + 8 g + e holds row
@@ -713,14 +713,11 @@ __device__ __forceinline__ f32x4 mma_term(int t, f32x4 c, const H8 &a, const H8 
 }
 __device__ __forceinline__ uint32_t abs_bits(float x) { return __builtin_bit_cast(uint32_t, x) & 0x7FFFFFFFu; }
 
-// The chain over one segment of a sequence, 16 NCT state columns per
-// workgroup (each operand fragment loaded serves all NCT column tiles),
-// products as fp16 hi + lo pairs.  The segment map carries a state S entering the segment
-// to M S + B; MAP = true computes the columns of X = [M | B] (128 x 256) by
-// running the chain step from X = [I | 0], with U entering only the B columns;
-// MAP = false runs it from the state the scan gave the segment and writes o
-// (and snapshots, and S_final after a sequence's last segment).  Workgroups
-// are numbered so that the column blocks of one (segment, head) share an XCD
+// The state pass: the chain over one segment of a sequence from the state the
+// scan gave it, 32 state columns per workgroup (each operand fragment loaded
+// serves both 16-column tiles), products as fp16 hi + lo pairs; writes o (and
+// snapshots, and S_final after a sequence's last segment).  Workgroups are
+// numbered so that the four column blocks of one (segment, head) share an XCD
 // (and its L2, which serves their common operand block), and the (segment,
 // head) pairs with work come first.
 //
@@ -730,23 +727,19 @@ __device__ __forceinline__ uint32_t abs_bits(float x) { return __builtin_bit_cas
 // [2^7, 2^11).  Then |Delta| = |U - W S| < 2^11 (1 + sqrt(128)) < 2^15 (each
 // row of W has norm <= 1 with unit keys and beta in [0, 1]), inside fp16's
 // range, and values 2^-10 below the largest keep all 22 bits of the pair.
-template <bool MAP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void chain_kernel(int N, int H, Table tab, float *__restrict__ o,
-                                                    float *__restrict__ S_final) {
-    constexpr int NCT = chain_nct<MAP>(), NB = 16 * NCT;  // state columns per workgroup
-    __shared__ ChainSmem<NB> sm;
-    constexpr int NCB = (MAP ? 2 * D : D) / NB;  // column blocks per (segment, head)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void chain_kernel(
+    int N, int H, Table tab, float *__restrict__ o, float *__restrict__ S_final) {
+    __shared__ ChainSmem sm;
+    constexpr int NCB = D / NB;  // column blocks per (segment, head)
     const int Lw = blockIdx.x;
     const int p = (Lw & 7) + 8 * (Lw / (8 * NCB)), cb = (Lw >> 3) % NCB;
     const int a = p / H, h = p % H;
-    if (a >= (MAP ? tab.sq.segA0(N) : tab.sq.seg0(N))) return;
-    const int n = MAP ? tab.sq.seq_of_segA(a, N) : tab.sq.seq_of_seg(a, N);
-    const int j = a - (MAP ? tab.sq.segA0(n) : tab.sq.seg0(n));
-    const int x = tab.sq.seg0(n) + j;  // segment index of the maps and states
+    if (a >= tab.sq.seg0(N)) return;
+    const int n = tab.sq.seq_of_seg(a, N);
+    const int j = a - tab.sq.seg0(n);
+    const int x = tab.sq.seg0(n) + j;  // segment index of the states
     const int pn = tab.sq.seg0(n + 1) - tab.sq.seg0(n);
-    const bool bcol = MAP && cb >= NCB / 2;              // columns of B (U enters)
-    const bool use_u = !MAP || bcol;
-    const int col0 = NB * (MAP ? cb % (NCB / 2) : cb);  // first column within M, B or the state
+    const int col0 = NB * cb;  // first column of the workgroup
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, lr = l & 15;
 
     // state slice: wave w owns key rows [32w, 32w+32) as two 16-row tiles (C
@@ -760,7 +753,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const int r = 32 * w + 16 * u + 4 * g + m, cc = col0 + 16 * ct + lr;
-                Sr[ct][u][m] = MAP ? (!bcol && r == cc ? 1.f : 0.f) : tab.Sin[sblk + (size_t)r * D + cc];
+                Sr[ct][u][m] = tab.Sin[sblk + (size_t)r * D + cc];
             }
     int E = 0;
 
@@ -772,25 +765,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
 
     // Operands of one chunk, in registers.  The barriers wait only for LDS
     // traffic, so loads stay in flight across them.  U is loaded one chunk
-    // ahead (its largest value sets the step's scale before the first barrier).
-    // The map pass loads each other group for chunk c + 1 as soon as chunk c has
-    // used it (the last chunk re-reads itself); the state pass, which has no
-    // registers to spare for that, issues all of chunk c's loads at the top of
-    // its step.
-    constexpr bool PF = true;
+    // ahead (its largest value sets the step's scale before the first
+    // barrier); each other group for chunk c + 1 as soon as chunk c has used it
+    // (the last chunk re-reads itself).
     H8 wf[4], qf[4], kf[2][2], af[2];
     float uv[NCT][4], gmv[2][4];
     auto load_w = [&](const char *blk) __attribute__((always_inline)) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             wf[ks] = ld_frag(blk + OFF_W + 1024 * (4 * w + ks) + 16 * l, LO_128);
-            if constexpr (!MAP) qf[ks] = ld_frag(blk + OFF_QT + 1024 * (4 * w + ks) + 16 * l, LO_128);
+            qf[ks] = ld_frag(blk + OFF_QT + 1024 * (4 * w + ks) + 16 * l, LO_128);
         }
     };
-    // (the map's M columns read nothing: a buffer of no records reads 0)
     auto load_u = [&](const char *blk) __attribute__((always_inline)) {
         const __amdgpu_buffer_rsrc_t ru = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(blk + OFF_U + 4 * (16 * w * D + col0)), 0, use_u ? 16 * D * 4 : 0, BUF_RSRC3);
+            (void *)(blk + OFF_U + 4 * (16 * w * D + col0)), 0, 16 * D * 4, BUF_RSRC3);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
@@ -807,9 +796,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
 #pragma unroll
             for (int m = 0; m < 4; ++m) gmv[u][m] = ((const float *)(blk + OFF_GM))[kr + 4 * g + m];
         }
-        if constexpr (!MAP)
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) af[ks] = ld_frag(blk + OFF_AQ + 1024 * (2 * w + ks) + 16 * l, LO_AQ);
+        for (int ks = 0; ks < 2; ++ks) af[ks] = ld_frag(blk + OFF_AQ + 1024 * (2 * w + ks) + 16 * l, LO_AQ);
     };
     auto block = [&](int cc) { return tab.blocks + ((size_t)cc * H + h) * BLK_BYTES; };
     // This wave's rows of the state slice, split, into the B-operand arrays.
@@ -830,18 +818,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
     };
     if (cbeg < cend) {
         load_u(block(cbeg));
-        if (PF) {
-            load_w(block(cbeg));
-            load_ka(block(cbeg));
-        }
+        load_w(block(cbeg));
+        load_ka(block(cbeg));
     }
 
     for (int c = cbeg; c < cend; ++c) {
         const char *nblk = block(min(c + 1, cend - 1));
-        if (!PF) {
-            load_w(block(c));
-            load_ka(block(c));
-        }
         const int64_t t0 = sstart + (int64_t)(c - cseq) * CH;
         const int len = (int)min((int64_t)CH, send - t0);
 
@@ -903,10 +885,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct) {
                     ws[ct] = mma_term(t, ws[ct], wf[ks], sb[ct]);
-                    if constexpr (!MAP) oacc[ct] = mma_term(t, oacc[ct], qf[ks], sb[ct]);
+                    oacc[ct] = mma_term(t, oacc[ct], qf[ks], sb[ct]);
                 }
         }
-        if (PF) load_w(nblk);
+        load_w(nblk);
         // (3) publish Delta as the B operand of Aqk Delta and K~^T Delta
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
@@ -942,45 +924,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
                 for (int u = 0; u < 2; ++u)
 #pragma unroll
                     for (int ct = 0; ct < NCT; ++ct) Sr[ct][u] = mma_term(t, Sr[ct][u], kf[u][ks], dF[ct][ks]);
-                if constexpr (!MAP)
-                    if (ks < nks_aq)
+                if (ks < nks_aq)
 #pragma unroll
-                        for (int ct = 0; ct < NCT; ++ct) oacc[ct] = mma_term(t, oacc[ct], af[ks], dF[ct][ks]);
+                    for (int ct = 0; ct < NCT; ++ct) oacc[ct] = mma_term(t, oacc[ct], af[ks], dF[ct][ks]);
             }
-        if (PF) load_ka(nblk);
-        if constexpr (!MAP) {
-            // (5b) snapshot after a full chunk that ends a stride
-            if (tab.ck.S && len == CH && (c - cseq + 1) % tab.ck.stride_chunks == 0) {
-                const int64_t slot = ck_base + (c - cseq + 1) / tab.ck.stride_chunks - 1;
-                if (slot < tab.ck.cap) {
-                    float *dst = tab.ck.S + ((size_t)slot * H + h) * D * D;
+        load_ka(nblk);
+        // (5b) snapshot after a full chunk that ends a stride
+        if (tab.ck.S && len == CH && (c - cseq + 1) % tab.ck.stride_chunks == 0) {
+            const int64_t slot = ck_base + (c - cseq + 1) / tab.ck.stride_chunks - 1;
+            if (slot < tab.ck.cap) {
+                float *dst = tab.ck.S + ((size_t)slot * H + h) * D * D;
 #pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct)
+                for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-                        for (int u = 0; u < 2; ++u)
+                    for (int u = 0; u < 2; ++u)
 #pragma unroll
-                            for (int m = 0; m < 4; ++m)
-                                dst[(size_t)(32 * w + 16 * u + 4 * g + m) * D + col0 + 16 * ct + lr] =
-                                    __builtin_amdgcn_ldexpf(Sr[ct][u][m], -E);
-                }
-            }
-            // (6) output rows of this chunk
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int t = 16 * w + 4 * g + m;
-                if (t < len)
-#pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct)
-                        o[((size_t)(t0 + t) * H + h) * D + col0 + 16 * ct + lr] = __builtin_amdgcn_ldexpf(oacc[ct][m], -E);
+                        for (int m = 0; m < 4; ++m)
+                            dst[(size_t)(32 * w + 16 * u + 4 * g + m) * D + col0 + 16 * ct + lr] =
+                                __builtin_amdgcn_ldexpf(Sr[ct][u][m], -E);
             }
         }
+        // (6) output rows of this chunk
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int t = 16 * w + 4 * g + m;
+            if (t < len)
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct)
+                    o[((size_t)(t0 + t) * H + h) * D + col0 + 16 * ct + lr] = __builtin_amdgcn_ldexpf(oacc[ct][m], -E);
+        }
     }
-    float *dst = nullptr;
-    if (MAP)
-        dst = (bcol ? tab.Bseg : tab.Mseg) + sblk;
-    else if (S_final && j == pn - 1)
-        dst = S_final + ((size_t)n * H + h) * D * D;
-    if (dst) {
+    if (S_final && j == pn - 1) {
+        float *dst = S_final + ((size_t)n * H + h) * D * D;
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
@@ -990,6 +965,209 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
                     dst[(size_t)(32 * w + 16 * u + 4 * g + m) * D + col0 + 16 * ct + lr] =
                         __builtin_amdgcn_ldexpf(Sr[ct][u][m], -E);
     }
+}
+
+// ------------------------------------------------------------- map pass --
+
+// LDS image of one chunk for the map pass, copied straight from its block: the
+// -W tiles (hi, then lo), the K~^T tiles (hi, then lo) and gamma.
+constexpr int MI_W = 0, MI_KT = 32768, MI_GM = 65536, MI_BYTES = MI_GM + 1024;
+
+// Copy the image of the chunk whose block is blk into img: 64 tiles of 1 KB,
+// eight per wave (buffer_load_dwordx4 ... lds: lane l lands at dst + 16 l),
+// and gamma by every wave (the same values; lanes 32-63 read past the block,
+// which gives zeros, into padding).  Completion is awaited with vmcnt.
+__device__ __forceinline__ void map_dma(const char *__restrict__ blk, char *img, int wv, int l) {
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void *)blk, 0, (int)BLK_BYTES, BUF_RSRC3);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int x = wv + 8 * i;
+        const int src = x < 32 ? (int)OFF_W + 1024 * x : (int)OFF_KT + 1024 * (x - 32);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(img + 1024 * x), 16, src + 16 * l, 0, 0, 0);
+    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(img + MI_GM), 16, (int)OFF_GM + 16 * l, 0, 0, 0);
+}
+
+// The affine map S -> M S + B of a segment (every segment of a sequence but its
+// last), one workgroup of eight waves per (segment, head): from X = [M | B] =
+// [I | 0] it runs the chain step X <- Diag(gamma) X + K~^T (U~ - W X) over the
+// segment's chunks, where U~ is U in the B columns and 0 in the M columns.
+// Wave w owns the 32 columns 32 w .. 32 w + 31 of X (waves 0-3: M, 4-7: B) as
+// C-layout tiles, all 128 rows, and feeds them as the B operand of W X by the
+// tile pairing of the block's k order; Delta likewise for K~^T Delta.  The
+// chunk's -W and K~^T tiles are copied into one of two LDS images a step
+// ahead, so each is read from memory once per workgroup; U (fp32) is loaded a
+// step ahead into registers.  Products as fp16 hi + lo pairs (three MFMAs),
+// with X and U at a power-of-two scale 2^E per wave (re-picked when the largest
+// |X| or |U| 2^E leaves [2^7, 2^11), as in the state pass).
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void map_kernel(int N, int H,
+                                                                                             Table tab) {
+    __shared__ __align__(16) char img0[MI_BYTES];
+    __shared__ __align__(16) char img1[MI_BYTES];
+    // workgroup i: head i mod H of the (i / H)-th segment with a successor
+    const int a = (int)blockIdx.x / H, h = (int)blockIdx.x % H;
+    if (a >= tab.sq.segA0(N)) return;
+    const int n = tab.sq.seq_of_segA(a, N);
+    const int j = a - tab.sq.segA0(n);
+    const int x = tab.sq.seg0(n) + j;  // segment index of the maps
+    const int cbeg = tab.sq.chunk0(n) + j * tab.sq.L, cend = cbeg + tab.sq.L;  // a full segment: L chunks
+    const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, g = l >> 4,
+              lr = l & 15;
+    const bool bcol = wv >= 4;
+    const int colw = 32 * (wv & 3);  // first column of the wave within M or B
+    auto block = [&](int c) { return tab.blocks + ((size_t)c * H + h) * BLK_BYTES; };
+
+    f32x4 X[8][2];
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) X[rt][ct][m] = !bcol && 16 * rt + 4 * g + m == colw + 16 * ct + lr ? 1.f : 0.f;
+    int E = 0;
+
+    // U of a chunk (B waves; a buffer of no records reads 0 for the M waves and
+    // past the segment): tile (rt, ct) rows 16 rt + 4 g + m, columns colw + 16 ct + lr
+    f32x4 uv[4][2];
+    auto load_u = [&](int c) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t ru = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(block(c) + OFF_U), 0, bcol && c < cend ? 64 * D * 4 : 0, BUF_RSRC3);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    uv[rt][ct][m] = __builtin_bit_cast(
+                        float, __builtin_amdgcn_raw_buffer_load_b32(ru, 4 * ((4 * g + m) * D + lr),
+                                                                    4 * (16 * rt * D + colw + 16 * ct), 0));
+    };
+    map_dma(block(cbeg), img0, wv, l);
+    load_u(cbeg);
+
+    auto step = [&](int c, const char *cur, char *nxt) __attribute__((always_inline)) {
+        // This wave's copies of `cur` and its U have landed, then every wave's
+        // have, and every wave is done with `nxt` (read in the step before).
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        __asm__ volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        __asm__ volatile("" ::: "memory");
+        if (c + 1 < cend) map_dma(block(c + 1), nxt, wv, l);
+        // The step's scale: e bounds max(|X|, |U| 2^E) by 2^(e - 126) (fp32
+        // exponent fields).  Inf or NaN present: keep E.
+        {
+            uint32_t mx = 0, mu = 0;
+#pragma unroll
+            for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        mx = max(mx, abs_bits(X[rt][ct][m]));
+                        if (rt < 4) mu = max(mu, abs_bits(uv[rt][ct][m]));
+                    }
+            const int es = (int)(mx >> 23), eu = (int)(mu >> 23);
+            const int el = (es == 255 || eu == 255) ? 0xFFFF : max(es, eu ? max(eu + E, 0) : 0);
+            const int e = (int)wave_umax((uint32_t)el);
+            if (e != 0xFFFF && e != 0 && (e < 134 || e > 137)) {
+                const int sh = 136 - e;
+                E += sh;
+#pragma unroll
+                for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+                    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                        for (int m = 0; m < 4; ++m) X[rt][ct][m] = __builtin_amdgcn_ldexpf(X[rt][ct][m], sh);
+            }
+        }
+        // Delta = U 2^E - W X (W stored negated, the accumulator starts at U 2^E)
+        f32x4 Dl[4][2];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) Dl[rt][ct][m] = __builtin_amdgcn_ldexpf(uv[rt][ct][m], E);
+        load_u(c + 1);
+        const char *lane = cur + 16 * l;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            H8 xb[2];  // X rows 32 s .. 32 s + 31 as the B operand: C tiles 2 s and 2 s + 1
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                uint32_t hw[4], lw[4];
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const f32x4 &xv = X[2 * s + (p >> 1)][ct];
+                    split_f16_pair(xv[2 * (p & 1)], xv[2 * (p & 1) + 1], hw[p], lw[p]);
+                }
+                xb[ct] = {__builtin_bit_cast(f16x8, u32x4{hw[0], hw[1], hw[2], hw[3]}),
+                          __builtin_bit_cast(f16x8, u32x4{lw[0], lw[1], lw[2], lw[3]})};
+            }
+#pragma unroll
+            for (int r2 = 0; r2 < 4; r2 += 2) {
+                H8 wa[2];
+#pragma unroll
+                for (int q = 0; q < 2; ++q) wa[q] = ld_frag(lane + MI_W + 1024 * (4 * (r2 + q) + s), LO_128);
+#pragma unroll
+                for (int t = 0; t < 3; ++t)
+#pragma unroll
+                    for (int q = 0; q < 2; ++q)
+#pragma unroll
+                        for (int ct = 0; ct < 2; ++ct) Dl[r2 + q][ct] = mma_term(t, Dl[r2 + q][ct], wa[q], xb[ct]);
+            }
+        }
+        // Delta as the B operand (tokens 32 s .. 32 s + 31: C tiles 2 s, 2 s + 1)
+        H8 db[2][2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                uint32_t hw[4], lw[4];
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const f32x4 &dv = Dl[2 * s + (p >> 1)][ct];
+                    split_f16_pair(dv[2 * (p & 1)], dv[2 * (p & 1) + 1], hw[p], lw[p]);
+                }
+                db[s][ct] = {__builtin_bit_cast(f16x8, u32x4{hw[0], hw[1], hw[2], hw[3]}),
+                             __builtin_bit_cast(f16x8, u32x4{lw[0], lw[1], lw[2], lw[3]})};
+            }
+        // X <- Diag(gamma) X + K~^T Delta
+#pragma unroll
+        for (int rt = 0; rt < 8; ++rt) {
+            const f32x4 gm = *(const f32x4 *)(cur + MI_GM + 64 * rt + 16 * g);  // gamma of rows 16 rt + 4 g + m
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) X[rt][ct][m] *= gm[m];
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int r2 = 0; r2 < 8; r2 += 2) {
+                H8 ka[2];
+#pragma unroll
+                for (int q = 0; q < 2; ++q) ka[q] = ld_frag(lane + MI_KT + 1024 * (2 * (r2 + q) + s), LO_128);
+#pragma unroll
+                for (int t = 0; t < 3; ++t)
+#pragma unroll
+                    for (int q = 0; q < 2; ++q)
+#pragma unroll
+                        for (int ct = 0; ct < 2; ++ct) X[r2 + q][ct] = mma_term(t, X[r2 + q][ct], ka[q], db[s][ct]);
+            }
+    };
+    for (int c = cbeg; c < cend; c += 2) {
+        step(c, img0, img1);
+        step(c + 1, img1, img0);
+    }
+    float *dst = (bcol ? tab.Bseg : tab.Mseg) + ((size_t)x * H + h) * D * D + colw;
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                dst[(size_t)(16 * rt + 4 * g + m) * D + 16 * ct + lr] = __builtin_amdgcn_ldexpf(X[rt][ct][m], -E);
 }
 
 // ------------------------------------------------------------ output step --
@@ -1055,8 +1233,8 @@ int launch_prefill(const void *q, const void *k, const void *v, bool f32io, cons
     tab.Mseg = (float *)(tab.blocks + (size_t)max_chunks(T_total, N) * (size_t)H * BLK_BYTES);
     tab.Bseg = tab.Mseg + st;
     tab.Sin = tab.Bseg + st;
-    // chain grids: 4 (state or map) workgroups of 256 per (segment, head)
-    // slot; a launch covers at most 2^32 - 1 work-items
+    // grids: the state pass 4 workgroups of 256 per (segment, head) slot, the
+    // map pass one of 512; a launch covers at most 2^32 - 1 work-items
     const int64_t slots8 = (nsm * H + 7) / 8;
     if (slots8 * 128 > (int64_t)(UINT32_MAX / 256) || max_chunks(T_total, N) * H > (int64_t)UINT32_MAX ||
         (int64_t)CH * H * D > (int64_t)INT32_MAX)
@@ -1072,13 +1250,12 @@ int launch_prefill(const void *q, const void *k, const void *v, bool f32io, cons
                            (const float *)q, (const float *)k, (const float *)v, z, beta, A, N, H, tab);
     }
     if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return -1;
-    hipLaunchKernelGGL(chain_kernel<true>, dim3((unsigned)(8 * (2 * D / (16 * chain_nct<true>())) * slots8)),
-                       dim3(256), 0, stream, N, H, tab, o, S_final);
+    hipLaunchKernelGGL(map_kernel, dim3((unsigned)(nsm * H)), dim3(512), 0, stream, N, H, tab);
     if (ev && hipEventRecord(ev[3], stream) != hipSuccess) return -1;
     if (launch_seg_scan(S0, N, H, tab.sq, tab.Mseg, tab.Bseg, tab.Sin, S_final, stream) != 0) return -1;
     if (ev && hipEventRecord(ev[4], stream) != hipSuccess) return -1;
-    hipLaunchKernelGGL(chain_kernel<false>, dim3((unsigned)(8 * (D / (16 * chain_nct<false>())) * slots8)),
-                       dim3(256), 0, stream, N, H, tab, o, S_final);
+    hipLaunchKernelGGL(chain_kernel, dim3((unsigned)(8 * (D / NB) * slots8)), dim3(256), 0, stream, N, H, tab, o,
+                       S_final);
     if (ly.gate && T_total > 0)
         hipLaunchKernelGGL(gated_rmsnorm_kernel, dim3((unsigned)((T_total * H + 3) / 4)), dim3(256), 0, stream, o,
                            ly.gate, ly.weight, ly.norm_eps, T_total * H);

@@ -57,7 +57,6 @@
 
 namespace kda {
 
-typedef __attribute__((address_space(3))) void lds_void;
 
 // Byte layout of the chain-operand block of one (chunk, head).
 constexpr int BO_W = 0;        // -W   A tiles (token tile rt 0..3, key block s 0..3), fp16, k = perm32(channel)

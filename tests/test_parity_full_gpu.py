@@ -9,7 +9,8 @@
   tokens of the long sequence from the state the GPU reaches before them (a second call over the
   first 1,044,480 tokens), plus the other three sequences in full.
 
-Bar: max|d| / RMS(ref) <= 1e-2 for o and S_final (bf16 q/k/v).
+Bar: max|d| / RMS(ref) <= 1e-2 for o and S_final (bf16 q/k/v); the 64K prefill also with fp32
+q/k/v at 1e-4 (the fp32 build's segment count and chain length at that size).
 """
 import numpy as np
 import pytest
@@ -46,6 +47,27 @@ def test_prefill_64k_full():
     eh = max(err(o[:, h], o_ref[:, h]) for h in range(H))
     say(f"  prefill_64k err_o={eo:.3e} err_S={es:.3e} worst-head err_o={eh:.3e}")
     assert eo <= TOL and es <= TOL and eh <= TOL
+
+
+@pytest.mark.timeout(300)
+def test_prefill_64k_full_fp32():
+    w = synth.WORKLOADS["prefill_64k"]
+    T, H = w["lens"][0], w["H"]
+    say(f"case prefill_64k fp32 T={T} H={H}: generating")
+    d = synth.prefill_inputs(w["seed"], T, H, dtype="f32", z_scale=w["z_scale"], s0_std=w["s0_std"])
+    q, k, v = (to_dev(d[n], torch.float32) for n in ("q", "k", "v"))
+    say("case prefill_64k fp32: GPU call")
+    o, Sf = kda.kda_chunk_fwd(q, k, v, to_dev(d["z"], torch.float32), to_dev(d["beta"], torch.float32),
+                              to_dev(d["A"], torch.float32), to_dev(d["S0"], torch.float32))
+    torch.cuda.synchronize()
+    o, Sf = o.cpu().numpy(), Sf.cpu().numpy()
+    say("case prefill_64k fp32: oracle")
+    o_ref, S_ref = oracle.recurrent(d["q"], d["k"], d["v"], d["z"], d["beta"], d["A"], d["S0"],
+                                    threads=host_pool_size())
+    eo, es = err(o, o_ref), err(Sf, S_ref)
+    eh = max(err(o[:, h], o_ref[:, h]) for h in range(H))
+    say(f"  prefill_64k fp32 err_o={eo:.3e} err_S={es:.3e} worst-head err_o={eh:.3e}")
+    assert eo <= 1e-4 and es <= 1e-4 and eh <= 1e-4
 
 
 @pytest.mark.timeout(600)
