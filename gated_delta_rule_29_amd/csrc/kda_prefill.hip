@@ -31,10 +31,11 @@
 //                 sequence's last, one workgroup of eight waves per
 //                 (segment, head), the chunk's operand tiles copied into LDS;
 //   seg_scan_kernel (kda_segment.hip)  the state entering each segment;
-//   chain_kernel  the state pass, one workgroup per (segment, head, 32 value
-//                 columns): keeps its 128 x 32 fp32 state slice in registers
-//                 across the segment's chunks and forms Delta, the output and
-//                 the next state with MFMA;
+//   state_kernel  the state pass, one workgroup of eight waves per (segment,
+//                 head): keeps the 128 x 128 fp32 state in registers across the
+//                 segment's chunks (16 columns per wave), the chunk's operand
+//                 tiles copied into LDS, and forms Delta, the output and the
+//                 next state with MFMA;
 //   gated_rmsnorm_kernel  (with the layer's output step) in place on o.
 //
 // This file serves fp32 q/k/v (bf16 q/k/v take kda_segment.hip's path).
@@ -47,8 +48,8 @@
 // preconditions (unit-length q and k, beta in [0, 1], decay factors <= 1)
 // their entries are at most about 1 in magnitude, where fp16 holds them to 22
 // bits down to 2^-3 and to 2^-25 absolutely below.  The state and Delta are
-// split on the fly at a power-of-two scale per workgroup that keeps them inside
-// fp16's range.
+// split on the fly, each wave's columns at a power-of-two scale of their own
+// that keeps them inside fp16's range.
 #include "kda_common.hpp"
 
 namespace kda {
@@ -102,11 +103,10 @@ __host__ inline Table carve(void *ws, int N) {
     return t;
 }
 __host__ inline int64_t max_chunks(int64_t T_total, int N) { return (T_total + CH - 1) / CH + N; }
-// Segments of the chain: about SEG32_TARGET (segment, head) pairs in all.  The
-// map pass runs one workgroup (133 KB of LDS, one per CU) per pair with a
-// successor: at 64K x 16, 240 of them fill the chip once (0.39 ms; with 128
-// pairs, 112 workgroups took 0.70 ms).  The state pass (four workgroups per
-// pair) took the same time from 128 to 1,024 pairs; fewer pairs shorten the scan.
+// Segments of the chain: about SEG32_TARGET (segment, head) pairs in all.  Both
+// chain passes run one workgroup (133 / 154 KB of LDS, one per CU) per pair (the
+// map pass per pair with a successor): at 64K x 16, 240 and 256 of them fill the
+// chip once (the map pass 0.39 ms; with 128 pairs, 112 workgroups took 0.70 ms).
 constexpr int SEG32_TARGET = 256;
 // The segment length is even: the map pass runs its chain two steps per loop
 // iteration (one per LDS image).
@@ -678,24 +678,7 @@ __global__ __launch_bounds__(256) void intra_kernel(const float *__restrict__ q,
     }
 }
 
-// ----------------------------------------------------------------- chain --
-
-constexpr int NCT = 2;         // 16-column tiles per state-pass workgroup (its registers allow no more)
-constexpr int NB = 16 * NCT;  // state columns per workgroup
-constexpr int PSH = 136;      // pitch (halves) of the state arrays
-constexpr int PDH = 72;       // pitch (halves) of the Delta arrays
-
-struct ChainSmem {
-    // the state slice times 2^E as fp16 hi + lo, transposed [column][key row],
-    // key rows in the operand tiles' k order (position 32 s + 8 g + e holds row
-    // 32 s + 16 (e >> 2) + 4 g + (e & 3)), so that a lane's 16 B at 32 s + 8 g are
-    // its B-operand slice of k-step s
-    __attribute__((aligned(16))) _Float16 Sh[NB * PSH], Slo[NB * PSH];
-    // Delta times 2^E as fp16 hi + lo, transposed [column][token], tokens in the
-    // same order
-    __attribute__((aligned(16))) _Float16 Dh[NB * PDH], Dlo[NB * PDH];
-    uint32_t ex[4];  // per wave: exponent bound of its state rows and U rows
-};
+// ---------------------------------------------------------- chain helpers --
 
 // A fragment as fp16 hi + lo.
 struct H8 {
@@ -712,260 +695,6 @@ __device__ __forceinline__ f32x4 mma_term(int t, f32x4 c, const H8 &a, const H8 
     return mfma_f16(t == 0 ? a.lo : a.hi, t == 1 ? b.lo : b.hi, c);
 }
 __device__ __forceinline__ uint32_t abs_bits(float x) { return __builtin_bit_cast(uint32_t, x) & 0x7FFFFFFFu; }
-
-// The state pass: the chain over one segment of a sequence from the state the
-// scan gave it, 32 state columns per workgroup (each operand fragment loaded
-// serves both 16-column tiles), products as fp16 hi + lo pairs; writes o (and
-// snapshots, and S_final after a sequence's last segment).  Workgroups are
-// numbered so that the four column blocks of one (segment, head) share an XCD
-// (and its L2, which serves their common operand block), and the (segment,
-// head) pairs with work come first.
-//
-// The workgroup carries its state columns, U, Delta and O times 2^E.  The map
-// is linear in (S, U) column by column, so any power-of-two scale is exact; E
-// is re-picked whenever the largest |S| or |U| of the workgroup leaves
-// [2^7, 2^11).  Then |Delta| = |U - W S| < 2^11 (1 + sqrt(128)) < 2^15 (each
-// row of W has norm <= 1 with unit keys and beta in [0, 1]), inside fp16's
-// range, and values 2^-10 below the largest keep all 22 bits of the pair.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void chain_kernel(
-    int N, int H, Table tab, float *__restrict__ o, float *__restrict__ S_final) {
-    __shared__ ChainSmem sm;
-    constexpr int NCB = D / NB;  // column blocks per (segment, head)
-    const int Lw = blockIdx.x;
-    const int p = (Lw & 7) + 8 * (Lw / (8 * NCB)), cb = (Lw >> 3) % NCB;
-    const int a = p / H, h = p % H;
-    if (a >= tab.sq.seg0(N)) return;
-    const int n = tab.sq.seq_of_seg(a, N);
-    const int j = a - tab.sq.seg0(n);
-    const int x = tab.sq.seg0(n) + j;  // segment index of the states
-    const int pn = tab.sq.seg0(n + 1) - tab.sq.seg0(n);
-    const int col0 = NB * cb;  // first column of the workgroup
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, lr = l & 15;
-
-    // state slice: wave w owns key rows [32w, 32w+32) as two 16-row tiles (C
-    // layout) of each column tile ct (columns col0 + 16 ct + lr)
-    f32x4 Sr[NCT][2];
-    const size_t sblk = ((size_t)x * H + h) * D * D;
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int r = 32 * w + 16 * u + 4 * g + m, cc = col0 + 16 * ct + lr;
-                Sr[ct][u][m] = tab.Sin[sblk + (size_t)r * D + cc];
-            }
-    int E = 0;
-
-    const int cseq = tab.sq.chunk0(n);  // the sequence's first chunk
-    const int cbeg = cseq + j * tab.sq.L, cend = min(tab.sq.chunk0(n + 1), cbeg + tab.sq.L);
-    const int64_t sstart = tab.sq.start(n), send = tab.sq.end(n);
-    const int nks_aq = w < 2 ? 1 : 2;  // 32-token k-steps of Aqk row tile w
-    const int64_t ck_base = tab.ck.S ? tab.ck.off[n] : 0;
-
-    // Operands of one chunk, in registers.  The barriers wait only for LDS
-    // traffic, so loads stay in flight across them.  U is loaded one chunk
-    // ahead (its largest value sets the step's scale before the first
-    // barrier); each other group for chunk c + 1 as soon as chunk c has used it
-    // (the last chunk re-reads itself).
-    H8 wf[4], qf[4], kf[2][2], af[2];
-    float uv[NCT][4], gmv[2][4];
-    auto load_w = [&](const char *blk) __attribute__((always_inline)) {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            wf[ks] = ld_frag(blk + OFF_W + 1024 * (4 * w + ks) + 16 * l, LO_128);
-            qf[ks] = ld_frag(blk + OFF_QT + 1024 * (4 * w + ks) + 16 * l, LO_128);
-        }
-    };
-    auto load_u = [&](const char *blk) __attribute__((always_inline)) {
-        const __amdgpu_buffer_rsrc_t ru = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(blk + OFF_U + 4 * (16 * w * D + col0)), 0, 16 * D * 4, BUF_RSRC3);
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-            for (int m = 0; m < 4; ++m)
-                uv[ct][m] = __builtin_bit_cast(
-                    float, __builtin_amdgcn_raw_buffer_load_b32(ru, 4 * ((4 * g + m) * D + 16 * ct + lr), 0, 0));
-    };
-    auto load_ka = [&](const char *blk) __attribute__((always_inline)) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int kr = 32 * w + 16 * u;
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) kf[u][ks] = ld_frag(blk + OFF_KT + 1024 * (2 * (2 * w + u) + ks) + 16 * l, LO_128);
-#pragma unroll
-            for (int m = 0; m < 4; ++m) gmv[u][m] = ((const float *)(blk + OFF_GM))[kr + 4 * g + m];
-        }
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) af[ks] = ld_frag(blk + OFF_AQ + 1024 * (2 * w + ks) + 16 * l, LO_AQ);
-    };
-    auto block = [&](int cc) { return tab.blocks + ((size_t)cc * H + h) * BLK_BYTES; };
-    // This wave's rows of the state slice, split, into the B-operand arrays.
-    // (Values past fp16's range become inf here; the step then rescales and
-    // publishes again before anything reads them.)
-    auto publish_state = [&]() __attribute__((always_inline)) {
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                uint32_t h0, l0, h1, l1;
-                split_f16_pair(Sr[ct][u][0], Sr[ct][u][1], h0, l0);
-                split_f16_pair(Sr[ct][u][2], Sr[ct][u][3], h1, l1);
-                const int e0 = (16 * ct + lr) * PSH + 32 * w + 8 * g + 4 * u;  // key row 32 w + 16 u + 4 g + m
-                *(u32x2 *)&sm.Sh[e0] = u32x2{h0, h1};
-                *(u32x2 *)&sm.Slo[e0] = u32x2{l0, l1};
-            }
-    };
-    if (cbeg < cend) {
-        load_u(block(cbeg));
-        load_w(block(cbeg));
-        load_ka(block(cbeg));
-    }
-
-    for (int c = cbeg; c < cend; ++c) {
-        const char *nblk = block(min(c + 1, cend - 1));
-        const int64_t t0 = sstart + (int64_t)(c - cseq) * CH;
-        const int len = (int)min((int64_t)CH, send - t0);
-
-        // (1) publish the state slice as the B operand of W S and Q~ S, and this
-        // wave's exponent bound: the fp32 exponent field of max(|S|, |U| 2^E)
-        // (255: inf or NaN present, which keeps E: the result is not finite).
-        {
-            uint32_t ms = 0, mu = 0;
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    ms = max(ms, max(abs_bits(Sr[ct][0][m]), abs_bits(Sr[ct][1][m])));
-                    mu = max(mu, abs_bits(uv[ct][m]));
-                }
-            const int es = (int)(ms >> 23), eu = (int)(mu >> 23);
-            const int el = (es == 255 || eu == 255) ? 0xFFFF : max(es, eu ? max(eu + E, 0) : 0);
-            const uint32_t ew = wave_umax((uint32_t)el);
-            publish_state();
-            if (l == 0) sm.ex[w] = ew;
-        }
-        lds_barrier();
-        {
-            const uint32_t e = __builtin_amdgcn_readfirstlane(max(max(sm.ex[0], sm.ex[1]), max(sm.ex[2], sm.ex[3])));
-            if (e != 0xFFFF && e != 0 && (e < 134 || e > 137)) {  // rescale (every wave takes this branch)
-                const int sh = 136 - (int)e;
-                E += sh;
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-                    for (int u = 0; u < 2; ++u)
-#pragma unroll
-                        for (int m = 0; m < 4; ++m) Sr[ct][u][m] = __builtin_amdgcn_ldexpf(Sr[ct][u][m], sh);
-                publish_state();
-                lds_barrier();
-            }
-        }
-
-        // (2) Delta rows [16w, 16w+16) = U 2^E - W S (W stored negated, the
-        // accumulator starts at U 2^E);  O = Q~ S
-        f32x4 ws[NCT], oacc[NCT];
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-#pragma unroll
-            for (int m = 0; m < 4; ++m) ws[ct][m] = __builtin_amdgcn_ldexpf(uv[ct][m], E);
-            oacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-        load_u(nblk);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            H8 sb[NCT];
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                const int e0 = (16 * ct + lr) * PSH + 32 * ks + 8 * g;
-                sb[ct] = {*(const f16x8 *)&sm.Sh[e0], *(const f16x8 *)&sm.Slo[e0]};
-            }
-#pragma unroll
-            for (int t = 0; t < 3; ++t)
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) {
-                    ws[ct] = mma_term(t, ws[ct], wf[ks], sb[ct]);
-                    oacc[ct] = mma_term(t, oacc[ct], qf[ks], sb[ct]);
-                }
-        }
-        load_w(nblk);
-        // (3) publish Delta as the B operand of Aqk Delta and K~^T Delta
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            uint32_t h0, l0, h1, l1;
-            split_f16_pair(ws[ct][0], ws[ct][1], h0, l0);
-            split_f16_pair(ws[ct][2], ws[ct][3], h1, l1);
-            const int e0 = (16 * ct + lr) * PDH + 32 * (w >> 1) + 8 * g + 4 * (w & 1);  // token 16 w + 4 g + m
-            *(u32x2 *)&sm.Dh[e0] = u32x2{h0, h1};
-            *(u32x2 *)&sm.Dlo[e0] = u32x2{l0, l1};
-        }
-        lds_barrier();
-        H8 dF[NCT][2];
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const int e0 = (16 * ct + lr) * PDH + 32 * ks + 8 * g;
-                dF[ct][ks] = {*(const f16x8 *)&sm.Dh[e0], *(const f16x8 *)&sm.Dlo[e0]};
-            }
-        // (4) S <- Diag(gamma) S + K~^T Delta  (key rows [32w, 32w+32)), and
-        // (5) O += Aqk Delta  (row tile w; Aqk is zero above the diagonal)
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-                for (int m = 0; m < 4; ++m) Sr[ct][u][m] *= gmv[u][m];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int t = 0; t < 3; ++t) {
-#pragma unroll
-                for (int u = 0; u < 2; ++u)
-#pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct) Sr[ct][u] = mma_term(t, Sr[ct][u], kf[u][ks], dF[ct][ks]);
-                if (ks < nks_aq)
-#pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct) oacc[ct] = mma_term(t, oacc[ct], af[ks], dF[ct][ks]);
-            }
-        load_ka(nblk);
-        // (5b) snapshot after a full chunk that ends a stride
-        if (tab.ck.S && len == CH && (c - cseq + 1) % tab.ck.stride_chunks == 0) {
-            const int64_t slot = ck_base + (c - cseq + 1) / tab.ck.stride_chunks - 1;
-            if (slot < tab.ck.cap) {
-                float *dst = tab.ck.S + ((size_t)slot * H + h) * D * D;
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-                    for (int u = 0; u < 2; ++u)
-#pragma unroll
-                        for (int m = 0; m < 4; ++m)
-                            dst[(size_t)(32 * w + 16 * u + 4 * g + m) * D + col0 + 16 * ct + lr] =
-                                __builtin_amdgcn_ldexpf(Sr[ct][u][m], -E);
-            }
-        }
-        // (6) output rows of this chunk
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int t = 16 * w + 4 * g + m;
-            if (t < len)
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct)
-                    o[((size_t)(t0 + t) * H + h) * D + col0 + 16 * ct + lr] = __builtin_amdgcn_ldexpf(oacc[ct][m], -E);
-        }
-    }
-    if (S_final && j == pn - 1) {
-        float *dst = S_final + ((size_t)n * H + h) * D * D;
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-                for (int m = 0; m < 4; ++m)
-                    dst[(size_t)(32 * w + 16 * u + 4 * g + m) * D + col0 + 16 * ct + lr] =
-                        __builtin_amdgcn_ldexpf(Sr[ct][u][m], -E);
-    }
-}
 
 // ------------------------------------------------------------- map pass --
 
@@ -1170,6 +899,266 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 dst[(size_t)(16 * rt + 4 * g + m) * D + 16 * ct + lr] = __builtin_amdgcn_ldexpf(X[rt][ct][m], -E);
 }
 
+// ------------------------------------------------------------ state pass --
+
+// LDS images of one chunk for the state pass, copied straight from its block.
+// Image A: the -W tiles (hi, then lo) and the Q~ tiles (hi, then lo); read by
+// the first products of a step, refilled for the next chunk as soon as every
+// wave has read it.  Image B (two of them, alternating by step): the K~^T tiles
+// (hi, then lo), the six Aqk tiles on or below the diagonal (hi, then lo) and
+// gamma; filled a whole step ahead.
+constexpr int SA_W = 0, SA_QT = 32768, SA_BYTES = 65536;
+constexpr int SB_KT = 0, SB_AQ = 32768, SB_GM = SB_AQ + 12288, SB_BYTES = SB_GM + 1024;
+
+__device__ __forceinline__ void state_dma_a(const char *__restrict__ blk, char *img, int wv, int l) {
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void *)blk, 0, (int)BLK_BYTES, BUF_RSRC3);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int x = wv + 8 * i;  // tile 0..63: -W hi, -W lo, Q~ hi, Q~ lo
+        const int src = x < 32 ? (int)OFF_W + 1024 * x : (int)OFF_QT + 1024 * (x - 32);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(img + 1024 * x), 16, src + 16 * l, 0, 0, 0);
+    }
+}
+__device__ __forceinline__ void state_dma_b(const char *__restrict__ blk, char *img, int wv, int l) {
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void *)blk, 0, (int)BLK_BYTES, BUF_RSRC3);
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+        const int x = wv + 8 * i;  // tile 0..43: K~^T hi, K~^T lo, Aqk hi (6), Aqk lo (6)
+        if (x < 44) {
+            int src;
+            if (x < 32) {
+                src = (int)OFF_KT + 1024 * x;
+            } else {  // slot q of the six Aqk tiles 2 rt + s with s <= rt / 2: tiles 0, 2, 4, 5, 6, 7
+                const int q = (x - 32) % 6;
+                src = (int)OFF_AQ + (x < 38 ? 0 : LO_AQ) + 1024 * (q < 2 ? 2 * q : q + 2);
+            }
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(img + 1024 * x), 16, src + 16 * l, 0, 0, 0);
+        }
+    }
+    // gamma by every wave (the same values; lanes 32-63 read past the block,
+    // which gives zeros, into padding)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(img + SB_GM), 16, (int)OFF_GM + 16 * l, 0, 0, 0);
+}
+
+// The state pass: the chain over one segment of a sequence from the state the
+// scan gave it, one workgroup of eight waves per (segment, head).  Wave w owns
+// the value columns 16 w .. 16 w + 15 of the state, all 128 rows, as C-layout
+// tiles, and feeds them as the B operand of W S and Q~ S by the tile pairing of
+// the block's k order (Delta likewise for Aqk Delta and K~^T Delta).  Each
+// chunk's operand tiles are read from memory once per workgroup, into the LDS
+// images above; U (fp32) is loaded into registers a step ahead.  Products as
+// fp16 hi + lo pairs (three MFMAs), with the wave's columns, U, Delta and O at a
+// power-of-two scale 2^E per wave (re-picked when the largest |S| or |U| 2^E
+// leaves [2^7, 2^11): then |Delta| < 2^11 (1 + sqrt(128)) < 2^15).  Writes o
+// (and snapshots, and S_final after a sequence's last segment).
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void state_kernel(
+    int N, int H, Table tab, float *__restrict__ o, float *__restrict__ S_final) {
+    __shared__ __align__(16) char imgA[SA_BYTES];
+    __shared__ __align__(16) char imgB0[SB_BYTES];
+    __shared__ __align__(16) char imgB1[SB_BYTES];
+    // workgroup i: head i mod H of the (i / H)-th segment
+    const int a = (int)blockIdx.x / H, h = (int)blockIdx.x % H;
+    if (a >= tab.sq.seg0(N)) return;
+    const int n = tab.sq.seq_of_seg(a, N);
+    const int j = a - tab.sq.seg0(n);
+    const int x = tab.sq.seg0(n) + j;  // segment index of the states
+    const int pn = tab.sq.seg0(n + 1) - tab.sq.seg0(n);
+    const int cseq = tab.sq.chunk0(n);
+    const int cbeg = cseq + j * tab.sq.L, cend = min(tab.sq.chunk0(n + 1), cbeg + tab.sq.L);
+    const int64_t sstart = tab.sq.start(n), send = tab.sq.end(n);
+    const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, g = l >> 4,
+              lr = l & 15;
+    const int col = 16 * wv + lr;  // this lane's state column
+    const size_t HD = (size_t)H * D;
+    auto block = [&](int c) { return tab.blocks + ((size_t)c * H + h) * BLK_BYTES; };
+
+    f32x4 X[8];
+    const size_t sblk = ((size_t)x * H + h) * D * D;
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) X[rt][m] = tab.Sin[sblk + (size_t)(16 * rt + 4 * g + m) * D + col];
+    int E = 0;
+
+    // U of a chunk: tile rt rows 16 rt + 4 g + m, column col (a buffer of no
+    // records reads 0 past the segment)
+    f32x4 uv[4];
+    auto load_u = [&](int c) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t ru = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(block(c) + OFF_U), 0, c < cend ? 64 * D * 4 : 0, BUF_RSRC3);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                uv[rt][m] = __builtin_bit_cast(
+                    float, __builtin_amdgcn_raw_buffer_load_b32(ru, 4 * ((4 * g + m) * D + col), 4 * 16 * rt * D, 0));
+    };
+    auto store_state = [&](float *dst) __attribute__((always_inline)) {
+#pragma unroll
+        for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                dst[(size_t)(16 * rt + 4 * g + m) * D + col] = __builtin_amdgcn_ldexpf(X[rt][m], -E);
+    };
+    const int64_t ck_base = tab.ck.S ? tab.ck.off[n] : 0;
+    if (cbeg < cend) {
+        state_dma_b(block(cbeg), imgB0, wv, l);
+        state_dma_a(block(cbeg), imgA, wv, l);
+        load_u(cbeg);
+    }
+    // Outstanding VMEM operations a step may leave behind the copy of image A
+    // for the next chunk: its 16 output stores (and the 32 snapshot stores of a
+    // step that ends a stride, after which the next step waits for everything).
+    bool drain = true;  // the first step waits for everything
+
+    auto step = [&](int c, const char *bcur, char *bnxt) __attribute__((always_inline)) {
+        // Image A and U of this chunk (and image B, issued a step earlier) have
+        // landed for this wave, then for every wave; every wave is done with
+        // the step before, so `bnxt` may be refilled.
+        if (drain)
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        else
+            __builtin_amdgcn_s_waitcnt(0x0F70 | 0x4000);  // vmcnt(16): all but the last step's output stores
+        __asm__ volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        __asm__ volatile("" ::: "memory");
+        if (c + 1 < cend) state_dma_b(block(c + 1), bnxt, wv, l);
+        // the step's scale (as in the map pass)
+        {
+            uint32_t mx = 0, mu = 0;
+#pragma unroll
+            for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    mx = max(mx, abs_bits(X[rt][m]));
+                    if (rt < 4) mu = max(mu, abs_bits(uv[rt][m]));
+                }
+            const int es = (int)(mx >> 23), eu = (int)(mu >> 23);
+            const int el = (es == 255 || eu == 255) ? 0xFFFF : max(es, eu ? max(eu + E, 0) : 0);
+            const int e = (int)wave_umax((uint32_t)el);
+            if (e != 0xFFFF && e != 0 && (e < 134 || e > 137)) {
+                const int sh = 136 - e;
+                E += sh;
+#pragma unroll
+                for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) X[rt][m] = __builtin_amdgcn_ldexpf(X[rt][m], sh);
+            }
+        }
+        // Delta = U 2^E - W S (W stored negated, the accumulator starts at U 2^E);  O = Q~ S
+        f32x4 Dl[4], O[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) Dl[rt][m] = __builtin_amdgcn_ldexpf(uv[rt][m], E);
+            O[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        load_u(c + 1);
+        const char *la = imgA + 16 * l;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            H8 xb;  // S rows 32 s .. 32 s + 31 as the B operand: C tiles 2 s and 2 s + 1
+            {
+                uint32_t hw[4], lw[4];
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const f32x4 &xv = X[2 * s + (p >> 1)];
+                    split_f16_pair(xv[2 * (p & 1)], xv[2 * (p & 1) + 1], hw[p], lw[p]);
+                }
+                xb = {__builtin_bit_cast(f16x8, u32x4{hw[0], hw[1], hw[2], hw[3]}),
+                      __builtin_bit_cast(f16x8, u32x4{lw[0], lw[1], lw[2], lw[3]})};
+            }
+#pragma unroll
+            for (int r2 = 0; r2 < 4; r2 += 2) {
+                H8 wa[2], qa[2];
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    wa[q] = ld_frag(la + SA_W + 1024 * (4 * (r2 + q) + s), LO_128);
+                    qa[q] = ld_frag(la + SA_QT + 1024 * (4 * (r2 + q) + s), LO_128);
+                }
+#pragma unroll
+                for (int t = 0; t < 3; ++t)
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) {
+                        Dl[r2 + q] = mma_term(t, Dl[r2 + q], wa[q], xb);
+                        O[r2 + q] = mma_term(t, O[r2 + q], qa[q], xb);
+                    }
+            }
+        }
+        // every wave has read image A: refill it with the next chunk's
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        __asm__ volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        __asm__ volatile("" ::: "memory");
+        if (c + 1 < cend) state_dma_a(block(c + 1), imgA, wv, l);
+        // Delta as the B operand (tokens 32 s .. 32 s + 31: C tiles 2 s, 2 s + 1)
+        H8 db[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            uint32_t hw[4], lw[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const f32x4 &dv = Dl[2 * s + (p >> 1)];
+                split_f16_pair(dv[2 * (p & 1)], dv[2 * (p & 1) + 1], hw[p], lw[p]);
+            }
+            db[s] = {__builtin_bit_cast(f16x8, u32x4{hw[0], hw[1], hw[2], hw[3]}),
+                     __builtin_bit_cast(f16x8, u32x4{lw[0], lw[1], lw[2], lw[3]})};
+        }
+        const char *lb = bcur + 16 * l;
+        // O += (Aqk * Tril) Delta: tiles (rt, s), s <= rt / 2, image slot q
+#pragma unroll
+        for (int q = 0; q < 6; ++q) {
+            const int rt = q < 2 ? q : (q < 4 ? 2 : 3), s = q < 2 ? 0 : (q & 1);
+            const H8 aa = ld_frag(lb + SB_AQ + 1024 * q, 6144);
+#pragma unroll
+            for (int t = 0; t < 3; ++t) O[rt] = mma_term(t, O[rt], aa, db[s]);
+        }
+        // S <- Diag(gamma) S + K~^T Delta
+#pragma unroll
+        for (int rt = 0; rt < 8; ++rt) {
+            const f32x4 gm = *(const f32x4 *)(bcur + SB_GM + 64 * rt + 16 * g);  // gamma of rows 16 rt + 4 g + m
+#pragma unroll
+            for (int m = 0; m < 4; ++m) X[rt][m] *= gm[m];
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int r4 = 0; r4 < 8; r4 += 4) {
+                H8 ka[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) ka[q] = ld_frag(lb + SB_KT + 1024 * (2 * (r4 + q) + s), LO_128);
+#pragma unroll
+                for (int t = 0; t < 3; ++t)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) X[r4 + q] = mma_term(t, X[r4 + q], ka[q], db[s]);
+            }
+        // output rows of this chunk, and a snapshot after a full chunk that ends a stride
+        const int64_t t0 = sstart + (int64_t)(c - cseq) * CH;
+        const int len = (int)min((int64_t)CH, send - t0);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int t = 16 * rt + 4 * g + m;
+                if (t < len) o[(size_t)(t0 + t) * HD + (size_t)h * D + col] = __builtin_amdgcn_ldexpf(O[rt][m], -E);
+            }
+        drain = false;
+        if (tab.ck.S && len == CH && (c - cseq + 1) % tab.ck.stride_chunks == 0) {
+            const int64_t slot = ck_base + (c - cseq + 1) / tab.ck.stride_chunks - 1;
+            if (slot < tab.ck.cap) {
+                store_state(tab.ck.S + ((size_t)slot * H + h) * D * D);
+                drain = true;
+            }
+        }
+    };
+    for (int c = cbeg; c < cend; c += 2) {
+        step(c, imgB0, imgB1);
+        if (c + 1 < cend) step(c + 1, imgB1, imgB0);
+    }
+    if (S_final && j == pn - 1) store_state(S_final + ((size_t)n * H + h) * D * D);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no copy may land after the workgroup ends
+}
+
 // ------------------------------------------------------------ output step --
 
 // The layer's output step on fp32 rows of 128 values, in place (one wave per
@@ -1233,10 +1222,9 @@ int launch_prefill(const void *q, const void *k, const void *v, bool f32io, cons
     tab.Mseg = (float *)(tab.blocks + (size_t)max_chunks(T_total, N) * (size_t)H * BLK_BYTES);
     tab.Bseg = tab.Mseg + st;
     tab.Sin = tab.Bseg + st;
-    // grids: the state pass 4 workgroups of 256 per (segment, head) slot, the
-    // map pass one of 512; a launch covers at most 2^32 - 1 work-items
-    const int64_t slots8 = (nsm * H + 7) / 8;
-    if (slots8 * 128 > (int64_t)(UINT32_MAX / 256) || max_chunks(T_total, N) * H > (int64_t)UINT32_MAX ||
+    // grids: one workgroup per (segment, head) slot; a launch covers at most
+    // 2^32 - 1 work-items
+    if (nsm * H > (int64_t)(UINT32_MAX / 512) || max_chunks(T_total, N) * H > (int64_t)UINT32_MAX ||
         (int64_t)CH * H * D > (int64_t)INT32_MAX)
         return -1;
     if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return -1;
@@ -1254,8 +1242,7 @@ int launch_prefill(const void *q, const void *k, const void *v, bool f32io, cons
     if (ev && hipEventRecord(ev[3], stream) != hipSuccess) return -1;
     if (launch_seg_scan(S0, N, H, tab.sq, tab.Mseg, tab.Bseg, tab.Sin, S_final, stream) != 0) return -1;
     if (ev && hipEventRecord(ev[4], stream) != hipSuccess) return -1;
-    hipLaunchKernelGGL(chain_kernel, dim3((unsigned)(8 * (D / NB) * slots8)), dim3(256), 0, stream, N, H, tab, o,
-                       S_final);
+    hipLaunchKernelGGL(state_kernel, dim3((unsigned)(nsm * H)), dim3(512), 0, stream, N, H, tab, o, S_final);
     if (ly.gate && T_total > 0)
         hipLaunchKernelGGL(gated_rmsnorm_kernel, dim3((unsigned)((T_total * H + 3) / 4)), dim3(256), 0, stream, o,
                            ly.gate, ly.weight, ly.norm_eps, T_total * H);
