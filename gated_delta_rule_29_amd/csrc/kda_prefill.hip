@@ -50,6 +50,8 @@
 // bits down to 2^-3 and to 2^-25 absolutely below.  The state and Delta are
 // split on the fly, each wave's columns at a power-of-two scale of their own
 // that keeps them inside fp16's range.
+#include <type_traits>
+
 #include "kda_common.hpp"
 
 namespace kda {
@@ -277,7 +279,9 @@ __device__ __forceinline__ void st_pair4(char *base, int lo, int tile, int l, in
     *(u32x2 *)(p + lo) = u32x2{l0, l1};
 }
 
-
+// SP: the unbounded softplus decay; LRZ: the low-rank forget gate (separate
+// instantiations, so that the plain path's loops carry none of their branches).
+template <bool SP, bool LRZ>
 __global__ __launch_bounds__(256) void intra_kernel(const float *__restrict__ q, const float *__restrict__ k,
                                                     const float *__restrict__ v, const float *__restrict__ z,
                                                     const float *__restrict__ beta,
@@ -350,7 +354,7 @@ __global__ __launch_bounds__(256) void intra_kernel(const float *__restrict__ q,
     // Unbounded softplus decay: E1 holds the logs G_t - R_s rather than their
     // exponentials (1 / E1 would overflow), and the diagonal Gram tiles are
     // formed position pair by position pair in phase 2.
-    const bool sp = tab.ly.gate_kind == GATE_SOFTPLUS;
+    constexpr bool sp = SP;
     const bool zh = tab.ly.gate_per_head;  // z is [tokens, H]
     // The running sums are kept in fp64: a log-decay difference formed from
     // fp32 sums of up to 64 gates (|G| up to 320) loses ~1e-5 absolute, which
@@ -365,7 +369,7 @@ __global__ __launch_bounds__(256) void intra_kernel(const float *__restrict__ q,
 #pragma unroll
         for (int u = 0; u < SUB; ++u) {
             const int t = (half + 2 * si) * SUB + u, tc = t < len ? t : 0;
-            zr[si][u] = tab.ly.zu ? 0.f : (zh ? z[(size_t)(t0 + tc) * H + h] : zc[tok(tc) + ch]);
+            zr[si][u] = LRZ ? 0.f : (zh ? z[(size_t)(t0 + tc) * H + h] : zc[tok(tc) + ch]);
         }
 #pragma unroll
     for (int si = 0; si < 2; ++si) {
@@ -377,7 +381,7 @@ __global__ __launch_bounds__(256) void intra_kernel(const float *__restrict__ q,
             float gt = 0.f;
             if (t < len) {
                 float zv;
-                if (tab.ly.zu) {  // low-rank forget gate: z = sum_j u[t, j] W[h, ch, j]
+                if constexpr (LRZ) {  // low-rank forget gate: z = sum_j u[t, j] W[h, ch, j]
                     const int r = tab.ly.zrank;
                     const __bf16 *ur = tab.ly.zu + (size_t)(t0 + t) * r, *wr = tab.ly.zw + ((size_t)h * D + ch) * r;
                     float acc = 0.f;
@@ -1234,8 +1238,18 @@ int launch_prefill(const void *q, const void *k, const void *v, bool f32io, cons
     if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return -1;
     if (T_total > 0) {
         const size_t smem = sizeof(IntraSmem);
-        hipLaunchKernelGGL(intra_kernel, dim3((unsigned)nc, (unsigned)H), dim3(256), smem, stream,
-                           (const float *)q, (const float *)k, (const float *)v, z, beta, A, N, H, tab);
+        auto intra = [&](auto sp, auto lrz) {
+            hipLaunchKernelGGL((intra_kernel<decltype(sp)::value, decltype(lrz)::value>), dim3((unsigned)nc, (unsigned)H),
+                               dim3(256), smem, stream, (const float *)q, (const float *)k, (const float *)v, z, beta,
+                               A, N, H, tab);
+        };
+        using T_ = std::true_type;
+        using F_ = std::false_type;
+        const bool sp = ly.gate_kind == GATE_SOFTPLUS, lr = ly.zu != nullptr;
+        if (sp)
+            lr ? intra(T_{}, T_{}) : intra(T_{}, F_{});
+        else
+            lr ? intra(F_{}, T_{}) : intra(F_{}, F_{});
     }
     if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return -1;
     hipLaunchKernelGGL(map_kernel, dim3((unsigned)(nsm * H)), dim3(512), 0, stream, N, H, tab);
@@ -1254,9 +1268,10 @@ int launch_prefill(const void *q, const void *k, const void *v, bool f32io, cons
 int set_prefill_attributes() {
     if (set_segment_attributes() != 0) return -1;
     const int smem = (int)sizeof(IntraSmem);
-    if (hipFuncSetAttribute((const void *)intra_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, smem) !=
-        hipSuccess)
-        return -1;
+    const void *fns[4] = {(const void *)intra_kernel<false, false>, (const void *)intra_kernel<false, true>,
+                          (const void *)intra_kernel<true, false>, (const void *)intra_kernel<true, true>};
+    for (const void *f : fns)
+        if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, smem) != hipSuccess) return -1;
     return 0;
 }
 
