@@ -1358,10 +1358,9 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
 // Loads and stores share the in-order vmcnt counter; the store wave, which
 // copies S_in[p] out of the exchange buffer, keeps the state stores off the
 // compute waves' counter.
-constexpr int SCAN_NT = 576;
-constexpr int SCAN_WAVE_BYTES = 9216;              // 16 rows of M (swizzled), then the 16 x 16 tile of B
+constexpr int SCAN_NT = 640;                          // 8 compute waves, a store wave, a copy wave
+constexpr int SCAN_WAVE_BYTES = 9216;                 // 16 rows of M (swizzled), then the 16 x 16 tile of B
 constexpr int SCAN_SLOT_BYTES = 8 * SCAN_WAVE_BYTES;  // one map
-constexpr int SCAN_COPIES = 9;                       // copy instructions per wave and map
 __global__ __launch_bounds__(SCAN_NT) void seg_scan_kernel(const float *__restrict__ S0, int N, int H, SegTable tab,
                                                            float *__restrict__ S_final) {
     // Distinct arrays: a read of one provably does not alias a copy in flight into the other.
@@ -1372,8 +1371,8 @@ __global__ __launch_bounds__(SCAN_NT) void seg_scan_kernel(const float *__restri
     const int n = nh / H, h = nh % H;
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, g = l >> 4,
               lr = l & 15;
-    __builtin_assume(w >= 0 && w < 9);
-    const bool storer = w == 8;
+    __builtin_assume(w >= 0 && w < 10);
+    const bool storer = w == 8, copier = w == 9;
     const int col = 16 * cb + lr, r0 = 16 * (w & 7);
     const int first = tab.sq.seg0(n), pn = tab.sq.seg0(n + 1) - first;
     f32x4 Sr;
@@ -1381,19 +1380,19 @@ __global__ __launch_bounds__(SCAN_NT) void seg_scan_kernel(const float *__restri
 #pragma unroll
     for (int m = 0; m < 4; ++m) Sr[m] = S0 ? S0[s0b + (size_t)(r0 + 4 * g + m) * D + col] : 0.f;
     if (pn == 0) {
-        if (S_final && !storer)
+        if (S_final && w < 8)
 #pragma unroll
             for (int m = 0; m < 4; ++m) S_final[s0b + (size_t)(r0 + 4 * g + m) * D + col] = Sr[m];
         return;
     }
     // Steps run in pairs (one per slot), pn rounded up to even: an odd count
     // ends with a step whose state nobody stores.  Every wave passes the same
-    // number of barriers.
+    // number of barriers: two per step.
     const int pe = (pn + 1) & ~1;
     if (storer) {
         // Lane (row group l / 4, column quad l % 4) writes rows 16 k + l / 4,
         // k = 0..7, four columns each; all read before the first store, so the
-        // stores issue back to back.  One pair of barriers per step, as below.
+        // stores issue back to back.
         for (int p = 0; p < pe; ++p) {
             lds_barrier();
             f32x4 x[8];
@@ -1410,44 +1409,70 @@ __global__ __launch_bounds__(SCAN_NT) void seg_scan_kernel(const float *__restri
         }
         return;
     }
-    // The copies: M_p rows r0 + 2i, r0 + 2i + 1 by instruction i (lane l lands at
-    // 16 l), 16-byte column granule c of a row at granule c ^ (row & 7) of its
-    // LDS row, so the 16 rows one operand read touches fall in different banks;
-    // then B_p's tile, row l / 4, columns 4 (l % 4) ...  From the sequence's
-    // first map on: lane offsets fixed, the map offset (below 2^31: a sequence
-    // has at most 256 / H + 1 segments per head) a scalar.  Past the last map
-    // the copies re-read it.
-    const size_t mbase = ((size_t)first * H + h) * D * D;
-    const int mbytes = ((max(pn - 2, 0) * H) * D * D + D * D) * 4;
-    const __amdgpu_buffer_rsrc_t rM = __builtin_amdgcn_make_buffer_rsrc((void *)(tab.Mseg + mbase), 0, mbytes, BUF_RSRC3);
-    const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc((void *)(tab.Bseg + mbase), 0, mbytes, BUF_RSRC3);
-    const int wb = SCAN_WAVE_BYTES * w;
-    int vM[8];
+    if (copier) {
+        // All copies of the maps, for the eight compute waves' regions (a wave
+        // that issued its own stalled on the vector memory queue for about 1.4K
+        // of its step's 5.5K cycles).  Region r of a slot: M_p rows 16 r + 2 i,
+        // 16 r + 2 i + 1 by instruction i (lane l lands at 16 l), 16-byte column
+        // granule c of a row at granule c ^ (row & 7) of its LDS row, so the 16
+        // rows one operand read touches fall in different banks; then B_p's tile,
+        // row 16 r + l / 4, columns 16 cb + 4 (l % 4) ..  From the sequence's first
+        // map on: lane offsets fixed, the region and map offsets (below 2^31: a
+        // sequence has at most 256 / H + 1 segments per head) scalars.  Past the
+        // last map the copies re-read it.
+        const size_t mbase = ((size_t)first * H + h) * D * D;
+        const int mbytes = ((max(pn - 2, 0) * H) * D * D + D * D) * 4;
+        const __amdgpu_buffer_rsrc_t rM =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(tab.Mseg + mbase), 0, mbytes, BUF_RSRC3);
+        const __amdgpu_buffer_rsrc_t rB =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(tab.Bseg + mbase), 0, mbytes, BUF_RSRC3);
+        int vM[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int row = 2 * i + (l >> 5), c = (l & 31) ^ (row & 7);
-        vM[i] = (r0 + row) * D * 4 + 16 * c;
+        for (int i = 0; i < 8; ++i) {
+            const int row = 2 * i + (l >> 5), c = (l & 31) ^ (row & 7);
+            vM[i] = row * D * 4 + 16 * c;
+        }
+        const int vB = ((l >> 2) * D + 16 * cb) * 4 + 16 * (l & 3);
+        auto copy_map = [&](int p, char *slot) __attribute__((always_inline)) {
+            const int so = min(p, max(pn - 2, 0)) * H * D * D * 4;
+#pragma unroll 1
+            for (int r = 0; r < 8; ++r) {  // (a loop: unrolled, its scalar offsets spill)
+                char *dst = slot + SCAN_WAVE_BYTES * r;
+                const int sr = so + 16 * r * D * 4;
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rM, (lds_void *)(dst + 1024 * i), 16, vM[i], sr, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_void *)(dst + 8192), 16, vB, sr, 0, 0);
+            }
+        };
+        // Map p lands in its slot before the second barrier of step p; map p + 1
+        // is issued after it, into the other slot, which the compute waves read
+        // in step p - 1 (all of them are past the first barrier of step p).
+        auto copy_step = [&](int p, char *nxt) __attribute__((always_inline)) {
+            lds_barrier();
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): map p has landed
+            lds_barrier();
+            copy_map(p + 1, nxt);
+        };
+        copy_map(0, slot0);
+        for (int p = 0; p < pe; p += 2) {
+            copy_step(p, slot1);
+            copy_step(p + 1, slot0);
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no copy may land after the workgroup ends
+        return;
     }
-    const int vB = ((r0 + (l >> 2)) * D + 16 * cb) * 4 + 16 * (l & 3);
-    auto copy_map = [&](int p, char *slot) __attribute__((always_inline)) {
-        const int so = min(p, max(pn - 2, 0)) * H * D * D * 4;
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rM, (lds_void *)(slot + wb + 1024 * i), 16, vM[i], so, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_void *)(slot + wb + 8192), 16, vB, so, 0, 0);
-    };
-    auto step = [&](int p, char *slot) __attribute__((always_inline)) {
+    const int wb = SCAN_WAVE_BYTES * w;
+    auto step = [&](int p, const char *slot) __attribute__((always_inline)) {
         *(f32x4 *)&Ss[lr * 132 + r0 + 4 * g] = Sr;  // S_in[p]
         lds_barrier();
         F8 sb[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) sb[ks] = ld_f8(&Ss[lr * 132 + 32 * ks + 8 * g]);
-        lds_barrier();  // (its LDS wait also covers the reads of sb)
+        lds_barrier();  // (its LDS wait also covers the reads of sb; after it, map p has landed)
         // (Steps at p >= pn - 1 compute states nobody reads, from the last
         // map: no branch may come between the reads of sb above and their use,
         // or the compiler may sink them below the barrier.)
-        // This map's copies have landed; the next map's (issued a step ago) may run.
-        __builtin_amdgcn_s_waitcnt(0x0F70 | SCAN_COPIES);
         const char *mrow = slot + wb + 512 * lr;
         F8 mr[4];
 #pragma unroll
@@ -1464,9 +1489,6 @@ __global__ __launch_bounds__(SCAN_NT) void seg_scan_kernel(const float *__restri
         f32x4 a[4];
 #pragma unroll
         for (int m = 0; m < 4; ++m) a[0][m] = ((const float *)(slot + wb + 8192))[(4 * g + m) * 16 + lr];
-        // The slot is read: refill it with the map two steps on.
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-        copy_map(p + 2, slot);
         // One accumulator per 32-row block of M (chains of 8 products, not 32),
         // added at the end: with M = I exactly one partial is nonzero, so an
         // identity transition still gives the state bit for bit.
@@ -1477,13 +1499,10 @@ __global__ __launch_bounds__(SCAN_NT) void seg_scan_kernel(const float *__restri
 #pragma unroll
         for (int m = 0; m < 4; ++m) Sr[m] = (a[0][m] + a[1][m]) + (a[2][m] + a[3][m]);
     };
-    copy_map(0, slot0);
-    copy_map(1, slot1);
     for (int p = 0; p < pe; p += 2) {
         step(p, slot0);
         step(p + 1, slot1);
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no copy may land after the workgroup ends
 }
 
 // ------------------------------------------------------------------ host --
