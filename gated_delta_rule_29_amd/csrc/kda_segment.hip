@@ -1350,23 +1350,34 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
 // MFMA products (an identity transition reproduces the state bit for bit).
 // An empty sequence gets S_final = S0 here.
 //
-// Eight compute waves of 16 rows each (a step is 32 products per wave) and one
-// store wave.  A compute wave copies its own 16 rows of M_p and of B_p's 16
-// columns straight into LDS (9 KB) and reads nothing else of the maps, so it
-// waits only for its own copies: a slot is refilled with the map two steps on
-// as soon as the wave has read it, and two slots keep two maps in flight.
-// Loads and stores share the in-order vmcnt counter; the store wave, which
-// copies S_in[p] out of the exchange buffer, keeps the state stores off the
-// compute waves' counter.
+// Eight compute waves of 16 rows each (a step is 32 products per wave), one
+// store wave and one copy wave.  The copy wave moves every map straight into
+// LDS: per compute wave its 16 rows of M_p and the 16 x 16 tile of B_p (9 KB),
+// into one of two slots, a map ahead, so the compute waves issue no copies and
+// wait on no memory counter.  Loads and stores share the in-order vmcnt
+// counter; the store wave, which copies S_in[p] out of the exchange buffer,
+// keeps the state stores off the copy wave's counter too.  The exchange buffer
+// is doubled like the slots, so a step needs one barrier: step p writes
+// S_in[p] into exchange buffer p mod 2, passes the barrier, then reads it and
+// map p.  Buffer and slot p mod 2 are written again only in step p + 2, after
+// the barrier of step p + 1, which no wave passes before every wave has used
+// what it read in step p.
 constexpr int SCAN_NT = 640;                          // 8 compute waves, a store wave, a copy wave
 constexpr int SCAN_WAVE_BYTES = 9216;                 // 16 rows of M (swizzled), then the 16 x 16 tile of B
 constexpr int SCAN_SLOT_BYTES = 8 * SCAN_WAVE_BYTES;  // one map
+// Exchange buffer: S_in[p]^T, column c (16) by row r (128), the 16-byte granule
+// r / 4 of a column at granule (r / 4) ^ c of its LDS row, so that the 16
+// columns one access touches fall in different banks with no padding (two
+// slots and two buffers fill the 160 KB of LDS exactly).
+__device__ __forceinline__ int xs_at(int c, int r) { return 128 * c + 4 * ((r >> 2) ^ c) + (r & 3); }
 __global__ __launch_bounds__(SCAN_NT) void seg_scan_kernel(const float *__restrict__ S0, int N, int H, SegTable tab,
                                                            float *__restrict__ S_final) {
-    // Distinct arrays: a read of one provably does not alias a copy in flight into the other.
+    // Distinct arrays: a read of one provably does not alias a copy in flight
+    // into the other, or a write of the other exchange buffer.
     __shared__ __align__(16) char slot0[SCAN_SLOT_BYTES];
     __shared__ __align__(16) char slot1[SCAN_SLOT_BYTES];
-    __shared__ __align__(16) float Ss[16 * 132];  // S_in[p]^T [column][row]
+    __shared__ __align__(16) float xs0[16 * 128];
+    __shared__ __align__(16) float xs1[16 * 128];
     const int nh = blockIdx.x, cb = blockIdx.y;
     const int n = nh / H, h = nh % H;
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, g = l >> 4,
@@ -1387,25 +1398,29 @@ __global__ __launch_bounds__(SCAN_NT) void seg_scan_kernel(const float *__restri
     }
     // Steps run in pairs (one per slot), pn rounded up to even: an odd count
     // ends with a step whose state nobody stores.  Every wave passes the same
-    // number of barriers: two per step.
+    // number of barriers: one per step.
     const int pe = (pn + 1) & ~1;
     if (storer) {
         // Lane (row group l / 4, column quad l % 4) writes rows 16 k + l / 4,
         // k = 0..7, four columns each; all read before the first store, so the
-        // stores issue back to back.
-        for (int p = 0; p < pe; ++p) {
+        // stores issue back to back (and the reads have completed before the
+        // wave reaches the next barrier).
+        auto store_step = [&](int p, const float *xs) __attribute__((always_inline)) {
             lds_barrier();
             f32x4 x[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) x[k][i] = Ss[(4 * (l & 3) + i) * 132 + 16 * k + (l >> 2)];
-            lds_barrier();
+                for (int i = 0; i < 4; ++i) x[k][i] = xs[xs_at(4 * (l & 3) + i, 16 * k + (l >> 2))];
             if (p < pn) {
                 float *sin = tab.Sin + ((size_t)(first + p) * H + h) * D * D + 16 * cb + 4 * (l & 3);
 #pragma unroll
                 for (int k = 0; k < 8; ++k) *(f32x4 *)(sin + (size_t)(16 * k + (l >> 2)) * D) = x[k];
             }
+        };
+        for (int p = 0; p < pe; p += 2) {
+            store_step(p, xs0);
+            store_step(p + 1, xs1);
         }
         return;
     }
@@ -1418,8 +1433,7 @@ __global__ __launch_bounds__(SCAN_NT) void seg_scan_kernel(const float *__restri
         // rows one operand read touches fall in different banks; then B_p's tile,
         // row 16 r + l / 4, columns 16 cb + 4 (l % 4) ..  From the sequence's first
         // map on: lane offsets fixed, the region and map offsets (below 2^31: a
-        // sequence has at most 256 / H + 1 segments per head) scalars.  Past the
-        // last map the copies re-read it.
+        // sequence has at most 256 / H + 1 segments per head) scalars.
         const size_t mbase = ((size_t)first * H + h) * D * D;
         const int mbytes = ((max(pn - 2, 0) * H) * D * D + D * D) * 4;
         const __amdgpu_buffer_rsrc_t rM =
@@ -1434,9 +1448,9 @@ __global__ __launch_bounds__(SCAN_NT) void seg_scan_kernel(const float *__restri
         }
         const int vB = ((l >> 2) * D + 16 * cb) * 4 + 16 * (l & 3);
         auto copy_map = [&](int p, char *slot) __attribute__((always_inline)) {
-            const int so = min(p, max(pn - 2, 0)) * H * D * D * 4;
+            const int so = p * H * D * D * 4;
 #pragma unroll 1
-            for (int r = 0; r < 8; ++r) {  // (a loop: unrolled, its scalar offsets spill)
+            for (int r = 0; r < 8; ++r) {
                 char *dst = slot + SCAN_WAVE_BYTES * r;
                 const int sr = so + 16 * r * D * 4;
 #pragma unroll
@@ -1445,16 +1459,16 @@ __global__ __launch_bounds__(SCAN_NT) void seg_scan_kernel(const float *__restri
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_void *)(dst + 8192), 16, vB, sr, 0, 0);
             }
         };
-        // Map p lands in its slot before the second barrier of step p; map p + 1
-        // is issued after it, into the other slot, which the compute waves read
-        // in step p - 1 (all of them are past the first barrier of step p).
+        // Map p has landed before the barrier of step p; map p + 1 is issued
+        // after it, into the other slot, which the compute waves read in step
+        // p - 1 (all of them have used those reads before reaching this barrier).
+        // Step q reads map q only while q + 1 < pn.
         auto copy_step = [&](int p, char *nxt) __attribute__((always_inline)) {
-            lds_barrier();
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): map p has landed
             lds_barrier();
-            copy_map(p + 1, nxt);
+            if (p + 2 < pn) copy_map(p + 1, nxt);
         };
-        copy_map(0, slot0);
+        if (pn >= 2) copy_map(0, slot0);
         for (int p = 0; p < pe; p += 2) {
             copy_step(p, slot1);
             copy_step(p + 1, slot0);
@@ -1463,16 +1477,21 @@ __global__ __launch_bounds__(SCAN_NT) void seg_scan_kernel(const float *__restri
         return;
     }
     const int wb = SCAN_WAVE_BYTES * w;
-    auto step = [&](int p, const char *slot) __attribute__((always_inline)) {
-        *(f32x4 *)&Ss[lr * 132 + r0 + 4 * g] = Sr;  // S_in[p]
-        lds_barrier();
+    auto step = [&](int p, const char *slot, float *xs) __attribute__((always_inline)) {
+        *(f32x4 *)&xs[xs_at(lr, r0 + 4 * g)] = Sr;  // S_in[p]
+        lds_barrier();  // every wave's rows of S_in[p], and map p, are in LDS
+        if (p + 1 >= pn) return;  // S_in[pn] is not needed (pass B forms S_final); there is no map p
         F8 sb[4];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) sb[ks] = ld_f8(&Ss[lr * 132 + 32 * ks + 8 * g]);
-        lds_barrier();  // (its LDS wait also covers the reads of sb; after it, map p has landed)
-        // (Steps at p >= pn - 1 compute states nobody reads, from the last
-        // map: no branch may come between the reads of sb above and their use,
-        // or the compiler may sink them below the barrier.)
+        for (int ks = 0; ks < 4; ++ks) {
+            const f32x4 lo = *(const f32x4 *)&xs[xs_at(lr, 32 * ks + 8 * g)];
+            const f32x4 hi = *(const f32x4 *)&xs[xs_at(lr, 32 * ks + 8 * g + 4)];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sb[ks].v[e] = lo[e];
+                sb[ks].v[4 + e] = hi[e];
+            }
+        }
         const char *mrow = slot + wb + 512 * lr;
         F8 mr[4];
 #pragma unroll
@@ -1500,8 +1519,8 @@ __global__ __launch_bounds__(SCAN_NT) void seg_scan_kernel(const float *__restri
         for (int m = 0; m < 4; ++m) Sr[m] = (a[0][m] + a[1][m]) + (a[2][m] + a[3][m]);
     };
     for (int p = 0; p < pe; p += 2) {
-        step(p, slot0);
-        step(p + 1, slot1);
+        step(p, slot0, xs0);
+        step(p + 1, slot1, xs1);
     }
 }
 
