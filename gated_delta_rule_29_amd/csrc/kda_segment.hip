@@ -863,8 +863,9 @@ constexpr int CH_NT = 64 * CH_NW;
 // form for an access of both memory and LDS, and while one is in flight it
 // waits for every LDS read to complete before the first use of any.
 // With `bytes` = 0 nothing is read and the copy writes zeros: issuing it
-// anyway keeps the number of copies in flight the same at every step.
-template <bool PASS_A, int NW>
+// anyway keeps the number of copies in flight the same at every step.  AUX is
+// the loads' cache policy (2: non-temporal).
+template <bool PASS_A, int NW, int AUX = 0>
 __device__ __forceinline__ void chain_dma(const char *__restrict__ blk, int bytes, char *lds, int wv, int l) {
     using Lo = ChainLds<PASS_A>;
     constexpr int NKB = Lo::GM / 1024;
@@ -875,13 +876,13 @@ __device__ __forceinline__ void chain_dma(const char *__restrict__ blk, int byte
         if (kb < NKB) {
             const int x = 1024 * kb;
             const int src = (PASS_A && x >= Lo::KT) ? BO_KT + (x - Lo::KT) : x;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(lds + x), 16, src + 16 * l, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(lds + x), 16, src + 16 * l, 0, 0, AUX);
         }
     }
     // gamma (512 B) by every wave, so that each issues the same number of
     // copies: the waves write the same values, and lanes 32-63 read past the
     // block (zeros) into padding.
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(lds + Lo::GM), 16, BO_GM + 16 * l, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(lds + Lo::GM), 16, BO_GM + 16 * l, 0, 0, AUX);
 }
 
 // One workgroup (8 waves) per (segment, head).  Pass A: wave w owns columns
@@ -896,7 +897,11 @@ __device__ __forceinline__ void chain_dma(const char *__restrict__ blk, int byte
 // G2 workgroups (G2 a multiple of 8, so that the two workgroups of a pair land
 // on one XCD and share its L2); the fused output step (which needs a row's 128
 // values in one workgroup) is not split.
-template <bool PASS_A, int NBA = CHAIN_NBUF_A, bool SPLIT = false>
+// STREAM (pass B): the block's loads, its last reads, carry the non-temporal
+// hint.  The host sets it when the blocks exceed the 256 MB Infinity Cache:
+// at 64K x 16 (1.29 GB of blocks) pass B then took 0.312 ms against 0.338,
+// while at 2K x 16 (40 MB, served from the cache) the hint cost 3 us.
+template <bool PASS_A, int NBA = CHAIN_NBUF_A, bool SPLIT = false, bool STREAM = false>
 __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void seg_chain_kernel(
     int N, int H, SegTable tab, float *__restrict__ o, float *__restrict__ S_final) {
     using Lo = ChainLds<PASS_A>;
@@ -918,6 +923,7 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     // Image-copy instructions one wave issues per chunk in pass A (its 32 KB
     // over the waves, and gamma).
     constexpr int DMA_OPS = (32 + NW - 1) / NW + 1;
+    constexpr int AUX = STREAM ? 2 : 0;  // cache policy of the block's loads
     static_assert(!SPLIT || NBA == 2 || DMA_OPS < 16, "vmcnt immediate");
 
     // Workgroup i takes head i mod H of the pass's (i / H)-th segment: the
@@ -989,11 +995,11 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
                 // lane part as the register offset, the tile part (wave-uniform) as the scalar one
                 const int tile = 8 * rt + utile + ct;
                 const u32x2 qq = __builtin_bit_cast(
-                    u32x2, __builtin_amdgcn_raw_buffer_load_b64(ru, 8 * l, BO_U + U_TILE * tile, 0));
+                    u32x2, __builtin_amdgcn_raw_buffer_load_b64(ru, 8 * l, BO_U + U_TILE * tile, AUX));
                 u[rt][ct].q01 = qq[0];
                 u[rt][ct].q23 = qq[1];
                 u[rt][ct].sc =
-                    __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ru, 4 * g, BO_US + 16 * tile, 0));
+                    __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ru, 4 * g, BO_US + 16 * tile, AUX));
             }
     };
     // A full state (this wave's columns) to dst [128][128]: buffer stores with
@@ -1104,7 +1110,7 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     // next one.  Issue order (U of chunk n + 1, then the image of chunk
     // n + NBUF - 1) lets a step wait for everything but the newest image.
     auto dma = [&](int chunk, char *lds) __attribute__((always_inline)) {
-        chain_dma<PASS_A, NW>(blk0 + (size_t)chunk * bstride, chunk < cend ? (int)BLK : 0, lds, wv, l);
+        chain_dma<PASS_A, NW, AUX>(blk0 + (size_t)chunk * bstride, chunk < cend ? (int)BLK : 0, lds, wv, l);
     };
     if (cbeg < cend) {
         dma(cbeg, buf0);
@@ -1625,6 +1631,8 @@ int launch_segment_prefill(const __bf16 *q, const __bf16 *k, const __bf16 *v, co
         pairsA = (int64_t)B * (segs - 1) * H;
     }
     const bool splitA = 2 * pairsA <= ncu, splitB = 2 * pairsB <= ncu && ly.gate == nullptr;
+    // Pass B streams the blocks (non-temporal loads) once they exceed the Infinity Cache.
+    const bool streamB = (size_t)ncm * H * BLK > ((size_t)256 << 20);
     const dim3 cgrid((unsigned)(nsm * H));
     const dim3 sgrid((unsigned)(2 * ((nsm * H + 7) / 8 * 8)));  // two halves, each a multiple of 8
     if (L % CHAIN_UNROLL_A == 0) {
@@ -1646,6 +1654,9 @@ int launch_segment_prefill(const __bf16 *q, const __bf16 *k, const __bf16 *v, co
     if (ev && hipEventRecord(ev[4], stream) != hipSuccess) return -1;
     if (splitB)
         hipLaunchKernelGGL((seg_chain_kernel<false, CHAIN_NBUF_A, true>), sgrid, dim3(CH_NT / 2), 0, stream, N, H,
+                           tab, o, S_final);
+    else if (streamB)
+        hipLaunchKernelGGL((seg_chain_kernel<false, CHAIN_NBUF_A, false, true>), cgrid, dim3(CH_NT), 0, stream, N, H,
                            tab, o, S_final);
     else
         hipLaunchKernelGGL(seg_chain_kernel<false>, cgrid, dim3(CH_NT), 0, stream, N, H, tab, o, S_final);
