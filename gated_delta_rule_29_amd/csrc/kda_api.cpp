@@ -88,7 +88,7 @@ KDA_EXPORT const char *kda_status_str(int status) {
 KDA_EXPORT int kda_version(void) { return 100; }
 
 KDA_EXPORT size_t kda_chunk_fwd_workspace_bytes(int64_t T_total, int32_t n_seqs, int32_t H, kda_dtype qkv_dtype) {
-    if (T_total < 0 || n_seqs < 0 || H < 0) return 0;
+    if (T_total < 0 || n_seqs < 0 || H < 0 || H > KDA_MAX_HEADS) return 0;
     if (qkv_dtype != KDA_BF16 && qkv_dtype != KDA_F32) return 0;
     if (T_total == 0 && n_seqs == 0) return 0;
     return kda::prefill_workspace_bytes(T_total, n_seqs, H, qkv_dtype == KDA_F32);
@@ -103,7 +103,7 @@ int chunk_fwd(const void *q, const void *k, const void *v, kda_dtype qkv_dtype, 
               size_t workspace_bytes, void *stream, void *const *stage_events, float *S_ckpt, int64_t ckpt_stride,
               int64_t ckpt_capacity, const kda_layer_opts *lo) {
     if (dk != kD || dv != kD) return KDA_ERR_SHAPE;
-    if (B < 0 || T < 0 || H < 0 || n_seqs < 0) return KDA_ERR_SHAPE;
+    if (B < 0 || T < 0 || H < 0 || H > KDA_MAX_HEADS || n_seqs < 0) return KDA_ERR_SHAPE;
     if (qkv_dtype != KDA_BF16 && qkv_dtype != KDA_F32) return KDA_ERR_DTYPE;
     if (cu_seqlens) {
         if (B != 1 || n_seqs < 1) return KDA_ERR_SEQLENS;

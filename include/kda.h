@@ -77,6 +77,13 @@ enum {
     KDA_ERR_ALIAS = -8      /* o overlaps an input                                 */
 };
 
+/*
+ * Largest head count the prefill entry points accept (KDA_ERR_SHAPE above it;
+ * the workspace size is then 0).  A chunk's rows of one input span
+ * 64 x H x 512 bytes, which the kernels address with 32-bit buffer offsets.
+ */
+#define KDA_MAX_HEADS 16384
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *kda_status_str(int status);
 

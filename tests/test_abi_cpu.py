@@ -53,6 +53,8 @@ def test_workspace_size():
         assert a > 0 and b >= a
         assert lib.kda_chunk_fwd_workspace_bytes(64, 1, 2, dt) > lib.kda_chunk_fwd_workspace_bytes(64, 1, 1, dt)
     assert lib.kda_chunk_fwd_workspace_bytes(64, 1, 1, 9) == 0
+    assert lib.kda_chunk_fwd_workspace_bytes(64, 1, 16384, 0) > 0  # KDA_MAX_HEADS
+    assert lib.kda_chunk_fwd_workspace_bytes(64, 1, 16385, 0) == 0
     # both paths keep one block of chain operands per (chunk, head): the size grows with ceil(T/64) + N
     for dt in (0, 1):
         assert lib.kda_chunk_fwd_workspace_bytes(65, 1, 1, dt) > lib.kda_chunk_fwd_workspace_bytes(64, 1, 1, dt)
@@ -86,7 +88,7 @@ def call_prefill(a):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(dk=64), SHAPE), (dict(dv=256), SHAPE), (dict(T=-1), SHAPE), (dict(H=-2), SHAPE),
-    (dict(dtype=7), DTYPE),
+    (dict(H=16385), SHAPE), (dict(dtype=7), DTYPE),
     (dict(q=None), NULL), (dict(k=None), NULL), (dict(v=None), NULL), (dict(z=None), NULL),
     (dict(beta=None), NULL), (dict(A=None), NULL), (dict(o=None), NULL),
     (dict(N=2), SEQLENS), (dict(cu=fake(11), B=2, N=2), SEQLENS), (dict(cu=fake(11), N=0), SEQLENS),
