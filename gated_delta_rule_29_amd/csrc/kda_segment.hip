@@ -787,15 +787,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GK == GATE_
 // ---------------------------------------------------------------- chain --
 
 // LDS image of one chunk's operands in the chain passes (double-buffered).
+// Pass A's image also holds U and its block scales, ahead of gamma in the
+// block's own order, so that one 1 KB copy moves both (pass B, whose two
+// images and output-step buffers fill the LDS, loads U into registers).
 template <bool PASS_A>
 struct ChainLds {
     static constexpr int W = 0;
     static constexpr int QT = 16384;                 // pass B only
     static constexpr int KT = PASS_A ? 16384 : 32768;
     static constexpr int AQ = 49152;                 // pass B only
-    static constexpr int GM = PASS_A ? 32768 : 61440;
-    static constexpr int BYTES = GM + 1024;  // gamma, then padding
+    static constexpr int U = 32768;                  // pass A only
+    static constexpr int US = 49152;                 // pass A only: U scales, then gamma
+    static constexpr int GM = PASS_A ? US + (BO_GM - BO_US) : 61440;
+    static constexpr int BYTES = PASS_A ? US + 1024 : GM + 1024;  // gamma, then padding
 };
+static_assert(BO_GM - BO_US == 512 && BLK == BO_GM + 512, "U scales and gamma end the block");
 
 // The operand stream of one chain step.  Pass A: 16 W tiles (k-step s
 // outermost), 8 gamma rows, 16 K~^T tiles; pass B: 16 (W, Q~) tile pairs, the
@@ -838,12 +844,6 @@ struct ChainTiles {
 #ifndef CHAIN_RING_B
 #define CHAIN_RING_B 6
 #endif
-#ifndef CHAIN_NBUF_A
-#define CHAIN_NBUF_A 3
-#endif
-// Pass A's loop body: a common multiple of its image count and the two U
-// register sets.  The segment length L is a multiple of it.
-constexpr int CHAIN_UNROLL_A = CHAIN_NBUF_A == 3 ? 6 : 2;
 
 // o is written once and never read here: streaming stores leave fewer dirty
 // lines in the caches for the work that follows (the decode step after a 64K
@@ -868,28 +868,31 @@ constexpr int CH_NT = 64 * CH_NW;
 template <bool PASS_A, int NW, int AUX = 0>
 __device__ __forceinline__ void chain_dma(const char *__restrict__ blk, int bytes, char *lds, int wv, int l) {
     using Lo = ChainLds<PASS_A>;
-    constexpr int NKB = Lo::GM / 1024;
+    constexpr int NKB = PASS_A ? Lo::US / 1024 : Lo::GM / 1024;
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void *)blk, 0, bytes, BUF_RSRC3);
 #pragma unroll
     for (int i = 0; i < (NKB + NW - 1) / NW; ++i) {
         const int kb = wv + NW * i;
         if (kb < NKB) {
             const int x = 1024 * kb;
-            const int src = (PASS_A && x >= Lo::KT) ? BO_KT + (x - Lo::KT) : x;
+            // pass A: W, K~^T, U from their block offsets
+            const int src = !PASS_A || x < Lo::KT ? x : x < Lo::U ? BO_KT + (x - Lo::KT) : BO_U + (x - Lo::U);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(lds + x), 16, src + 16 * l, 0, 0, AUX);
         }
     }
-    // gamma (512 B) by every wave, so that each issues the same number of
-    // copies: the waves write the same values, and lanes 32-63 read past the
-    // block (zeros) into padding.
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(lds + Lo::GM), 16, BO_GM + 16 * l, 0, 0, AUX);
+    // The block's last KB by every wave, so that each issues the same number
+    // of copies (the waves write the same values): pass A, U's scales and
+    // gamma; pass B, gamma, whose lanes 32-63 read past the block (zeros)
+    // into padding.
+    if constexpr (PASS_A)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(lds + Lo::US), 16, BO_US + 16 * l, 0, 0, AUX);
+    else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(lds + Lo::GM), 16, BO_GM + 16 * l, 0, 0, AUX);
 }
 
 // One workgroup (8 waves) per (segment, head).  Pass A: wave w owns columns
 // 32w .. 32w+31 of X = [M | B] (waves 0-3: M, from I; waves 4-7: B, from 0, with
 // U); pass B: wave w owns value columns 16w .. 16w+15 of the state.
-// NBA: pass A's image count, 3 (a six-step loop body, segments a multiple of
-// 6 chunks) or 2 (a two-step body, any even segment length).
 // SPLIT: for inputs with fewer (segment, head) pairs than half the CUs, two
 // workgroups per pair, each with half of the columns, so that twice as many
 // CUs share the work: pass A's eight waves take 16 columns each of M or of B,
@@ -901,17 +904,17 @@ __device__ __forceinline__ void chain_dma(const char *__restrict__ blk, int byte
 // hint.  The host sets it when the blocks exceed the 256 MB Infinity Cache:
 // at 64K x 16 (1.29 GB of blocks) pass B then took 0.312 ms against 0.338,
 // while at 2K x 16 (40 MB, served from the cache) the hint cost 3 us.
-template <bool PASS_A, int NBA = CHAIN_NBUF_A, bool SPLIT = false, bool STREAM = false>
+template <bool PASS_A, bool SPLIT = false, bool STREAM = false>
 __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void seg_chain_kernel(
     int N, int H, SegTable tab, float *__restrict__ o, float *__restrict__ S_final) {
     using Lo = ChainLds<PASS_A>;
-    // Pass A rotates three LDS images (its image is small), pass B two.
+    // Two LDS images: the copy of the next chunk's runs during a step.
     // Distinct arrays (not one array indexed by step): a read of one then
-    // provably does not alias a copy in flight into another.
-    constexpr int NBUF = PASS_A ? NBA : 2;
+    // provably does not alias a copy in flight into the other.  (Pass A with
+    // three images, each copy issued two steps ahead, took the same time.)
+    constexpr int NBUF = 2;
     __shared__ __align__(16) char buf0[Lo::BYTES];
     __shared__ __align__(16) char buf1[Lo::BYTES];
-    __shared__ __align__(16) char buf2[NBUF == 3 ? Lo::BYTES : 16];
     // Fused output step of pass B (see store_o): per-row partial sums of
     // squares [parity][wave][row], and each wave's gate tile [wave][row][16].
     __shared__ __align__(16) float opart[PASS_A ? 4 : 2 * CH_NW * CH];
@@ -920,11 +923,7 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     // eight waves with one tile each, pass B runs four.
     constexpr int NCT = PASS_A && !SPLIT ? 2 : 1;
     constexpr int NW = SPLIT && !PASS_A ? 4 : CH_NW;
-    // Image-copy instructions one wave issues per chunk in pass A (its 32 KB
-    // over the waves, and gamma).
-    constexpr int DMA_OPS = (32 + NW - 1) / NW + 1;
     constexpr int AUX = STREAM ? 2 : 0;  // cache policy of the block's loads
-    static_assert(!SPLIT || NBA == 2 || DMA_OPS < 16, "vmcnt immediate");
 
     // Workgroup i takes head i mod H of the pass's (i / H)-th segment: the
     // workgroups with work come first and in one block, so they spread evenly
@@ -984,8 +983,12 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     int E = 0;
 
     // Past the segment's last chunk the copies read nothing (and U is 0).
+    // Pass B loads U into registers one step ahead; pass A reads it from the
+    // chunk's LDS image at the start of the step that uses it (with register
+    // loads one step ahead, pass A took 0.202 against 0.192 ms at 64K x 16).
     using UReg = UBlk;  // as stored: decoded at the start of the step that uses it
     auto load_u = [&](int chunk, UReg (&u)[4][NCT]) {
+        if constexpr (PASS_A) return;
         const __amdgpu_buffer_rsrc_t ru = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(blk0 + (size_t)chunk * bstride), 0, chunk < cend ? u_records : 0, BUF_RSRC3);
 #pragma unroll
@@ -1106,19 +1109,14 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     f32x4 O[4];
     int64_t t0_prev = 0;
     int len_prev = 0;
-    // Copies in flight: the images of the next NBUF - 1 chunks and the U of the
-    // next one.  Issue order (U of chunk n + 1, then the image of chunk
-    // n + NBUF - 1) lets a step wait for everything but the newest image.
+    // Copies in flight during a step: the image of the next chunk (and, in
+    // pass B, its U).
     auto dma = [&](int chunk, char *lds) __attribute__((always_inline)) {
         chain_dma<PASS_A, NW, AUX>(blk0 + (size_t)chunk * bstride, chunk < cend ? (int)BLK : 0, lds, wv, l);
     };
     if (cbeg < cend) {
         dma(cbeg, buf0);
         load_u(cbeg, ua);
-        // Keep the two copies in issue order: the first step waits for the
-        // older one only.
-        __builtin_amdgcn_sched_barrier(0);
-        if (NBUF == 3) dma(cbeg + 1, buf1);
     }
 
     // One chain step on the image in `cur` (Delta accumulates into Dl, which
@@ -1126,12 +1124,11 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     // step read) and `un`.
     auto step = [&](int chunk, const char *cur, char *nxt, UReg (&Dcur)[4][NCT], UReg (&un)[4][NCT])
                     __attribute__((always_inline)) {
-        // This wave's copies of this chunk and its U have landed (waits in a
-        // form the compiler sees, so it adds none of its own for them), then
-        // every wave's have, and `nxt` is free.  With three images the newest
-        // copy (at most DMA_OPS instructions of this wave) may still run.
-        // (Pass B also waits for its LDS writes: the output-step partials.)
-        __builtin_amdgcn_s_waitcnt(PASS_A ? 0x0F70 | (NBUF == 3 ? DMA_OPS : 0) : 0x0070);
+        // This wave's copies of this chunk (and its U) have landed (waits in
+        // a form the compiler sees, so it adds none of its own for them), then
+        // every wave's have, and `nxt` is free.  (Pass B also waits for its
+        // LDS writes: the output-step partials.)
+        __builtin_amdgcn_s_waitcnt(PASS_A ? 0x0F70 : 0x0070);
         // The barrier is a bare s_barrier between compiler-only fences: the
         // waits above are the only memory ordering needed (no wave writes LDS
         // but by these copies, and every LDS read of the previous step has
@@ -1140,6 +1137,23 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __builtin_amdgcn_s_barrier();
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if constexpr (PASS_A) {  // this chunk's U, from its image (the waves of M have none)
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) {
+                    const int tile = 8 * rt + utile + ct;
+                    if (colw >= 128) {
+                        const u32x2 qq = *(const u32x2 *)(cur + Lo::U + U_TILE * tile + 8 * l);
+                        Dcur[rt][ct].q01 = qq[0];
+                        Dcur[rt][ct].q23 = qq[1];
+                        Dcur[rt][ct].sc = *(const float *)(cur + Lo::US + 16 * tile + 4 * g);
+                    } else {
+                        Dcur[rt][ct].q01 = Dcur[rt][ct].q23 = 0u;
+                        Dcur[rt][ct].sc = 0.f;
+                    }
+                }
+        }
         // The step's scale: e bounds max(|X|, |U 2^E|) by 2^(e - 126) (fp32
         // exponent fields; |U| < 2^14 sc in its block format).  Inf or NaN
         // present: keep E, the result is not finite either way.
@@ -1293,12 +1307,10 @@ __global__ __launch_bounds__(CH_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
         }
     };
     // Unrolled so that every step's image and U set are fixed arrays.
-    constexpr int UNROLL = PASS_A && NBUF == 3 ? 6 : 2;
+    constexpr int UNROLL = 2;
     auto buf = [&](auto ic) -> char * {
-        constexpr int b = decltype(ic)::value % NBUF;
-        if constexpr (b == 0) return buf0;
-        else if constexpr (b == 1) return buf1;
-        else return buf2;
+        if constexpr (decltype(ic)::value % NBUF == 0) return buf0;
+        else return buf1;
     };
     for (int chunk = cbeg; chunk < cend; chunk += UNROLL) {
         static_for<UNROLL>([&](auto ic) __attribute__((always_inline)) {
@@ -1541,11 +1553,8 @@ constexpr int SEG_TARGET_WGS = 256;  // chain workgroups in flight: one per CU (
 #define SEG_L_MIN 4
 #endif
 // Chunks per segment: about SEG_TARGET_WGS (segment, head) pairs in all,
-// rounded up to even (a whole number of two-step pass-A loop bodies; the
-// three-image pass A runs when L is also a multiple of 6).  Its steps take the
-// same time with two images as with three, so L is not rounded further: at
-// 64K x 16, L = 64 (16 equal segments per head) ran pass A in 0.202 ms against
-// 0.209 ms with L = 66.
+// rounded up to even (a whole number of two-step pass-A loop bodies): at
+// 64K x 16, L = 64 (16 equal segments per head).
 static inline int seg_len(int64_t T_total, int H) {
     const int64_t nc = (T_total + CH - 1) / CH;
     const int64_t per_head = SEG_TARGET_WGS / (H > 0 ? H : 1) > 0 ? SEG_TARGET_WGS / H : 1;
@@ -1635,29 +1644,19 @@ int launch_segment_prefill(const __bf16 *q, const __bf16 *k, const __bf16 *v, co
     const bool streamB = (size_t)ncm * H * BLK > ((size_t)256 << 20);
     const dim3 cgrid((unsigned)(nsm * H));
     const dim3 sgrid((unsigned)(2 * ((nsm * H + 7) / 8 * 8)));  // two halves, each a multiple of 8
-    if (L % CHAIN_UNROLL_A == 0) {
-        if (splitA)
-            hipLaunchKernelGGL((seg_chain_kernel<true, CHAIN_NBUF_A, true>), sgrid, dim3(CH_NT), 0, stream, N, H,
-                               tab, o, S_final);
-        else
-            hipLaunchKernelGGL((seg_chain_kernel<true, CHAIN_NBUF_A>), cgrid, dim3(CH_NT), 0, stream, N, H, tab, o,
-                               S_final);
-    } else {
-        if (splitA)
-            hipLaunchKernelGGL((seg_chain_kernel<true, 2, true>), sgrid, dim3(CH_NT), 0, stream, N, H, tab, o,
-                               S_final);
-        else
-            hipLaunchKernelGGL((seg_chain_kernel<true, 2>), cgrid, dim3(CH_NT), 0, stream, N, H, tab, o, S_final);
-    }
+    if (splitA)
+        hipLaunchKernelGGL((seg_chain_kernel<true, true>), sgrid, dim3(CH_NT), 0, stream, N, H, tab, o, S_final);
+    else
+        hipLaunchKernelGGL((seg_chain_kernel<true>), cgrid, dim3(CH_NT), 0, stream, N, H, tab, o, S_final);
     if (ev && hipEventRecord(ev[3], stream) != hipSuccess) return -1;
     hipLaunchKernelGGL(seg_scan_kernel, dim3((unsigned)(N * H), 8), dim3(SCAN_NT), 0, stream, S0, N, H, tab, S_final);
     if (ev && hipEventRecord(ev[4], stream) != hipSuccess) return -1;
     if (splitB)
-        hipLaunchKernelGGL((seg_chain_kernel<false, CHAIN_NBUF_A, true>), sgrid, dim3(CH_NT / 2), 0, stream, N, H,
-                           tab, o, S_final);
+        hipLaunchKernelGGL((seg_chain_kernel<false, true>), sgrid, dim3(CH_NT / 2), 0, stream, N, H, tab, o,
+                           S_final);
     else if (streamB)
-        hipLaunchKernelGGL((seg_chain_kernel<false, CHAIN_NBUF_A, false, true>), cgrid, dim3(CH_NT), 0, stream, N, H,
-                           tab, o, S_final);
+        hipLaunchKernelGGL((seg_chain_kernel<false, false, true>), cgrid, dim3(CH_NT), 0, stream, N, H, tab, o,
+                           S_final);
     else
         hipLaunchKernelGGL(seg_chain_kernel<false>, cgrid, dim3(CH_NT), 0, stream, N, H, tab, o, S_final);
     if (hipGetLastError() != hipSuccess) return -1;
