@@ -55,13 +55,15 @@ def _unit_rows(x: np.ndarray) -> np.ndarray:
     return (x / np.maximum(n, np.float32(1e-30))).astype(np.float32)
 
 
-def _token_block(seed, tensor, t0, t1, H, D, scale=1.0):
-    """Rows [t0, t1) of a [T, H, D] standard-normal tensor built from 4096-token slices."""
+def _token_block(seed, tensor, t0, t1, H, D, scale=1.0, slice_tokens=SLICE):
+    """Rows [t0, t1) of a [T, H, D] standard-normal tensor built from slices of slice_tokens tokens
+    (4096 by default; a short input over many heads may take a shorter slice, which draws fewer
+    values and gives a different, equally seeded stream)."""
     out = np.empty((t1 - t0, H, D), dtype=np.float32)
-    s0, s1 = t0 // SLICE, (t1 - 1) // SLICE
+    s0, s1 = t0 // slice_tokens, (t1 - 1) // slice_tokens
     for s in range(s0, s1 + 1):
-        a, b = s * SLICE, (s + 1) * SLICE
-        full = rng(seed, tensor, s).standard_normal((SLICE, H, D), dtype=np.float32)
+        a, b = s * slice_tokens, (s + 1) * slice_tokens
+        full = rng(seed, tensor, s).standard_normal((slice_tokens, H, D), dtype=np.float32)
         lo, hi = max(a, t0), min(b, t1)
         out[lo - t0:hi - t0] = full[lo - a:hi - a]
     if scale != 1.0:
@@ -70,17 +72,18 @@ def _token_block(seed, tensor, t0, t1, H, D, scale=1.0):
 
 
 def prefill_tokens(seed: int, t0: int, t1: int, H: int, dtype: str = "bf16",
-                   z_scale: float = 1.0, D: int = 128) -> dict:
+                   z_scale: float = 1.0, D: int = 128, slice_tokens: int = SLICE) -> dict:
     """Token rows [t0, t1) of the packed [T_total, H, D] inputs (q, k, v, z, beta)."""
-    q = _unit_rows(_token_block(seed, "q", t0, t1, H, D))
-    k = _unit_rows(_token_block(seed, "k", t0, t1, H, D))
-    v = _token_block(seed, "v", t0, t1, H, D)
+    st = slice_tokens
+    q = _unit_rows(_token_block(seed, "q", t0, t1, H, D, slice_tokens=st))
+    k = _unit_rows(_token_block(seed, "k", t0, t1, H, D, slice_tokens=st))
+    v = _token_block(seed, "v", t0, t1, H, D, slice_tokens=st)
     if dtype == "bf16":
         q, k, v = bf16_round(q), bf16_round(k), bf16_round(v)
     elif dtype != "f32":
         raise ValueError(dtype)
-    z = _token_block(seed, "z", t0, t1, H, D, scale=z_scale)
-    bl = _token_block(seed, "beta", t0, t1, H, 1)[..., 0]
+    z = _token_block(seed, "z", t0, t1, H, D, scale=z_scale, slice_tokens=st)
+    bl = _token_block(seed, "beta", t0, t1, H, 1, slice_tokens=st)[..., 0]
     beta = (1.0 / (1.0 + np.exp(-bl.astype(np.float64)))).astype(np.float32)
     return {"q": q, "k": k, "v": v, "z": z, "beta": beta}
 
@@ -97,8 +100,8 @@ def initial_state(seed: int, N: int, H: int, std: float, D: int = 128):
 
 
 def prefill_inputs(seed: int, T_total: int, H: int, dtype: str = "bf16", z_scale: float = 1.0,
-                   s0_std: float = 0.0, n_seqs: int = 1, D: int = 128) -> dict:
-    d = prefill_tokens(seed, 0, T_total, H, dtype, z_scale, D)
+                   s0_std: float = 0.0, n_seqs: int = 1, D: int = 128, slice_tokens: int = SLICE) -> dict:
+    d = prefill_tokens(seed, 0, T_total, H, dtype, z_scale, D, slice_tokens)
     d["A"] = head_params(seed, H)
     d["S0"] = initial_state(seed, n_seqs, H, s0_std, D)
     return d
