@@ -268,7 +268,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GK == GATE_
     const __amdgpu_buffer_rsrc_t rwz = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(tab.ly.zw + (LRZ ? (size_t)h * D * zr : 0)), 0, LRZ ? D * zr2 : 0, BUF_RSRC3);
     f32x4 zc[2][4];
+    // A wave issues its global loads at raised priority (s_setprio 3, back to 0
+    // after the issue), so the arbiter lets it get its loads out ahead of the
+    // other waves' VALU work: 0.547 -> 0.537 ms at 64K x 16.
+    __builtin_amdgcn_s_setprio(3);
     load_half(0);  // the first half's k loads are in flight during the projection
+    __builtin_amdgcn_s_setprio(0);
     if constexpr (LRZ) {
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
@@ -324,7 +329,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GK == GATE_
     for (int hf = 0; hf < 2; ++hf) {
         if (hf) {
             __syncthreads();  // the Gram half before is done with E1 and CB
+            __builtin_amdgcn_s_setprio(3);
             load_half(1);
+            __builtin_amdgcn_s_setprio(0);
         }
         __builtin_amdgcn_sched_barrier(0);
         const int ch = 64 * hf + 16 * w + lr, chl = 16 * w + lr;
@@ -479,8 +486,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GK == GATE_
                 const int ks = 2 * hf + kh;
                 const int c0 = 32 * ks + 4 * g, cl = 32 * kh + 4 * g;  // global / in-half channel
                 const int ro = r * ph + 2 * c0;                         // rows past the end read as 0
+                __builtin_amdgcn_s_setprio(3);
                 const bf16x4 k0 = ld_bf16x4(rk, ro), k1 = ld_bf16x4(rk, ro + 32);
                 const bf16x4 q0 = ld_bf16x4(rq, ro), q1 = ld_bf16x4(rq, ro + 32);
+                __builtin_amdgcn_s_setprio(0);
                 f32x4 ea = *(const f32x4 *)&sm.a.E1[r * PEH + cl], eb = *(const f32x4 *)&sm.a.E1[r * PEH + cl + 16];
                 const f32x4 la = ea, lb = eb;  // softplus decay: logs G_r - R_i
                 if constexpr (GK != GATE_K3)
@@ -710,6 +719,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GK == GATE_
     // V in the same operand layout as (K * Gam)^T, read again here (it is not
     // kept in registers across the Gram phase, which keeps three workgroups on a CU)
     bf16x8 vb[2][2];
+    __builtin_amdgcn_s_setprio(3);
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
@@ -721,6 +731,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GK == GATE_
                 vb[hf][ks][e] = __builtin_bit_cast(
                     __bf16, (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rv, tl * ph + 2 * ch, tu * ph, 0));
             }
+    __builtin_amdgcn_s_setprio(0);
     {
         // T diag(beta) as split bf16 fragments, each of the six (token tile rt,
         // token block ks) tiles formed once, by wave p mod 4, into the CB region
